@@ -1,0 +1,26 @@
+"""CPU oracle for paged decode attention -- test infrastructure only.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg
+of ``bench.py`` may import this package.  It shares no code with the HIP path
+and imports nothing from it.
+"""
+from .paged_attention import (  # noqa: F401
+    attention,
+    gather_kv,
+    gather_sequence,
+    gather_sequence_fast,
+    key_vector,
+    kv_head_of,
+    lse,
+    lse_merge,
+    num_partitions,
+    online_block_attention,
+    paged_decode,
+    partition_partials,
+    poison_unused,
+    reshape_and_cache,
+    scores_fp64,
+    used_fill,
+    value_vector,
+    x_of,
+)
