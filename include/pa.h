@@ -1,0 +1,186 @@
+/*
+ * pa.h -- C ABI of libpa.so: paged decode attention for AMD Instinct MI355X
+ * (CDNA4, gfx950).
+ *
+ * What it computes is fixed by three web pages on vLLM's PagedAttention:
+ *   - "读 vLLM 的 PagedAttention kernel" (inference-learning-path.pages.dev):
+ *     §3.1 the paged K/V pool layouts, §3.2 the slot_mapping cache write,
+ *     §3.3 the kernel inputs and the v1/v2 PARTITION_SIZE split, §2 and §3.4
+ *     the block-table walk with an online-softmax fold;
+ *   - "KV Cache与PagedAttention内存管理" (aiqz.cc), section 自回归推理 for
+ *     softmax(QK^T/sqrt(d_k))V and section 分页机制 for the page map;
+ *   - "vLLM 的 PagedAttention：KV cache 为什么要分页" (bhhxx.wiki), §4.3 for
+ *     the per-block kernel loop.
+ *
+ * Conventions shared by every call
+ *   - Every pointer argument is a DEVICE pointer into memory the caller owns
+ *     (allocated by the caller, e.g. through PyTorch).  The library never
+ *     allocates, frees or synchronises; it validates its host-side arguments,
+ *     enqueues kernels on `stream` (a hipStream_t; NULL = the null stream) and
+ *     returns.  Calls keep no state between them and may be made from several
+ *     host threads.
+ *   - Element types: q, key, value, k_cache and v_cache hold IEEE fp16; out,
+ *     tmp_out, exp_sums and max_logits hold fp32; block_tables and seq_lens
+ *     int32; slot_mapping and cu_seq_lens int64.  All tensors are dense
+ *     row-major with the shapes given below, except key/value rows, whose
+ *     token stride is an argument.
+ *   - block_size must be 16 and head_size 64 or 128 (PA_ERR_UNSUPPORTED
+ *     otherwise).  x = 16 bytes / sizeof(fp16) = 8.
+ *   - Return value: PA_OK, or a negative pa_status before anything is
+ *     enqueued.  PA_ERR_LAUNCH reports a failed launch.  A kernel fault shows
+ *     up at the caller's next synchronisation, as HIP does.
+ *   - Values the host cannot see (block ids, seq_lens, slots) are checked on
+ *     the device so that no bad value turns into an out-of-bounds access:
+ *     a decode unit that meets a block id outside [0, num_blocks) or a length
+ *     longer than its block-table row writes NaN into its outputs instead of
+ *     reading; the cache write skips slots outside the pool.
+ */
+#ifndef PA_MI355X_PA_H
+#define PA_MI355X_PA_H
+
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define PA_API __attribute__((visibility("default")))
+#else
+#define PA_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+    PA_OK = 0,
+    PA_ERR_INVALID_ARG = -1,  /* null pointer, non-positive or inconsistent size */
+    PA_ERR_UNSUPPORTED = -2,  /* head_size not 64/128, block_size not 16        */
+    PA_ERR_MISALIGNED = -3,   /* a pointer or stride breaks 16-byte alignment    */
+    PA_ERR_LAUNCH = -4        /* the HIP runtime refused a launch               */
+} pa_status;
+
+/* Version of this ABI (bumped on any signature change). */
+PA_API int pa_abi_version(void);
+
+/* Human-readable text for a pa_status value (static storage). */
+PA_API const char* pa_status_str(int status);
+
+/*
+ * pa_decode_v1 -- unpartitioned paged decode attention.
+ *
+ * For every sequence s and query head h (KV head kvh = h / (num_heads /
+ * num_kv_heads)): walk block_tables[s] in logical order over the
+ * ceil(L/16) blocks of L = seq_lens[s] tokens, load each block's K and V from
+ * the pools (§3.1), and return
+ *     out[s,h,:] = sum_t softmax_t(scale * q[s,h,:] . K_t) V_t
+ * computed block by block with an online softmax (running max, normaliser
+ * and accumulator, §2 flowchart / §3.3), fp32 accumulation.
+ *
+ *   out          [num_seqs, num_heads, head_size] fp32, written
+ *   q            [num_seqs, num_heads, head_size] fp16
+ *   k_cache      [num_blocks, num_kv_heads, head_size/8, 16, 8] fp16
+ *   v_cache      [num_blocks, num_kv_heads, head_size, 16] fp16
+ *   block_tables [num_seqs, max_blocks_per_seq] int32: physical block ids;
+ *                entries past ceil(L/16) are never read
+ *   seq_lens     [num_seqs] int32: L <= 0 gives an all-zero row; slots past L
+ *                in the last block are never read (any bits, NaN included)
+ *   num_heads must be a multiple of num_kv_heads; scale must be finite and > 0.
+ */
+PA_API int pa_decode_v1(float* out, const void* q, const void* k_cache, const void* v_cache,
+                 const int32_t* block_tables, const int32_t* seq_lens,
+                 int num_seqs, int num_heads, int num_kv_heads, int head_size,
+                 int block_size, int max_blocks_per_seq, int num_blocks,
+                 float scale, void* stream);
+
+/* ceil(max_seq_len / partition_size): the partition count v2 scratch is sized
+ * for; -1 if an argument is not positive. */
+PA_API int pa_v2_max_partitions(int max_seq_len, int partition_size);
+
+/*
+ * pa_decode_v2 -- partitioned paged decode attention, first pass (§3.3: a
+ * PARTITION_SIZE > 0 cuts a long sequence into partitions computed in
+ * parallel and merged afterwards).
+ *
+ * Partition p of sequence s covers tokens [p*PS, min((p+1)*PS, L)),
+ * p < ceil(L/PS).  For each query head h it writes
+ *     max_logits[s,h,p] = m_p = max_t z_t          (z_t = scale * q . K_t)
+ *     exp_sums[s,h,p]   = l_p = sum_t exp(z_t - m_p)
+ *     tmp_out[s,h,p,:]  = sum_t exp(z_t - m_p) V_t / l_p
+ * in natural-log units.  Entries with p >= ceil(L/PS) are not written.
+ * pa_reduce merges them into the final output.
+ *
+ *   tmp_out     [num_seqs, num_heads, max_num_partitions, head_size] fp32 scratch
+ *   exp_sums    [num_seqs, num_heads, max_num_partitions] fp32 scratch
+ *   max_logits  [num_seqs, num_heads, max_num_partitions] fp32 scratch
+ *   other arguments as in pa_decode_v1;
+ *   partition_size: a positive multiple of 16;
+ *   max_num_partitions: >= ceil(L/PS) for every sequence (a longer sequence
+ *   gets NaN partials).
+ */
+PA_API int pa_decode_v2(float* tmp_out, float* exp_sums, float* max_logits,
+                 const void* q, const void* k_cache, const void* v_cache,
+                 const int32_t* block_tables, const int32_t* seq_lens,
+                 int num_seqs, int num_heads, int num_kv_heads, int head_size,
+                 int block_size, int max_blocks_per_seq, int num_blocks,
+                 int max_num_partitions, int partition_size, float scale,
+                 void* stream);
+
+/*
+ * pa_reduce -- v2 second pass: log-sum-exp merge of the partials (the pages
+ * say only "merged afterwards"; this is the exact merge).
+ *
+ * With n = ceil(L/PS), M = max_{p<n} m_p and w_p = l_p exp(m_p - M):
+ *     out[s,h,:] = sum_{p<n} (w_p / sum_q w_q) tmp_out[s,h,p,:]
+ * n = 0 gives zeros; n > max_num_partitions gives NaN.
+ *
+ *   out [num_seqs, num_heads, head_size] fp32, written; the other arrays as
+ *   written by pa_decode_v2 with the same num_heads, head_size,
+ *   max_num_partitions and partition_size.
+ */
+PA_API int pa_reduce(float* out, const float* tmp_out, const float* exp_sums,
+              const float* max_logits, const int32_t* seq_lens,
+              int num_seqs, int num_heads, int head_size,
+              int max_num_partitions, int partition_size, void* stream);
+
+/*
+ * reshape_and_cache -- scatter new tokens' K and V into the pools through
+ * slot_mapping (§3.2: a flat physical slot = block id * block_size + offset
+ * in the block; the write is the same indirection as the read, in the other
+ * direction).
+ *
+ * For token i with slot = slot_mapping[i], b = slot / 16, o = slot % 16:
+ *     k_cache[b, h, d/8, o, d%8] = key[i, h, d]
+ *     v_cache[b, h, d, o]        = value[i, h, d]     for every h, d.
+ * A bit-exact copy.  slot < 0 skips the token (padding); a slot at or past
+ * num_blocks*16 is skipped too.  Two tokens with the same slot race.
+ *
+ *   key, value   [num_tokens, num_kv_heads, head_size] fp16, token stride
+ *                key_stride / value_stride elements (a multiple of 8, at
+ *                least num_kv_heads*head_size)
+ *   k_cache, v_cache  as in pa_decode_v1, updated in place
+ *   slot_mapping [num_tokens] int64
+ */
+PA_API int reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                      const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
+                      int head_size, int block_size, int num_blocks,
+                      int64_t key_stride, int64_t value_stride, void* stream);
+
+/*
+ * pa_gather_kv -- the read-side indirection alone: every sequence's K and V
+ * copied bit-exactly, in logical token order, to contiguous arrays.
+ *
+ *   k_out, v_out [sum_s L_s, num_kv_heads, head_size] fp16, written: token t
+ *                of sequence s goes to row cu_seq_lens[s] + t
+ *   cu_seq_lens  [num_seqs] int64: starting row of each sequence
+ *   other arguments as in pa_decode_v1.  A bad block id writes NaN rows.
+ */
+PA_API int pa_gather_kv(void* k_out, void* v_out, const void* k_cache, const void* v_cache,
+                 const int32_t* block_tables, const int32_t* seq_lens,
+                 const int64_t* cu_seq_lens, int num_seqs, int num_kv_heads,
+                 int head_size, int block_size, int max_blocks_per_seq, int num_blocks,
+                 void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_MI355X_PA_H */

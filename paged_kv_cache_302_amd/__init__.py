@@ -1,0 +1,22 @@
+"""Paged decode attention for AMD Instinct MI355X (gfx950).
+
+The compute lives in libpa.so (hand-written HIP kernels behind a C ABI,
+declared in include/pa.h); this package is its thin Python binding.
+"""
+from ._lib import (  # noqa: F401
+    LIB_PATH,
+    PagedAttentionError,
+    exported_symbols,
+    load_library,
+    pa_abi_version,
+    pa_decode_v1,
+    pa_decode_v2,
+    pa_gather_kv,
+    pa_reduce,
+    pa_v2_max_partitions,
+    paged_attention_v1,
+    paged_attention_v2,
+    reshape_and_cache,
+    split_kv_cache,
+    v2_scratch,
+)

@@ -1,0 +1,152 @@
+// The two directions of the paged indirection (page "读 vLLM 的
+// PagedAttention kernel", §3.2: the write path scatters tokens to physical
+// slots through slot_mapping, the read path gathers them back through the
+// block table).
+//
+// reshape_and_cache: one thread per (token, KV head, 8-element chunk of the
+// head dims).  The chunk is one 16-byte load of key; in the x-packed K pool it
+// is one 16-byte store (k_cache[b, h, c, o, 0..7]).  V is stored transposed
+// (v_cache[b, h, d, o]): the same 16-byte load of value becomes eight 2-byte
+// stores 32 bytes apart.  A pure copy, so bit-exact.
+//
+// pa_gather_kv: the inverse, for testing the read-side indirection alone.
+// One thread per (sequence, logical block, token slot, KV head, chunk).
+#include "pa_device.h"
+#include "pa_host.h"
+
+namespace pa {
+
+template <int D>
+__global__ __launch_bounds__(256) void reshape_and_cache_kernel(
+    const f16* __restrict__ key, const f16* __restrict__ value, f16* __restrict__ k_cache,
+    f16* __restrict__ v_cache, const int64_t* __restrict__ slot_mapping, int num_tokens,
+    int num_kv_heads, long long num_slots, long long key_stride, long long value_stride) {
+    constexpr int C = D / kX;
+    const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    const long long total = (long long)num_tokens * num_kv_heads * C;
+    if (gid >= total) return;
+    const int c = (int)(gid % C);
+    const int h = (int)((gid / C) % num_kv_heads);
+    const int i = (int)(gid / ((long long)C * num_kv_heads));
+    const long long slot = slot_mapping[i];
+    if (slot < 0 || slot >= num_slots) return;
+    const long long b = slot / kBlock;
+    const int o = (int)(slot % kBlock);
+    const f16x8 kv = *reinterpret_cast<const f16x8*>(key + i * key_stride + h * D + c * kX);
+    const f16x8 vv = *reinterpret_cast<const f16x8*>(value + i * value_stride + h * D + c * kX);
+    const size_t tile = ((size_t)b * num_kv_heads + h) * (size_t)(D * kBlock);
+    *reinterpret_cast<f16x8*>(k_cache + tile + ((size_t)c * kBlock + o) * kX) = kv;
+    f16* vdst = v_cache + tile + (size_t)(c * kX) * kBlock + o;
+#pragma unroll
+    for (int j = 0; j < kX; ++j) vdst[j * kBlock] = vv[j];
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void gather_kv_kernel(
+    f16* __restrict__ k_out, f16* __restrict__ v_out, const f16* __restrict__ k_cache,
+    const f16* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
+    const int32_t* __restrict__ seq_lens, const int64_t* __restrict__ cu_seq_lens,
+    int num_kv_heads, int max_blocks_per_seq, int num_blocks, int wgs_per_block) {
+    constexpr int C = D / kX;
+    // workgroup -> (sequence, logical block, part of the block's items)
+    const int sb = blockIdx.x / wgs_per_block;
+    const int part = blockIdx.x - sb * wgs_per_block;
+    const int s = sb / max_blocks_per_seq;
+    const int lb = sb - s * max_blocks_per_seq;
+    const int item = part * blockDim.x + threadIdx.x;  // (slot o, head h, chunk c)
+    if (item >= kBlock * num_kv_heads * C) return;
+    const int c = item % C;
+    const int h = (item / C) % num_kv_heads;
+    const int o = item / (C * num_kv_heads);
+    const int L = seq_lens[s];
+    const int t = lb * kBlock + o;
+    if (t >= L || lb >= max_blocks_per_seq) return;
+    const int phys = block_tables[(size_t)s * max_blocks_per_seq + lb];
+    const size_t row = ((size_t)cu_seq_lens[s] + t) * num_kv_heads + h;
+    f16x8 kv, vv;
+    if (phys < 0 || phys >= num_blocks) {
+        const f16 nan = __builtin_bit_cast(f16, (unsigned short)0x7E00);
+        for (int j = 0; j < kX; ++j) kv[j] = vv[j] = nan;
+    } else {
+        const size_t tile = ((size_t)phys * num_kv_heads + h) * (size_t)(D * kBlock);
+        kv = *reinterpret_cast<const f16x8*>(k_cache + tile + ((size_t)c * kBlock + o) * kX);
+        const f16* vsrc = v_cache + tile + (size_t)(c * kX) * kBlock + o;
+#pragma unroll
+        for (int j = 0; j < kX; ++j) vv[j] = vsrc[j * kBlock];
+    }
+    *reinterpret_cast<f16x8*>(k_out + row * D + c * kX) = kv;
+    *reinterpret_cast<f16x8*>(v_out + row * D + c * kX) = vv;
+}
+
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" int reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                                 const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
+                                 int head_size, int block_size, int num_blocks,
+                                 int64_t key_stride, int64_t value_stride, void* stream) {
+    int rc = check_head_block(head_size, block_size);
+    if (rc != PA_OK) return rc;
+    if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PA_ERR_INVALID_ARG;
+    const int64_t row = (int64_t)num_kv_heads * head_size;
+    if (key_stride < row || value_stride < row) return PA_ERR_INVALID_ARG;
+    if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PA_ERR_INVALID_ARG;
+    if (!aligned16(key) || !aligned16(value) || !aligned16(k_cache) || !aligned16(v_cache) ||
+        !aligned8(slot_mapping) || key_stride % 8 != 0 || value_stride % 8 != 0)
+        return PA_ERR_MISALIGNED;
+    if (num_tokens == 0) return PA_OK;
+    const long long items = (long long)num_tokens * num_kv_heads * (head_size / kX);
+    const long long grid = (items + 255) / 256;
+    if (grid > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
+    const long long slots = (long long)num_blocks * kBlock;
+    hipStream_t st = as_stream(stream);
+    auto k = static_cast<const f16*>(key);
+    auto v = static_cast<const f16*>(value);
+    auto kc = static_cast<f16*>(k_cache);
+    auto vc = static_cast<f16*>(v_cache);
+    if (head_size == 128)
+        hipLaunchKernelGGL(reshape_and_cache_kernel<128>, dim3((unsigned)grid), dim3(256), 0, st, k,
+                           v, kc, vc, slot_mapping, num_tokens, num_kv_heads, slots,
+                           (long long)key_stride, (long long)value_stride);
+    else
+        hipLaunchKernelGGL(reshape_and_cache_kernel<64>, dim3((unsigned)grid), dim3(256), 0, st, k,
+                           v, kc, vc, slot_mapping, num_tokens, num_kv_heads, slots,
+                           (long long)key_stride, (long long)value_stride);
+    return launch_status();
+}
+
+extern "C" int pa_gather_kv(void* k_out, void* v_out, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* seq_lens,
+                            const int64_t* cu_seq_lens, int num_seqs, int num_kv_heads,
+                            int head_size, int block_size, int max_blocks_per_seq, int num_blocks,
+                            void* stream) {
+    int rc = check_head_block(head_size, block_size);
+    if (rc != PA_OK) return rc;
+    if (num_seqs < 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0)
+        return PA_ERR_INVALID_ARG;
+    if (!k_out || !v_out || !k_cache || !v_cache || !block_tables || !seq_lens || !cu_seq_lens)
+        return PA_ERR_INVALID_ARG;
+    if (!aligned16(k_out) || !aligned16(v_out) || !aligned16(k_cache) || !aligned16(v_cache) ||
+        !aligned4(block_tables) || !aligned4(seq_lens) || !aligned8(cu_seq_lens))
+        return PA_ERR_MISALIGNED;
+    if (num_seqs == 0) return PA_OK;
+    const int items = kBlock * num_kv_heads * (head_size / kX);
+    const int wgs = (items + 255) / 256;
+    const long long grid = (long long)num_seqs * max_blocks_per_seq * wgs;
+    if (grid > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
+    hipStream_t st = as_stream(stream);
+    auto ko = static_cast<f16*>(k_out);
+    auto vo = static_cast<f16*>(v_out);
+    auto kc = static_cast<const f16*>(k_cache);
+    auto vc = static_cast<const f16*>(v_cache);
+    if (head_size == 128)
+        hipLaunchKernelGGL(gather_kv_kernel<128>, dim3((unsigned)grid), dim3(256), 0, st, ko, vo,
+                           kc, vc, block_tables, seq_lens, cu_seq_lens, num_kv_heads,
+                           max_blocks_per_seq, num_blocks, wgs);
+    else
+        hipLaunchKernelGGL(gather_kv_kernel<64>, dim3((unsigned)grid), dim3(256), 0, st, ko, vo,
+                           kc, vc, block_tables, seq_lens, cu_seq_lens, num_kv_heads,
+                           max_blocks_per_seq, num_blocks, wgs);
+    return launch_status();
+}

@@ -1,0 +1,675 @@
+// Paged decode attention for gfx950 (MI355X): pa_decode_v1 and pa_decode_v2.
+//
+// What is computed (page "读 vLLM 的 PagedAttention kernel", §2 flowchart,
+// §3.3 and §3.4): for one query token per sequence, walk the sequence's block
+// table in logical order; for each 16-token block load its K and V tiles from
+// the pools (§3.1 layouts), score the block, fold it into a running
+// (max, normaliser, accumulator) with an online softmax, and at the end
+// write acc / l.  The partitioned variant (§3.3, PARTITION_SIZE > 0) does the
+// same over fixed token ranges and writes per-partition (o_p, m_p, l_p) for
+// pa_reduce to merge.
+//
+// Work decomposition.  A work unit is one (sequence, KV head, head chunk)
+// in v1 and one (sequence, KV head, head chunk, partition) in v2; a unit
+// serves every query head of its KV group (up to 16 per chunk), so each K/V
+// byte is read once per KV head.  One workgroup of NW wavefronts runs one
+// unit; wave w takes the unit's blocks w, w+NW, w+2NW, ... and the waves'
+// states are merged through LDS with the same max/rescale algebra.
+// Consecutive workgroups take the KV heads of the same (sequence, partition),
+// so concurrently running waves read neighbouring 4 KiB tiles of the same
+// physical blocks.  v2 enumerates only the partitions that exist (a prefix
+// sum over seq_lens inside each workgroup), so the grid is dense in real
+// work and the round-robin placement of workgroups on the eight XCDs stays
+// balanced.
+//
+// Two inner paths:
+//  * MFMA (G = H/KVH >= 2).  Scores S^T[t][h] = K[t][:] . Q[h][:] are one
+//    16x16 tile per block: D/32 v_mfma_f32_16x16x32_f16 with A = the K tile
+//    and B = Q^T.  In the x-packed K layout the 16-byte chunk of lane l at
+//    element 512*c + 8*l is exactly A's row (token) l%16, k-group l/16 for
+//    k-chunk c, so four coalesced 1 KiB global_load_dwordx4 per block feed
+//    the MFMA with no shuffles.  The output tile puts head l%16 and tokens
+//    4*(l/16)+r in lane l, which is already the B operand P^T of
+//    O^T[d][h] += V^T[d][t] P^T[t][h] (v_mfma_f32_16x16x16_f16, A = V^T read
+//    straight from the [d][t] V tile as 8-byte runs).  So the softmax state
+//    of head h lives in the lanes with l%16 == h: the per-block max needs a
+//    reduction over 4 lanes only, and the rescale of the accumulator is
+//    lane-local.
+//  * VALU (G == 1).  A single query row is a matrix-vector product, not a
+//    dense contraction: lane l owns token l%16 for the scores (v_dot2_f32_f16
+//    over its 32 head dims, then a 4-lane sum), the block max is a DPP row
+//    reduction, and the PV product uses the 16-byte V chunk of lane l (head
+//    dims 32c + l/2, 8 tokens) with fp16 weight pairs fetched by ds_bpermute.
+//
+// Masking.  Only the last block of a sequence can be partly filled.  Slots
+// at or past the sequence length are selected out: their scores become -inf
+// and their V elements are replaced by 0 before the product, so NaN or
+// garbage in unused slots never reaches the output (0 * NaN would).
+//
+// Softmax arithmetic.  The running max is kept on the raw dot products; each
+// weight is exp2((dot - m) * scale * log2 e), so the largest score of a block
+// gets exactly 1 and a one-token sequence returns its V bit-exactly.
+#include <math.h>
+
+#include "pa_device.h"
+#include "pa_host.h"
+
+namespace pa {
+
+struct DecodeParams {
+    float* out;           // v1: out[S,H,D]; v2: tmp_out[S,H,P,D]
+    float* exp_sums;      // v2: [S,H,P]
+    float* max_logits;    // v2: [S,H,P]
+    const f16* q;
+    const f16* k_cache;
+    const f16* v_cache;
+    const int32_t* block_tables;
+    const int32_t* seq_lens;
+    int num_seqs;
+    int num_heads;
+    int num_kv_heads;
+    int group;            // H / KVH
+    int head_chunks;      // ceil(group / 16) on the MFMA path, 1 on the VALU path
+    int max_blocks_per_seq;
+    int num_blocks;
+    int max_num_partitions;
+    int partition_size;   // tokens, multiple of 16 (v2)
+    float scale;          // natural units
+    float scale_log2;     // scale * log2(e)
+};
+
+// --------------------------------------------------------------------------
+// Block-table access: the wave's blocks k = 0..n-1 (logical block
+// first + k*NW) have their physical ids cached 64 at a time in one VGPR
+// (lane j holds entry k0 + j) and are read back with v_readlane.
+// --------------------------------------------------------------------------
+template <int NW>
+struct TableWindow {
+    const int32_t* row;
+    int first, n;
+    int k0;
+    int cur, nxt;
+
+    __device__ __forceinline__ int load(int kbase) const {
+        const int j = lane_id();
+        const int k = kbase + j;
+        return (k < n) ? row[first + k * NW] : 0;
+    }
+    __device__ __forceinline__ void init(const int32_t* r, int f, int cnt) {
+        row = r;
+        first = f;
+        n = cnt;
+        k0 = 0;
+        cur = load(0);
+        nxt = (n > 64) ? load(64) : 0;
+    }
+    // physical id of the wave's k-th block; k is wave-uniform and k >= k0
+    __device__ __forceinline__ int get(int k) const {
+        const int d = k - k0;
+        return d < 64 ? __builtin_amdgcn_readlane(cur, d) : __builtin_amdgcn_readlane(nxt, d - 64);
+    }
+    // called once block k has been consumed
+    __device__ __forceinline__ void advance(int k) {
+        if (k + 1 - k0 == 64) {
+            k0 += 64;
+            cur = nxt;
+            nxt = (k0 + 64 < n) ? load(k0 + 64) : 0;
+        }
+    }
+};
+
+// --------------------------------------------------------------------------
+// MFMA path (2 <= G): up to 16 query heads of one KV group per wave
+// --------------------------------------------------------------------------
+template <int D>
+struct MfmaPath {
+    static constexpr int KC = D / 32;   // 16x16x32 steps for the scores
+    static constexpr int NT = D / 16;   // 16-wide head-dim tiles of the output
+    static constexpr int kHeads = 16;
+
+    struct Tile {
+        f16x8 k[KC];   // lane (g,i): K[t=i][d = 32c + 8g .. +7]
+        f16x4 v[NT];   // lane (g,i): V[d = 16nt + i][t = 4g .. 4g+3]
+    };
+    struct State {
+        f32x4 acc[NT]; // lane (g,i): O^T[d = 16nt + 4g + r][h = i]
+        float m;       // running max of raw dot products of head i
+        float l;       // sum of weights over this lane's tokens 4g..4g+3
+    };
+    struct QRegs {
+        f16x8 q[KC];   // lane (g,i): Q[h = i][d = 32c + 8g .. +7]
+    };
+
+    __device__ static void load_q(QRegs& qr, const DecodeParams& p, int s, int h0, int nh) {
+        const int l = lane_id(), i = l & 15, g = l >> 4;
+        const f16* qrow = p.q + ((size_t)s * p.num_heads + h0 + i) * D + 8 * g;
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+            f16x8 z = {};
+            qr.q[c] = (i < nh) ? *reinterpret_cast<const f16x8*>(qrow + 32 * c) : z;
+        }
+    }
+
+    __device__ static void init(State& st) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) st.acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        st.m = -INFINITY;
+        st.l = 0.f;
+    }
+
+    __device__ __forceinline__ static void load(Tile& t, const f16* kt, const f16* vt) {
+        const int l = lane_id(), i = l & 15, g = l >> 4;
+        const f16x8* kp = reinterpret_cast<const f16x8*>(kt) + l;
+        const f16x4* vp = reinterpret_cast<const f16x4*>(vt) + 4 * i + g;
+#pragma unroll
+        for (int c = 0; c < KC; ++c) t.k[c] = kp[64 * c];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) t.v[nt] = vp[64 * nt];
+    }
+
+    __device__ __forceinline__ static void process(State& st, Tile& t, const QRegs& qr,
+                                                   int nvalid, float sl2) {
+        const int l = lane_id(), g = l >> 4;
+        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < KC; ++c)
+            s = __builtin_amdgcn_mfma_f32_16x16x32_f16(t.k[c], qr.q[c], s, 0, 0, 0);
+        if (nvalid < kBlock) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (4 * g + r >= nvalid) s[r] = -INFINITY;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (4 * g + r >= nvalid) t.v[nt][r] = (f16)0.f;
+        }
+        float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+        bm = col4_max(bm);
+        const float mn = fmaxf(st.m, bm);
+        const float corr = exp2_fast((st.m - mn) * sl2);
+        float pr[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pr[r] = exp2_fast((s[r] - mn) * sl2);
+        st.l = st.l * corr + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+        st.m = mn;
+        const f16x4 pv = {(f16)pr[0], (f16)pr[1], (f16)pr[2], (f16)pr[3]};
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            st.acc[nt] *= corr;
+            st.acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(t.v[nt], pv, st.acc[nt], 0, 0, 0);
+        }
+    }
+
+    // Per-head totals of the wave: l summed over the four token groups.
+    __device__ static float wave_l(const State& st) { return col4_sum(st.l); }
+
+    // Write the wave's normalised result for heads < nh directly.
+    __device__ static void store_direct(const State& st, float ltot, float* dst_head0,
+                                        size_t head_stride, int nh, bool bad) {
+        const int l = lane_id(), i = l & 15, g = l >> 4;
+        if (i >= nh) return;
+        const float inv = 1.f / ltot;
+        float* row = dst_head0 + (size_t)i * head_stride;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            f32x4 o = st.acc[nt] * inv;
+            if (bad) o = f32x4{NAN, NAN, NAN, NAN};
+            *reinterpret_cast<f32x4*>(row + 16 * nt + 4 * g) = o;
+        }
+    }
+
+    // Stage the wave's state for the cross-wave merge: acc[h][d] unnormalised.
+    __device__ static void stage(const State& st, float ltot, float* s_acc, float* s_m,
+                                 float* s_l, int nh) {
+        const int l = lane_id(), i = l & 15, g = l >> 4;
+        if (i >= nh) return;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+            *reinterpret_cast<f32x4*>(s_acc + i * D + 16 * nt + 4 * g) = st.acc[nt];
+        if (g == 0) {
+            s_m[i] = st.m;
+            s_l[i] = ltot;
+        }
+    }
+};
+
+// --------------------------------------------------------------------------
+// VALU path (G == 1): one query head per wave
+// --------------------------------------------------------------------------
+template <int D>
+struct ValuPath {
+    static constexpr int KC = D / 32;
+    static constexpr int kHeads = 1;
+
+    struct Tile {
+        f16x8 k[KC];   // lane l: K[t = l%16][d = 32c + 8(l/16) .. +7]
+        f16x8 v[KC];   // lane l: V[d = 32c + l/2][t = 8(l&1) .. +7]
+    };
+    struct State {
+        float acc[KC]; // lane l: partial O[d = 32c + l/2] over tokens 8(l&1)..+7
+        float m;       // running max of raw dot products
+        float l;       // sum of weights of token l%16 over blocks
+    };
+    struct QRegs {
+        f16x8 q[KC];   // lane l: q[d = 32c + 8(l/16) .. +7]
+    };
+
+    __device__ static void load_q(QRegs& qr, const DecodeParams& p, int s, int h0, int) {
+        const int g = lane_id() >> 4;
+        const f16* qrow = p.q + ((size_t)s * p.num_heads + h0) * D + 8 * g;
+#pragma unroll
+        for (int c = 0; c < KC; ++c) qr.q[c] = *reinterpret_cast<const f16x8*>(qrow + 32 * c);
+    }
+
+    __device__ static void init(State& st) {
+#pragma unroll
+        for (int c = 0; c < KC; ++c) st.acc[c] = 0.f;
+        st.m = -INFINITY;
+        st.l = 0.f;
+    }
+
+    __device__ __forceinline__ static void load(Tile& t, const f16* kt, const f16* vt) {
+        const int l = lane_id();
+        const f16x8* kp = reinterpret_cast<const f16x8*>(kt) + l;
+        const f16x8* vp = reinterpret_cast<const f16x8*>(vt) + l;
+#pragma unroll
+        for (int c = 0; c < KC; ++c) t.k[c] = kp[64 * c];
+#pragma unroll
+        for (int c = 0; c < KC; ++c) t.v[c] = vp[64 * c];
+    }
+
+    __device__ __forceinline__ static void process(State& st, Tile& t, const QRegs& qr,
+                                                   int nvalid, float sl2) {
+        const int l = lane_id(), i = l & 15, h = l & 1;
+        float part = 0.f;
+#pragma unroll
+        for (int c = 0; c < KC; ++c)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                part = dot2(f16x2{t.k[c][2 * j], t.k[c][2 * j + 1]},
+                            f16x2{qr.q[c][2 * j], qr.q[c][2 * j + 1]}, part);
+        float z = col4_sum(part);               // dot of token i, in every row
+        if (nvalid < kBlock) {
+            if (i >= nvalid) z = -INFINITY;
+#pragma unroll
+            for (int c = 0; c < KC; ++c)
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    if (8 * h + j >= nvalid) t.v[c][j] = (f16)0.f;
+        }
+        const float bm = row16_max(z);
+        const float mn = fmaxf(st.m, bm);
+        const float corr = exp2_fast((st.m - mn) * sl2);
+        const float pw = exp2_fast((z - mn) * sl2);
+        st.l = st.l * corr + pw;
+        st.m = mn;
+        // even lane t holds the fp16 pair (p_t, p_{t+1}); lane l needs the
+        // pairs of tokens 8h + 2kk, kk = 0..3
+        const f16x2 pair = pack2(pw, dpp<kDppXor1>(pw));
+        const int pair_bits = __builtin_bit_cast(int, pair);
+        f16x2 pp[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            pp[kk] = __builtin_bit_cast(f16x2, fetch_lane(pair_bits, 8 * h + 2 * kk));
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+            float a = st.acc[c] * corr;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                a = dot2(f16x2{t.v[c][2 * kk], t.v[c][2 * kk + 1]}, pp[kk], a);
+            st.acc[c] = a;
+        }
+    }
+
+    __device__ static float wave_l(const State& st) { return row16_sum(st.l); }
+
+    __device__ static void store_direct(const State& st, float ltot, float* dst_head0,
+                                        size_t, int, bool bad) {
+        const int l = lane_id();
+        const float inv = 1.f / ltot;
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+            const float full = st.acc[c] + dpp<kDppXor1>(st.acc[c]);
+            if ((l & 1) == 0) dst_head0[32 * c + (l >> 1)] = bad ? NAN : full * inv;
+        }
+    }
+
+    __device__ static void stage(const State& st, float ltot, float* s_acc, float* s_m,
+                                 float* s_l, int) {
+        const int l = lane_id();
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+            const float full = st.acc[c] + dpp<kDppXor1>(st.acc[c]);
+            if ((l & 1) == 0) s_acc[32 * c + (l >> 1)] = full;
+        }
+        if (l == 0) {
+            s_m[0] = st.m;
+            s_l[0] = ltot;
+        }
+    }
+};
+
+// --------------------------------------------------------------------------
+// v2 unit lookup: the r-th existing partition, counting sequences in order
+// and partitions p < ceil(L_s / PS) (capped at max_num_partitions).
+// --------------------------------------------------------------------------
+__device__ __forceinline__ int n_parts(int L, int PS, int Pmax) {
+    if (L <= 0) return 0;
+    const int n = (L - 1) / PS + 1;
+    return n < Pmax ? n : Pmax;
+}
+
+__device__ bool find_partition(const DecodeParams& p, int r, int& s_out, int& p_out) {
+    const int lane = lane_id();
+    int base = 0;  // partitions of the sequences before this chunk (uniform)
+    for (int s0 = 0; s0 < p.num_seqs; s0 += 64) {
+        const int s = s0 + lane;
+        const int np = (s < p.num_seqs) ? n_parts(p.seq_lens[s], p.partition_size, p.max_num_partitions) : 0;
+        int incl = np;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int t = __shfl_up(incl, off);
+            if (lane >= off) incl += t;
+        }
+        const int total = __builtin_amdgcn_readlane(incl, 63);
+        if (r < base + total) {
+            const unsigned long long mask = __ballot(base + incl > r);
+            const int first = __ffsll((long long)mask) - 1;
+            const int excl = __builtin_amdgcn_readlane(incl - np, first);
+            s_out = s0 + first;
+            p_out = r - base - excl;
+            return true;
+        }
+        base += total;
+    }
+    return false;
+}
+
+// --------------------------------------------------------------------------
+// The kernel
+// --------------------------------------------------------------------------
+template <class Path, int D, int NW, bool V2>
+__global__ __launch_bounds__(64 * NW) void pa_decode_kernel(DecodeParams p) {
+    extern __shared__ float lds[];
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index, uniform
+    const int kvhc_count = p.num_kv_heads * p.head_chunks;
+    const int kvhc = blockIdx.x % kvhc_count;
+    const int kvh = kvhc / p.head_chunks;
+    const int hc = kvhc - kvh * p.head_chunks;
+    const int h0 = kvh * p.group + hc * Path::kHeads;
+    const int nh_left = p.group - hc * Path::kHeads;
+    const int nh = nh_left < Path::kHeads ? nh_left : Path::kHeads;
+
+    int s, part = 0;
+    if constexpr (V2) {
+        if (!find_partition(p, blockIdx.x / kvhc_count, s, part)) return;
+    } else {
+        s = blockIdx.x / kvhc_count;
+    }
+    const int L = p.seq_lens[s];
+    const size_t out_head_stride = V2 ? (size_t)p.max_num_partitions * D : (size_t)D;
+    float* out_h0 = V2 ? p.out + (((size_t)s * p.num_heads + h0) * p.max_num_partitions + part) * D
+                       : p.out + ((size_t)s * p.num_heads + h0) * D;
+
+    if (!V2 && L <= 0) {  // empty sequence: zeros (v2 has no partition for it)
+        for (int e = threadIdx.x; e < nh * D; e += 64 * NW)
+            out_h0[(size_t)(e / D) * out_head_stride + (e % D)] = 0.f;
+        return;
+    }
+    const int nb_seq = (L + kBlock - 1) / kBlock;
+    bool bad = nb_seq > p.max_blocks_per_seq;
+    if constexpr (V2) bad = bad || (L - 1) / p.partition_size + 1 > p.max_num_partitions;
+
+    // token / block range of this unit
+    int tok_end = L, blk_begin = 0, blk_end = nb_seq;
+    if constexpr (V2) {
+        const int pb = p.partition_size / kBlock;
+        blk_begin = part * pb;
+        blk_end = min(nb_seq, blk_begin + pb);
+        tok_end = min(L, (part + 1) * p.partition_size);
+    }
+    if (bad) blk_end = blk_begin;  // read nothing
+
+    typename Path::State st;
+    Path::init(st);
+    typename Path::QRegs qr;
+    Path::load_q(qr, p, s, h0, nh);
+
+    // this wave's blocks: blk_begin + w + k*NW, k < n
+    const int first = blk_begin + w;
+    const int n = first < blk_end ? (blk_end - first + NW - 1) / NW : 0;
+    const size_t tile = (size_t)D * kBlock;
+    const f16* kbase = p.k_cache + (size_t)kvh * tile;
+    const f16* vbase = p.v_cache + (size_t)kvh * tile;
+    const size_t blk_stride = (size_t)p.num_kv_heads * tile;
+    const int32_t* row = p.block_tables + (size_t)s * p.max_blocks_per_seq;
+    const float sl2 = p.scale_log2;
+
+    if (n > 0) {
+        TableWindow<NW> tw;
+        tw.init(row, first, n);
+        typename Path::Tile ta, tb;
+        auto addr_ok = [&](int phys) { return phys >= 0 && phys < p.num_blocks; };
+        int ph = tw.get(0);
+        if (!addr_ok(ph)) { bad = true; ph = 0; }
+        Path::load(ta, kbase + (size_t)ph * blk_stride, vbase + (size_t)ph * blk_stride);
+        int k = 0;
+        // Two tiles in flight: block k+1 is requested before block k is
+        // processed.  The request is unconditional (past the wave's last block
+        // it re-reads the current one, a cache hit) so that the wait counts
+        // before each use are exact and never include the newer loads.
+        while (true) {
+            int nv = min(kBlock, tok_end - (first + k * NW) * kBlock);
+            if (k + 1 < n) {
+                const int ph1 = tw.get(k + 1);
+                if (addr_ok(ph1)) ph = ph1; else bad = true;
+            }
+            Path::load(tb, kbase + (size_t)ph * blk_stride, vbase + (size_t)ph * blk_stride);
+            Path::process(st, ta, qr, nv, sl2);
+            tw.advance(k);
+            if (++k >= n) break;
+            nv = min(kBlock, tok_end - (first + k * NW) * kBlock);
+            if (k + 1 < n) {
+                const int ph1 = tw.get(k + 1);
+                if (addr_ok(ph1)) ph = ph1; else bad = true;
+            }
+            Path::load(ta, kbase + (size_t)ph * blk_stride, vbase + (size_t)ph * blk_stride);
+            Path::process(st, tb, qr, nv, sl2);
+            tw.advance(k);
+            if (++k >= n) break;
+        }
+    }
+
+    const float ltot = Path::wave_l(st);
+    if constexpr (NW == 1) {
+        Path::store_direct(st, ltot, out_h0, out_head_stride, nh, bad);
+        if constexpr (V2) {
+            const int l = lane_id();
+            if (l < nh) {
+                // lane l < nh holds head l's max and total weight on both paths
+                const size_t idx = ((size_t)s * p.num_heads + h0 + l) * p.max_num_partitions + part;
+                p.max_logits[idx] = bad ? NAN : st.m * p.scale;
+                p.exp_sums[idx] = bad ? NAN : ltot;
+            }
+        }
+        return;
+    } else {
+        // merge the NW wave states through LDS
+        const int HP = Path::kHeads;
+        float* s_acc = lds;                              // [NW][nh][D]
+        float* s_m = lds + NW * nh * D;                  // [NW][HP]
+        float* s_l = s_m + NW * HP;                      // [NW][HP]
+        int* s_bad = reinterpret_cast<int*>(s_l + NW * HP);  // [NW]
+        Path::stage(st, ltot, s_acc + w * nh * D, s_m + w * HP, s_l + w * HP, nh);
+        if (lane_id() == 0) s_bad[w] = bad ? 1 : 0;
+        __syncthreads();
+        int any_bad = 0;
+#pragma unroll
+        for (int v = 0; v < NW; ++v) any_bad |= s_bad[v];
+        for (int e = threadIdx.x; e < nh * D; e += 64 * NW) {
+            const int j = e / D, d = e - j * D;
+            float M = -INFINITY;
+#pragma unroll
+            for (int v = 0; v < NW; ++v) M = fmaxf(M, s_m[v * HP + j]);
+            float num = 0.f, den = 0.f;
+#pragma unroll
+            for (int v = 0; v < NW; ++v) {
+                const float f = exp2_fast((s_m[v * HP + j] - M) * sl2);
+                num += s_acc[(v * nh + j) * D + d] * f;
+                den += s_l[v * HP + j] * f;
+            }
+            out_h0[(size_t)j * out_head_stride + d] = any_bad ? NAN : num / den;
+            if constexpr (V2) {
+                if (d == 0) {
+                    const size_t idx = ((size_t)s * p.num_heads + h0 + j) * p.max_num_partitions + part;
+                    p.max_logits[idx] = any_bad ? NAN : M * p.scale;
+                    p.exp_sums[idx] = any_bad ? NAN : den;
+                }
+            }
+        }
+    }
+}
+
+// --------------------------------------------------------------------------
+// Host side
+// --------------------------------------------------------------------------
+static size_t merge_lds_bytes(int NW, int nh_max, int D, int hp) {
+    if (NW == 1) return 0;
+    return (size_t)NW * ((size_t)nh_max * D + 2 * hp) * sizeof(float) + NW * sizeof(int);
+}
+
+template <class Path, int D, bool V2>
+static int launch_nw(int NW, const DecodeParams& p, int grid, int nh_max, hipStream_t st) {
+    // keep the merge buffer within the default 64 KiB of dynamic LDS
+    while (NW > 1 && merge_lds_bytes(NW, nh_max, D, Path::kHeads) > 65536) NW /= 2;
+    const size_t lds = merge_lds_bytes(NW, nh_max, D, Path::kHeads);
+    switch (NW) {
+        case 1: hipLaunchKernelGGL((pa_decode_kernel<Path, D, 1, V2>), dim3(grid), dim3(64), lds, st, p); break;
+        case 2: hipLaunchKernelGGL((pa_decode_kernel<Path, D, 2, V2>), dim3(grid), dim3(128), lds, st, p); break;
+        case 4: hipLaunchKernelGGL((pa_decode_kernel<Path, D, 4, V2>), dim3(grid), dim3(256), lds, st, p); break;
+        case 8: hipLaunchKernelGGL((pa_decode_kernel<Path, D, 8, V2>), dim3(grid), dim3(512), lds, st, p); break;
+        default: return PA_ERR_INVALID_ARG;
+    }
+    return launch_status();
+}
+
+template <bool V2>
+static int launch_decode(const DecodeParams& p, int head_size, int NW, int grid, hipStream_t st) {
+    const bool mfma = p.group >= 2;
+    const int nh_max = mfma ? (p.group < 16 ? p.group : 16) : 1;
+    if (head_size == 128)
+        return mfma ? launch_nw<MfmaPath<128>, 128, V2>(NW, p, grid, nh_max, st)
+                    : launch_nw<ValuPath<128>, 128, V2>(NW, p, grid, nh_max, st);
+    return mfma ? launch_nw<MfmaPath<64>, 64, V2>(NW, p, grid, nh_max, st)
+                : launch_nw<ValuPath<64>, 64, V2>(NW, p, grid, nh_max, st);
+}
+
+static int check_decode_args(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_tables, const int32_t* seq_lens, int num_seqs,
+                             int num_heads, int num_kv_heads, int head_size, int block_size,
+                             int max_blocks_per_seq, int num_blocks, float scale) {
+    int rc = check_head_block(head_size, block_size);
+    if (rc != PA_OK) return rc;
+    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
+        num_blocks <= 0)
+        return PA_ERR_INVALID_ARG;
+    if (num_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+    if (!(scale > 0.f) || !isfinite(scale)) return PA_ERR_INVALID_ARG;
+    if (!q || !k_cache || !v_cache || !block_tables || !seq_lens) return PA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned4(block_tables) ||
+        !aligned4(seq_lens))
+        return PA_ERR_MISALIGNED;
+    return PA_OK;
+}
+
+static DecodeParams make_params(const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* block_tables, const int32_t* seq_lens,
+                                int num_seqs, int num_heads, int num_kv_heads,
+                                int max_blocks_per_seq, int num_blocks, float scale) {
+    DecodeParams p{};
+    p.q = static_cast<const f16*>(q);
+    p.k_cache = static_cast<const f16*>(k_cache);
+    p.v_cache = static_cast<const f16*>(v_cache);
+    p.block_tables = block_tables;
+    p.seq_lens = seq_lens;
+    p.num_seqs = num_seqs;
+    p.num_heads = num_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.group = num_heads / num_kv_heads;
+    p.head_chunks = p.group >= 2 ? (p.group + 15) / 16 : 1;
+    p.max_blocks_per_seq = max_blocks_per_seq;
+    p.num_blocks = num_blocks;
+    p.scale = scale;
+    p.scale_log2 = scale * kLog2e;
+    p.max_num_partitions = 1;
+    p.partition_size = 0;
+    return p;
+}
+
+// Waves per workgroup: enough wavefronts in flight to cover the HBM latency
+// (the unit count alone is too small to fill 256 CUs on short batches), but
+// no more waves than a unit has blocks.
+static int pick_waves(long long units, long long blocks_per_unit) {
+    const long long target = 256LL * 12;  // ~12 resident waves per CU
+    int nw = 1;
+    while (nw < 8 && units * nw < target && (long long)(nw * 2) * 2 <= blocks_per_unit) nw *= 2;
+    return nw;
+}
+
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" int pa_decode_v1(float* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* seq_lens, int num_seqs,
+                            int num_heads, int num_kv_heads, int head_size, int block_size,
+                            int max_blocks_per_seq, int num_blocks, float scale, void* stream) {
+    int rc = check_decode_args(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_heads,
+                               num_kv_heads, head_size, block_size, max_blocks_per_seq, num_blocks,
+                               scale);
+    if (rc != PA_OK) return rc;
+    if (!out) return PA_ERR_INVALID_ARG;
+    if (!aligned16(out)) return PA_ERR_MISALIGNED;
+    if (num_seqs == 0) return PA_OK;
+    DecodeParams p = make_params(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_heads,
+                                 num_kv_heads, max_blocks_per_seq, num_blocks, scale);
+    p.out = out;
+    const long long units = (long long)num_seqs * num_kv_heads * p.head_chunks;
+    if (units > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
+    const int nw = pick_waves(units, max_blocks_per_seq);
+    return launch_decode<false>(p, head_size, nw, (int)units, as_stream(stream));
+}
+
+extern "C" int pa_v2_max_partitions(int max_seq_len, int partition_size) {
+    if (max_seq_len <= 0 || partition_size <= 0) return -1;
+    return (max_seq_len - 1) / partition_size + 1;
+}
+
+extern "C" int pa_decode_v2(float* tmp_out, float* exp_sums, float* max_logits, const void* q,
+                            const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                            const int32_t* seq_lens, int num_seqs, int num_heads, int num_kv_heads,
+                            int head_size, int block_size, int max_blocks_per_seq, int num_blocks,
+                            int max_num_partitions, int partition_size, float scale, void* stream) {
+    int rc = check_decode_args(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_heads,
+                               num_kv_heads, head_size, block_size, max_blocks_per_seq, num_blocks,
+                               scale);
+    if (rc != PA_OK) return rc;
+    if (!tmp_out || !exp_sums || !max_logits) return PA_ERR_INVALID_ARG;
+    if (max_num_partitions <= 0 || partition_size <= 0 || partition_size % 16 != 0)
+        return PA_ERR_INVALID_ARG;
+    if (!aligned16(tmp_out) || !aligned4(exp_sums) || !aligned4(max_logits))
+        return PA_ERR_MISALIGNED;
+    if (num_seqs == 0) return PA_OK;
+    DecodeParams p = make_params(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_heads,
+                                 num_kv_heads, max_blocks_per_seq, num_blocks, scale);
+    p.out = tmp_out;
+    p.exp_sums = exp_sums;
+    p.max_logits = max_logits;
+    p.max_num_partitions = max_num_partitions;
+    p.partition_size = partition_size;
+    const long long units = (long long)num_seqs * num_kv_heads * p.head_chunks * max_num_partitions;
+    if (units > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
+    const int nw = pick_waves(units / 2, partition_size / 16);
+    return launch_decode<true>(p, head_size, nw, (int)units, as_stream(stream));
+}

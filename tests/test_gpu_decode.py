@@ -1,0 +1,247 @@
+"""GPU parity of the decode kernels against the fp64 oracle: v1, v2 partials,
+pa_reduce alone, v2 + reduce; the invariants the pages fix (paged == dense,
+physical placement is free, a partly filled last block) and edge cases."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_302_amd as pa
+import workloads as wl
+from tests._util import assert_parity, dev_inputs, device, to_dev
+
+pytestmark = pytest.mark.gpu
+
+# (label, num_seqs, num_heads, num_kv_heads, head_size, len_lo, len_hi, partition_size)
+CASES = [
+    ("mha_d64", 4, 4, 4, 64, 1, 130, 32),
+    ("mha_d128", 3, 6, 6, 128, 1, 300, 64),
+    ("g2_d128", 3, 4, 2, 128, 1, 300, 64),
+    ("g4_d128", 4, 16, 4, 128, 1, 700, 128),
+    ("g7_d128", 3, 14, 2, 128, 100, 600, 512),
+    ("g8_d64", 3, 16, 2, 64, 1, 400, 64),
+    ("g16_d128", 2, 32, 2, 128, 1, 300, 64),
+    ("g24_d128", 2, 24, 1, 128, 1, 300, 64),     # two head chunks (16 + 8)
+    ("g32_d64", 2, 32, 1, 64, 1, 200, 32),
+]
+
+
+def make_case(case, seed):
+    label, S, H, KVH, D, lo, hi, ps = case
+    w = wl.small_workload(label, num_seqs=S, num_heads=H, num_kv_heads=KVH, head_size=D,
+                          seq_len_lo=lo, seq_len_hi=hi, partition_size=ps)
+    inp = wl.make_inputs(w, seed)
+    oracle.poison_unused(inp.k_cache, inp.v_cache, inp.block_tables, inp.seq_lens, 16)
+    return inp
+
+
+def run_v1(inp):
+    d = dev_inputs(inp)
+    return pa.paged_attention_v1(d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
+                                 d["seq_lens"], inp.scale).cpu().numpy()
+
+
+def run_v2(inp, ps, max_seq_len=None):
+    d = dev_inputs(inp)
+    S, H, D = inp.q.shape
+    msl = max_seq_len or inp.workload.max_seq_len
+    P = pa.pa_v2_max_partitions(msl, ps)
+    tmp, es, ml = pa.v2_scratch(S, H, D, P, device())
+    for t in (tmp, es, ml):
+        t.fill_(float("nan"))
+    pa.pa_decode_v2(tmp, es, ml, d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
+                    d["seq_lens"], inp.scale, ps)
+    out = torch.empty((S, H, D), dtype=torch.float32, device=device())
+    pa.pa_reduce(out, tmp, es, ml, d["seq_lens"], ps)
+    return out.cpu().numpy(), tmp.cpu().numpy(), es.cpu().numpy(), ml.cpu().numpy(), P
+
+
+def ref_out(inp):
+    return oracle.paged_decode(inp.q, inp.k_cache, inp.v_cache, inp.block_tables, inp.seq_lens,
+                               inp.scale, 16)
+
+
+@pytest.mark.parametrize("seed", [1, 11])
+def test_tiny_workload_v1(seed):
+    inp = wl.make_inputs(wl.WORKLOADS["tiny"], seed)
+    oracle.poison_unused(inp.k_cache, inp.v_cache, inp.block_tables, inp.seq_lens, 16)
+    assert_parity(run_v1(inp), ref_out(inp), "tiny v1")
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_v1_matches_oracle(case):
+    inp = make_case(case, 2)
+    assert_parity(run_v1(inp), ref_out(inp), case[0])
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_v2_partials_and_merge_match_oracle(case):
+    inp = make_case(case, 3)
+    ps = case[7]
+    out, tmp, es, ml, P = run_v2(inp, ps)
+    t_ref, e_ref, m_ref = oracle.partition_partials(inp.q, inp.k_cache, inp.v_cache,
+                                                    inp.block_tables, inp.seq_lens, inp.scale, 16,
+                                                    ps, P)
+    valid = ~np.isnan(e_ref)                     # partitions that exist
+    assert np.isnan(es[~valid]).all(), "v2 wrote a partition past the sequence"
+    assert_parity(tmp[valid], t_ref[valid], case[0] + " o_p")
+    np.testing.assert_allclose(ml[valid], m_ref[valid], rtol=1e-5, atol=1e-5)
+    np.testing.assert_allclose(es[valid], e_ref[valid], rtol=2e-5)
+    assert_parity(out, ref_out(inp), case[0] + " v2+reduce")
+
+
+@pytest.mark.parametrize("case", CASES[:5], ids=[c[0] for c in CASES[:5]])
+def test_reduce_alone_on_oracle_partials(case):
+    """pa_reduce fed with the oracle's own partials (rounded to fp32)."""
+    inp = make_case(case, 4)
+    ps = case[7]
+    S, H, D = inp.q.shape
+    P = pa.pa_v2_max_partitions(inp.workload.max_seq_len, ps)
+    t_ref, e_ref, m_ref = oracle.partition_partials(inp.q, inp.k_cache, inp.v_cache,
+                                                    inp.block_tables, inp.seq_lens, inp.scale, 16,
+                                                    ps, P)
+    dev = device()
+    tmp = to_dev(t_ref.astype(np.float32))
+    es = to_dev(e_ref.astype(np.float32))
+    ml = to_dev(m_ref.astype(np.float32))
+    out = torch.empty((S, H, D), dtype=torch.float32, device=dev)
+    pa.pa_reduce(out, tmp, es, ml, to_dev(inp.seq_lens), ps)
+    merged = oracle.lse_merge(t_ref, e_ref, m_ref, inp.seq_lens, ps)
+    np.testing.assert_allclose(out.cpu().numpy(), merged, rtol=1e-5, atol=1e-6)
+
+
+def test_v1_equals_v2_within_tolerance():
+    inp = make_case(CASES[3], 5)
+    a = run_v1(inp)
+    b = run_v2(inp, 128)[0]
+    assert_parity(a, b, "v1 vs v2")
+
+
+# --------------------------------------------------------------------------
+# Invariants and closed forms
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("H,KVH,D", [(4, 4, 128), (8, 2, 128), (28, 4, 128), (16, 2, 64)])
+def test_seq_len_one_returns_v_exactly(H, KVH, D):
+    w = wl.small_workload(num_seqs=3, num_heads=H, num_kv_heads=KVH, head_size=D, seq_len_lo=1,
+                          seq_len_hi=1)
+    inp = wl.make_inputs(w, 6)
+    oracle.poison_unused(inp.k_cache, inp.v_cache, inp.block_tables, inp.seq_lens, 16)
+    G = H // KVH
+    expect = np.empty((3, H, D), dtype=np.float32)
+    for s in range(3):
+        b = inp.block_tables[s, 0]
+        for h in range(H):
+            expect[s, h] = inp.v_cache[b, h // G, :, 0].astype(np.float32)
+    assert np.array_equal(run_v1(inp), expect)
+    assert np.array_equal(run_v2(inp, 512)[0], expect)
+
+
+def test_identical_keys_give_mean_of_v():
+    w = wl.small_workload(num_seqs=2, num_heads=8, num_kv_heads=2, head_size=128, seq_len_lo=300,
+                          seq_len_hi=700)
+    inp = wl.make_inputs(w, 7)
+    # every key of KV head h equals one fixed vector
+    k = np.random.default_rng(0).standard_normal((2, 128)).astype(np.float16)
+    for h in range(2):
+        inp.k_cache[:, h] = k[h].reshape(16, 1, 8)
+    oracle.poison_unused(inp.k_cache, inp.v_cache, inp.block_tables, inp.seq_lens, 16)
+    want = np.empty((2, 8, 128))
+    for s in range(2):
+        for kvh in range(2):
+            _, V = oracle.gather_sequence_fast(inp.k_cache, inp.v_cache, inp.block_tables[s],
+                                               int(inp.seq_lens[s]), kvh, 16)
+            want[s, kvh * 4:(kvh + 1) * 4] = V.astype(np.float64).mean(axis=0)
+    assert_parity(run_v1(inp), want, "identical keys v1")
+    assert_parity(run_v2(inp, 64)[0], want, "identical keys v2")
+
+
+@pytest.mark.parametrize("case", [CASES[0], CASES[3]], ids=["mha", "gqa"])
+def test_permuting_physical_ids_is_bit_identical(case):
+    inp = make_case(case, 8)
+    NB = inp.num_blocks
+    perm = np.random.default_rng(1).permutation(NB)
+    inp2 = wl.DecodeInputs(inp.workload, inp.seed, inp.seq_lens,
+                           np.where(inp.block_tables >= 0, perm[np.maximum(inp.block_tables, 0)], -1)
+                           .astype(np.int32), NB, inp.q, np.empty_like(inp.k_cache),
+                           np.empty_like(inp.v_cache))
+    inp2.k_cache[perm] = inp.k_cache
+    inp2.v_cache[perm] = inp.v_cache
+    assert np.array_equal(run_v1(inp), run_v1(inp2))
+    assert np.array_equal(run_v2(inp, case[7])[0], run_v2(inp2, case[7])[0])
+
+
+def test_reruns_are_bit_identical():
+    inp = make_case(CASES[4], 9)
+    a, b = run_v1(inp), run_v1(inp)
+    assert a.tobytes() == b.tobytes()
+    c, d = run_v2(inp, 512)[0], run_v2(inp, 512)[0]
+    assert c.tobytes() == d.tobytes()
+
+
+def test_zero_length_sequence_gives_zeros():
+    inp = make_case(CASES[2], 10)
+    inp.seq_lens[1] = 0
+    ref = ref_out(inp)
+    out1 = run_v1(inp)
+    out2 = run_v2(inp, 64)[0]
+    assert (out1[1] == 0).all() and (out2[1] == 0).all()
+    assert_parity(out1, ref, "v1 with empty sequence")
+    assert_parity(out2, ref, "v2 with empty sequence")
+
+
+def test_out_of_range_block_id_gives_nan_not_a_read():
+    """A block id >= num_blocks marks its unit's output NaN.  The pools are
+    allocated four blocks larger than the num_blocks the call sees, so the id
+    used here stays inside memory even if the device check were missing."""
+    inp = make_case(CASES[3], 12)
+    NB = inp.num_blocks
+    kc = np.concatenate([inp.k_cache, np.zeros((4,) + inp.k_cache.shape[1:], np.float16)])
+    vc = np.concatenate([inp.v_cache, np.zeros((4,) + inp.v_cache.shape[1:], np.float16)])
+    bt = inp.block_tables.copy()
+    bt[1, 0] = NB + 2
+    d = dict(q=to_dev(inp.q), k=to_dev(kc)[:NB], v=to_dev(vc)[:NB], bt=to_dev(bt),
+             sl=to_dev(inp.seq_lens))
+    out = pa.paged_attention_v1(d["q"], d["k"], d["v"], d["bt"], d["sl"], inp.scale).cpu().numpy()
+    out2 = pa.paged_attention_v2(d["q"], d["k"], d["v"], d["bt"], d["sl"], inp.scale, 128,
+                                 inp.workload.max_seq_len).cpu().numpy()
+    ref = ref_out(inp)
+    G = 4
+    for o in (out, out2):
+        assert np.isnan(o[1, 0:G]).all()           # KV head 0 of sequence 1 saw the bad id
+        ok = np.ones(o.shape[:2], dtype=bool)
+        ok[1, 0:G] = False
+        assert_parity(o[ok], ref[ok], "other units unaffected")
+
+
+def test_worked_example_embedded():
+    """The kernel page's worked example (§4: q, six keys and values of head
+    size 4, block size 4, blocks [3, 1]) embedded in head size 64 / block
+    size 16: q and K zero-padded past dim 4, V zero-padded, one block at a
+    random physical id, scale 1/sqrt(4) passed explicitly.  The first four
+    outputs match the page's printed values up to the fp16 rounding of the
+    inputs; the rest are exactly zero."""
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "worked_example.json")) as f:
+        ex = json.load(f)
+    D, NB = 64, 8
+    q = np.zeros((1, 1, D), np.float16)
+    q[0, 0, :4] = ex["q"]
+    K = np.zeros((6, D), np.float16)
+    V = np.zeros((6, D), np.float16)
+    K[:, :4] = ex["K"]
+    V[:, :4] = ex["V"]
+    kc = np.full((NB, 1, D // 8, 16, 8), np.nan, np.float16)
+    vc = np.full((NB, 1, D, 16), np.nan, np.float16)
+    b = 5
+    kc[b, 0, :, :6, :] = K.reshape(6, D // 8, 8).transpose(1, 0, 2)
+    vc[b, 0, :, :6] = V.T
+    bt = np.array([[b]], np.int32)
+    sl = np.array([6], np.int32)
+    out = pa.paged_attention_v1(to_dev(q), to_dev(kc), to_dev(vc), to_dev(bt), to_dev(sl),
+                                ex["scale"]).cpu().numpy()[0, 0]
+    np.testing.assert_allclose(out[:4], ex["expected_out"], atol=1e-3)
+    assert (out[4:] == 0).all()
