@@ -1,0 +1,280 @@
+"""Benchmark: paged decode attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long_gqa]
+                    [--kernel v2|v1] [--seed S] [--no-cpu-baseline]
+
+One step is one decode step of the whole hot path over one synthetic batch:
+the cache write of the step's new token per sequence (reshape_and_cache at
+logical position L_s - 1), then the decode attention over L_s tokens
+(pa_decode_v2 + pa_reduce, or pa_decode_v1).  Inputs are generated once and
+are resident in HBM before timing starts.
+
+The metric is effective KV bandwidth: sum_s L_s * 2 * num_kv_heads * head_size
+* 2 bytes per step divided by the step time, also given as a fraction of the
+MI355X HBM peak (8 TB/s).  Rank 0 prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "paged decode attention: effective KV GB/s (% of HBM peak) + µs/call"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long_gqa")
+    ap.add_argument("--kernel", default="v2", choices=["v1", "v2"])
+    ap.add_argument("--seed", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="CPU time budget of the oracle baseline sample")
+    return ap.parse_args()
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return 1
+
+
+def cpu_baseline(inp, gpu_out, budget_s: float):
+    """The oracle (fp64 NumPy) on a bounded sample of the same workload:
+    whole (sequence, KV head) units in order until the time budget is spent.
+    Returns its throughput in the metric's unit, and its agreement with the
+    GPU output on the sampled rows."""
+    import oracle
+    import workloads as wl
+    w = inp.workload
+    G = w.num_heads // w.num_kv_heads
+    # the same cache write the GPU step made, so both see the same K/V
+    oracle.reshape_and_cache(inp.key, inp.value, inp.k_cache, inp.v_cache,
+                             wl.new_token_slots(inp), w.block_size, inplace=True)
+    done_bytes = 0
+    spent = 0.0
+    units = 0
+    max_err = 0.0
+    for s in range(w.num_seqs):
+        L = int(inp.seq_lens[s])
+        for kvh in range(w.num_kv_heads):
+            t0 = time.perf_counter()
+            K, V = oracle.gather_sequence_fast(inp.k_cache, inp.v_cache, inp.block_tables[s], L,
+                                               kvh, w.block_size)
+            ref = oracle.attention(inp.q[s, kvh * G:(kvh + 1) * G], K, V, inp.scale)
+            spent += time.perf_counter() - t0
+            done_bytes += L * 2 * w.head_size * 2
+            units += 1
+            max_err = max(max_err, float(np.abs(ref - gpu_out[s, kvh * G:(kvh + 1) * G]).max()))
+            if spent >= budget_s:
+                break
+        if spent >= budget_s:
+            break
+    return {
+        "value": round(done_bytes / spent / 1e9, 4),
+        "unit": "GB/s",
+        "cores": blas_threads(),
+        "kind": "oracle",
+        "sample": f"{units} whole (sequence, KV head) units of the same inputs "
+                  f"({done_bytes / 1e9:.3f} GB of K/V), fp64 NumPy gather + two-pass softmax",
+        "seconds": round(spent, 3),
+        "host_cpus": os.cpu_count(),
+        "affinity_cpus": len(os.sched_getaffinity(0)),
+        "cpu_model": cpu_model(),
+        "max_abs_diff_vs_gpu": max_err,
+    }
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for name in ("pa_decode.hip", "pa_device.h"):
+        with open(os.path.join(ROOT, "paged_kv_cache_302_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kname: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (profiles/traffic_<kernel>_<workload>.txt), or None when there is none or
+    the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kname}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return int(float(fields["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode "
+              "kernels are not sharded across GPUs in this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import paged_kv_cache_302_amd as pa
+    import workloads as wl
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    dev = torch.device("cuda:0")
+    w = wl.WORKLOADS[args.workload]
+    t0 = time.time()
+    inp = wl.make_inputs(w, args.seed)
+    gen_s = time.time() - t0
+    S, H, D, KVH = w.num_seqs, w.num_heads, w.head_size, w.num_kv_heads
+    G = H // KVH
+
+    def t(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    q, kc, vc = t(inp.q), t(inp.k_cache), t(inp.v_cache)
+    bt, sl = t(inp.block_tables), t(inp.seq_lens)
+    # the step's new token per sequence, written at logical position L_s - 1
+    slots = wl.new_token_slots(inp)
+    key, val, slot_d = t(inp.key), t(inp.value), t(slots)
+
+    PS = w.partition_size
+    P = pa.pa_v2_max_partitions(w.max_seq_len, PS)
+    tmp, es, ml = pa.v2_scratch(S, H, D, P, dev)
+    out = torch.empty((S, H, D), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        pa.reshape_and_cache(key, val, kc, vc, slot_d)
+        if ev is not None:
+            ev[1].record(stream)
+        if args.kernel == "v2":
+            pa.pa_decode_v2(tmp, es, ml, q, kc, vc, bt, sl, inp.scale, PS)
+            if ev is not None:
+                ev[2].record(stream)
+            pa.pa_reduce(out, tmp, es, ml, sl, PS)
+        else:
+            pa.pa_decode_v1(out, q, kc, vc, bt, sl, inp.scale)
+            if ev is not None:
+                ev[2].record(stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` steps, synchronised on both sides
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    ms_per_step = elapsed * 1e3 / args.steps
+
+    cache_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    decode_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    reduce_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    dec_avg_s = float(np.mean(decode_ms)) / 1e3
+
+    kv_bytes = inp.kv_bytes
+    unique_bytes = inp.unique_kv_bytes if w.group_size else kv_bytes
+    value = kv_bytes / (ms_per_step / 1e3) / 1e9
+    achieved = unique_bytes / dec_avg_s / 1e9
+    kname = "pa_decode_v2" if args.kernel == "v2" else "pa_decode_v1"
+    traffic = read_traffic(kname, args.workload)
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload,
+            "kernel": f"reshape_and_cache + {kname}" + (" + pa_reduce" if args.kernel == "v2" else ""),
+            "num_seqs": S, "num_heads": H, "num_kv_heads": KVH, "head_size": D,
+            "block_size": w.block_size, "partition_size": PS if args.kernel == "v2" else None,
+            "seq_lens": [int(x) for x in inp.seq_lens] if S <= 16 else
+                        [int(inp.seq_lens.min()), int(inp.seq_lens.max())],
+            "sum_seq_len": int(inp.seq_lens.sum()),
+            "kv_bytes_per_step": kv_bytes,
+            "unique_kv_bytes_per_step": unique_bytes,
+            "num_blocks": inp.num_blocks, "seed": args.seed,
+        },
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "kernels_us": {
+            "reshape_and_cache": round(float(np.median(cache_ms)) * 1e3, 2),
+            kname: round(float(np.median(decode_ms)) * 1e3, 2),
+            **({"pa_reduce": round(float(np.median(reduce_ms)) * 1e3, 2)} if args.kernel == "v2" else {}),
+        },
+        "roofline": {
+            "kernel": kname,
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": unique_bytes,
+            "avg_launch_us": round(dec_avg_s * 1e6, 2),
+        },
+        "input_gen_s": round(gen_s, 2),
+    }
+    if not args.no_cpu_baseline:
+        gpu_out = out.cpu().numpy()
+        res["cpu_baseline"] = cpu_baseline(inp, gpu_out, args.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

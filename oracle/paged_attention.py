@@ -274,16 +274,17 @@ def online_block_attention(q, K, V, scale: float, block_size: int) -> np.ndarray
 # Cache write and logical-order gather (kernel page §3.2)
 # ---------------------------------------------------------------------------
 
-def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, block_size: int):
-    """Scatter new tokens into copies of the pools, token by token.
+def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, block_size: int,
+                      inplace: bool = False):
+    """Scatter new tokens into the pools, token by token.
 
     Token i goes to flat physical slot s = slot_mapping[i]: block s // B, offset
     s % B.  Its K lands in k_cache[b, h, d // x, o, d % x] and its V in
     v_cache[b, h, d, o] for every KV head h.  slot < 0 skips the token.
-    Returns the new (k_cache, v_cache); inputs are not modified.
+    Returns the new (k_cache, v_cache): copies, unless inplace=True.
     """
-    kc = k_cache.copy()
-    vc = v_cache.copy()
+    kc = k_cache if inplace else k_cache.copy()
+    vc = v_cache if inplace else v_cache.copy()
     T, KVH, D = key.shape
     x = kc.shape[4]
     for i in range(T):

@@ -208,12 +208,11 @@ def test_out_of_range_block_id_gives_nan_not_a_read():
     out2 = pa.paged_attention_v2(d["q"], d["k"], d["v"], d["bt"], d["sl"], inp.scale, 128,
                                  inp.workload.max_seq_len).cpu().numpy()
     ref = ref_out(inp)
-    G = 4
     for o in (out, out2):
-        assert np.isnan(o[1, 0:G]).all()           # KV head 0 of sequence 1 saw the bad id
+        assert np.isnan(o[1]).all()     # every KV head of sequence 1 walks the bad row
         ok = np.ones(o.shape[:2], dtype=bool)
-        ok[1, 0:G] = False
-        assert_parity(o[ok], ref[ok], "other units unaffected")
+        ok[1] = False
+        assert_parity(o[ok], ref[ok], "other sequences unaffected")
 
 
 def test_worked_example_embedded():

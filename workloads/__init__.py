@@ -197,7 +197,7 @@ class DecodeInputs:
     q: np.ndarray
     k_cache: np.ndarray
     v_cache: np.ndarray
-    # cache-write step (shared-prefix workload): one new token per sequence
+    # cache-write step: one new token per sequence
     key: Optional[np.ndarray] = None
     value: Optional[np.ndarray] = None
     new_pos: Optional[np.ndarray] = None
@@ -246,13 +246,13 @@ def make_inputs(w: Workload, seed: int, fill_values: bool = True) -> DecodeInput
         fill_normal_fp16(k_cache, ss_k, w.sigma)
         fill_normal_fp16(v_cache, ss_v, w.sigma)
     inp = DecodeInputs(w, seed, seq_lens, bt, NB, q, k_cache, v_cache)
-    if w.group_size:
-        rng_new = np.random.default_rng(ss_new)
-        shape = (w.num_seqs, w.num_kv_heads, w.head_size)
-        inp.key = (rng_new.standard_normal(shape, dtype=np.float32) * np.float32(w.sigma)).astype(np.float16)
-        inp.value = (rng_new.standard_normal(shape, dtype=np.float32) * np.float32(w.sigma)).astype(np.float16)
-        # the new token sits at logical position L_s - 1 (appended, then attended)
-        inp.new_pos = (seq_lens.astype(np.int64) - 1)
+    # the decode step's new token per sequence: written to the cache at
+    # logical position L_s - 1, then attended (append, then attend)
+    rng_new = np.random.default_rng(ss_new)
+    shape = (w.num_seqs, w.num_kv_heads, w.head_size)
+    inp.key = (rng_new.standard_normal(shape, dtype=np.float32) * np.float32(w.sigma)).astype(np.float16)
+    inp.value = (rng_new.standard_normal(shape, dtype=np.float32) * np.float32(w.sigma)).astype(np.float16)
+    inp.new_pos = np.maximum(seq_lens.astype(np.int64) - 1, 0)
     return inp
 
 
@@ -264,9 +264,10 @@ def slot_of(block_tables: np.ndarray, seq: int, pos: int, block_size: int) -> in
 
 
 def new_token_slots(inp: DecodeInputs) -> np.ndarray:
-    """slot_mapping (int64) for the cache-write step's new tokens."""
+    """slot_mapping (int64) for the cache-write step's new tokens (-1, i.e.
+    skip, for an empty sequence)."""
     B = inp.workload.block_size
-    return np.array([slot_of(inp.block_tables, s, int(p), B)
+    return np.array([slot_of(inp.block_tables, s, int(p), B) if inp.seq_lens[s] > 0 else -1
                      for s, p in enumerate(inp.new_pos)], dtype=np.int64)
 
 
