@@ -1,0 +1,140 @@
+"""GPU parity at the full workload sizes, in the launch configuration bench.py
+times (the same calls on the same shapes): one decode step -- the cache write
+of each sequence's new token, then v1 or v2 + reduce -- checked on sampled
+(sequence, head) rows against the oracle, plus properties that hold at any
+size (shared prefix == private copies, a planted needle at 128K context)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_302_amd as pa
+import workloads as wl
+from tests._util import assert_parity, device, to_dev
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+class Step:
+    """Device copies of one workload instance and the decode step bench.py runs."""
+
+    def __init__(self, inp):
+        self.inp = inp
+        w = inp.workload
+        self.w = w
+        self.q = to_dev(inp.q)
+        self.kc = to_dev(inp.k_cache)
+        self.vc = to_dev(inp.v_cache)
+        self.bt = to_dev(inp.block_tables)
+        self.sl = to_dev(inp.seq_lens)
+        self.slots = wl.new_token_slots(inp)
+        self.key, self.val, self.slot_d = to_dev(inp.key), to_dev(inp.value), to_dev(self.slots)
+        S, H, D = inp.q.shape
+        self.P = pa.pa_v2_max_partitions(w.max_seq_len, w.partition_size)
+        self.tmp, self.es, self.ml = pa.v2_scratch(S, H, D, self.P, device())
+        self.out = torch.empty((S, H, D), dtype=torch.float32, device=device())
+
+    def run(self, kernel):
+        pa.reshape_and_cache(self.key, self.val, self.kc, self.vc, self.slot_d)
+        if kernel == "v2":
+            pa.pa_decode_v2(self.tmp, self.es, self.ml, self.q, self.kc, self.vc, self.bt, self.sl,
+                            self.inp.scale, self.w.partition_size)
+            pa.pa_reduce(self.out, self.tmp, self.es, self.ml, self.sl, self.w.partition_size)
+        else:
+            pa.pa_decode_v1(self.out, self.q, self.kc, self.vc, self.bt, self.sl, self.inp.scale)
+        return self.out.cpu().numpy()
+
+    def host_after_write(self):
+        """Apply the same cache write to the host pools (oracle scatter)."""
+        oracle.reshape_and_cache(self.inp.key, self.inp.value, self.inp.k_cache, self.inp.v_cache,
+                                 self.slots, self.w.block_size, inplace=True)
+
+
+def sample_heads(w, seq_lens, n_seq=4, seed=0):
+    rng = np.random.default_rng(seed)
+    S, H = w.num_seqs, w.num_heads
+    seqs = {0, S - 1, int(np.argmax(seq_lens)), int(np.argmin(seq_lens))}
+    seqs |= set(int(s) for s in rng.choice(S, size=min(S, n_seq), replace=False))
+    pairs = []
+    for s in sorted(seqs):
+        hs = {0, H - 1} | set(int(h) for h in rng.choice(H, size=min(H, 4), replace=False))
+        pairs += [(s, h) for h in sorted(hs)]
+    return pairs
+
+
+@pytest.mark.parametrize("name,kernel", [
+    ("gqa7b", "v1"), ("gqa7b", "v2"), ("mha7b", "v1"), ("mha7b", "v2"),
+    ("long_gqa", "v2"), ("shared_prefix", "v2"),
+])
+def test_full_workload_step_sampled_parity(name, kernel):
+    w = wl.WORKLOADS[name]
+    inp = wl.make_inputs(w, {"gqa7b": 2, "mha7b": 3, "long_gqa": 4, "shared_prefix": 5}[name])
+    st = Step(inp)
+    out = st.run(kernel)
+    assert np.isfinite(out).all()
+    st.host_after_write()
+    pairs = sample_heads(w, inp.seq_lens)
+    ref = oracle.paged_decode(inp.q, inp.k_cache, inp.v_cache, inp.block_tables, inp.seq_lens,
+                              inp.scale, w.block_size, heads=pairs)
+    idx = tuple(np.array(pairs).T)
+    assert_parity(out[idx], ref[idx], f"{name} {kernel}")
+    # the cache write itself, read back at the written slots
+    kc = st.kc.cpu().numpy()
+    assert kc.tobytes() == inp.k_cache.tobytes()
+
+
+def test_shared_prefix_equals_private_copies_bit_exact():
+    """Sequences that share their prefix blocks (one physical copy, referenced
+    by every table of the group) give bit-identical outputs to the same
+    sequences with the prefix copied into private blocks."""
+    w = wl.WORKLOADS["shared_prefix"]
+    inp = wl.make_inputs(w, 5)
+    shared = Step(inp).run("v2")
+    B = w.block_size
+    pre = w.prefix_len // B
+    NB = inp.num_blocks
+    n_groups = w.num_seqs // w.group_size
+    extra = n_groups * (w.group_size - 1) * pre
+    kc = np.concatenate([inp.k_cache, np.empty((extra,) + inp.k_cache.shape[1:], np.float16)])
+    vc = np.concatenate([inp.v_cache, np.empty((extra,) + inp.v_cache.shape[1:], np.float16)])
+    bt = inp.block_tables.copy()
+    nxt = NB
+    for s in range(w.num_seqs):
+        if s % w.group_size == 0:
+            continue                       # the group's first sequence keeps the originals
+        for i in range(pre):
+            kc[nxt] = inp.k_cache[bt[s, i]]
+            vc[nxt] = inp.v_cache[bt[s, i]]
+            bt[s, i] = nxt
+            nxt += 1
+    assert nxt == kc.shape[0]
+    priv = wl.DecodeInputs(w, inp.seed, inp.seq_lens, bt, kc.shape[0], inp.q, kc, vc,
+                           key=inp.key, value=inp.value, new_pos=inp.new_pos)
+    private = Step(priv).run("v2")
+    assert np.array_equal(shared, private)
+
+
+def test_long_context_needle():
+    """At 32K-128K context the outputs of random data are ~1e-3, so plant a
+    needle: for one sequence, the key of one token of KV head 0 is set to
+    alpha * q/|q| of query head 0 (alpha = 30), which takes nearly all of head
+    0's softmax weight.  The GPU output of that head must follow the oracle
+    closely at an O(1) magnitude."""
+    w = wl.WORKLOADS["long_gqa"]
+    inp = wl.make_inputs(w, 14)
+    s = 3
+    L = int(inp.seq_lens[s])
+    t_star = L // 3
+    b, o = int(inp.block_tables[s, t_star // 16]), t_star % 16
+    qv = inp.q[s, 0].astype(np.float64)
+    k_star = (30.0 * qv / np.linalg.norm(qv)).astype(np.float16)
+    inp.k_cache[b, 0, :, o, :] = k_star.reshape(16, 8)
+    st = Step(inp)
+    out = st.run("v2")
+    st.host_after_write()
+    ref = oracle.paged_decode(inp.q, inp.k_cache, inp.v_cache, inp.block_tables, inp.seq_lens,
+                              inp.scale, 16, heads=[(s, 0), (s, 1)])
+    v_star = inp.v_cache[b, 0, :, o].astype(np.float64)
+    # the needle dominates: the output is close to v*
+    assert np.abs(ref[s, 0] - v_star).max() < 0.2
+    assert_parity(out[s, 0:2], ref[s, 0:2], "needle")
