@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU time budget of the oracle baseline sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the steps, run three plain device copies of exactly 1 GiB "
+                         "(the known-size reference for rocprofv3 FETCH_SIZE/WRITE_SIZE)")
     return ap.parse_args()
 
 
@@ -210,6 +213,15 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     ms_per_step = elapsed * 1e3 / args.steps
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cache_ms = [e[0].elapsed_time(e[1]) for e in evs]
     decode_ms = [e[1].elapsed_time(e[2]) for e in evs]
