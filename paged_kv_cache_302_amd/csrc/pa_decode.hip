@@ -54,7 +54,33 @@
 #include "pa_device.h"
 #include "pa_host.h"
 
+// Compile-time tuning knobs (defaults are the measured best on MI355X).
+#ifndef PA_PREFETCH_TILES
+#define PA_PREFETCH_TILES 2   // K/V tiles held in registers per wave (2 = one block ahead)
+#endif
+#ifndef PA_NT_LOADS
+#define PA_NT_LOADS 1         // nontemporal K/V loads (streamed once: +9% on MI355X)
+#endif
+#ifndef PA_V2_WAVES
+#define PA_V2_WAVES 0         // waves per v2 workgroup (0 = heuristic)
+#endif
+#ifndef PA_V1_WAVES
+#define PA_V1_WAVES 0         // waves per v1 workgroup (0 = heuristic)
+#endif
+#ifndef PA_UNIT_ORDER
+#define PA_UNIT_ORDER 0       // v2 grid order: 0 = KV heads fastest, 1 = partitions fastest
+#endif
+
 namespace pa {
+
+template <class T>
+__device__ __forceinline__ T ld_stream(const T* p) {
+#if PA_NT_LOADS
+    return __builtin_nontemporal_load(p);
+#else
+    return *p;
+#endif
+}
 
 struct DecodeParams {
     float* out;           // v1: out[S,H,D]; v2: tmp_out[S,H,P,D]
@@ -162,9 +188,9 @@ struct MfmaPath {
         const f16x8* kp = reinterpret_cast<const f16x8*>(kt) + l;
         const f16x4* vp = reinterpret_cast<const f16x4*>(vt) + 4 * i + g;
 #pragma unroll
-        for (int c = 0; c < KC; ++c) t.k[c] = kp[64 * c];
+        for (int c = 0; c < KC; ++c) t.k[c] = ld_stream(kp + 64 * c);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) t.v[nt] = vp[64 * nt];
+        for (int nt = 0; nt < NT; ++nt) t.v[nt] = ld_stream(vp + 64 * nt);
     }
 
     __device__ __forceinline__ static void process(State& st, Tile& t, const QRegs& qr,
@@ -274,9 +300,9 @@ struct ValuPath {
         const f16x8* kp = reinterpret_cast<const f16x8*>(kt) + l;
         const f16x8* vp = reinterpret_cast<const f16x8*>(vt) + l;
 #pragma unroll
-        for (int c = 0; c < KC; ++c) t.k[c] = kp[64 * c];
+        for (int c = 0; c < KC; ++c) t.k[c] = ld_stream(kp + 64 * c);
 #pragma unroll
-        for (int c = 0; c < KC; ++c) t.v[c] = vp[64 * c];
+        for (int c = 0; c < KC; ++c) t.v[c] = ld_stream(vp + 64 * c);
     }
 
     __device__ __forceinline__ static void process(State& st, Tile& t, const QRegs& qr,
@@ -360,6 +386,16 @@ __device__ __forceinline__ int n_parts(int L, int PS, int Pmax) {
     return n < Pmax ? n : Pmax;
 }
 
+__device__ int total_partitions(const DecodeParams& p) {
+    int total = 0;
+    for (int s0 = 0; s0 < p.num_seqs; s0 += 64) {
+        const int s = s0 + lane_id();
+        float np = (s < p.num_seqs) ? (float)n_parts(p.seq_lens[s], p.partition_size, p.max_num_partitions) : 0.f;
+        total += (int)wave_sum(np);
+    }
+    return __builtin_amdgcn_readfirstlane(total);
+}
+
 __device__ bool find_partition(const DecodeParams& p, int r, int& s_out, int& p_out) {
     const int lane = lane_id();
     int base = 0;  // partitions of the sequences before this chunk (uniform)
@@ -394,7 +430,21 @@ __global__ __launch_bounds__(64 * NW) void pa_decode_kernel(DecodeParams p) {
     extern __shared__ float lds[];
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index, uniform
     const int kvhc_count = p.num_kv_heads * p.head_chunks;
+#if PA_UNIT_ORDER == 1
+    int kvhc, r_unit;
+    if constexpr (V2) {
+        const int R = total_partitions(p);
+        if ((int)blockIdx.x >= R * kvhc_count) return;
+        kvhc = blockIdx.x / R;
+        r_unit = blockIdx.x % R;
+    } else {
+        kvhc = blockIdx.x % kvhc_count;
+        r_unit = blockIdx.x / kvhc_count;
+    }
+#else
     const int kvhc = blockIdx.x % kvhc_count;
+    const int r_unit = blockIdx.x / kvhc_count;
+#endif
     const int kvh = kvhc / p.head_chunks;
     const int hc = kvhc - kvh * p.head_chunks;
     const int h0 = kvh * p.group + hc * Path::kHeads;
@@ -403,9 +453,9 @@ __global__ __launch_bounds__(64 * NW) void pa_decode_kernel(DecodeParams p) {
 
     int s, part = 0;
     if constexpr (V2) {
-        if (!find_partition(p, blockIdx.x / kvhc_count, s, part)) return;
+        if (!find_partition(p, r_unit, s, part)) return;
     } else {
-        s = blockIdx.x / kvhc_count;
+        s = r_unit;
     }
     const int L = p.seq_lens[s];
     const size_t out_head_stride = V2 ? (size_t)p.max_num_partitions * D : (size_t)D;
@@ -449,35 +499,64 @@ __global__ __launch_bounds__(64 * NW) void pa_decode_kernel(DecodeParams p) {
     if (n > 0) {
         TableWindow<NW> tw;
         tw.init(row, first, n);
+        int ph = 0;
+        // physical id of the wave's j-th block; past the wave's last block the
+        // previous id is repeated (a re-read that hits the cache), so every
+        // tile request is unconditional and the wait counts before each use
+        // are exact: a conditional request makes the compiler wait on the
+        // newer loads too
+        auto phys = [&](int j) {
+            if (j < n) {
+                const int v = tw.get(j);
+                if (v >= 0 && v < p.num_blocks) ph = v; else bad = true;
+            }
+            return ph;
+        };
+        auto tile_k = [&](int id) { return kbase + (size_t)id * blk_stride; };
+        auto tile_v = [&](int id) { return vbase + (size_t)id * blk_stride; };
+        auto valid = [&](int k) { return min(kBlock, tok_end - (first + k * NW) * kBlock); };
         typename Path::Tile ta, tb;
-        auto addr_ok = [&](int phys) { return phys >= 0 && phys < p.num_blocks; };
-        int ph = tw.get(0);
-        if (!addr_ok(ph)) { bad = true; ph = 0; }
-        Path::load(ta, kbase + (size_t)ph * blk_stride, vbase + (size_t)ph * blk_stride);
         int k = 0;
-        // Two tiles in flight: block k+1 is requested before block k is
-        // processed.  The request is unconditional (past the wave's last block
-        // it re-reads the current one, a cache hit) so that the wait counts
-        // before each use are exact and never include the newer loads.
-        while (true) {
-            int nv = min(kBlock, tok_end - (first + k * NW) * kBlock);
-            if (k + 1 < n) {
-                const int ph1 = tw.get(k + 1);
-                if (addr_ok(ph1)) ph = ph1; else bad = true;
+        if constexpr (PA_PREFETCH_TILES == 3) {
+            // three tiles in registers: blocks k+1 and k+2 in flight while k is processed
+            typename Path::Tile tc;
+            int id = phys(0);
+            Path::load(ta, tile_k(id), tile_v(id));
+            id = phys(1);
+            Path::load(tb, tile_k(id), tile_v(id));
+            while (true) {
+                id = phys(k + 2);
+                Path::load(tc, tile_k(id), tile_v(id));
+                Path::process(st, ta, qr, valid(k), sl2);
+                tw.advance(k);
+                if (++k >= n) break;
+                id = phys(k + 2);
+                Path::load(ta, tile_k(id), tile_v(id));
+                Path::process(st, tb, qr, valid(k), sl2);
+                tw.advance(k);
+                if (++k >= n) break;
+                id = phys(k + 2);
+                Path::load(tb, tile_k(id), tile_v(id));
+                Path::process(st, tc, qr, valid(k), sl2);
+                tw.advance(k);
+                if (++k >= n) break;
             }
-            Path::load(tb, kbase + (size_t)ph * blk_stride, vbase + (size_t)ph * blk_stride);
-            Path::process(st, ta, qr, nv, sl2);
-            tw.advance(k);
-            if (++k >= n) break;
-            nv = min(kBlock, tok_end - (first + k * NW) * kBlock);
-            if (k + 1 < n) {
-                const int ph1 = tw.get(k + 1);
-                if (addr_ok(ph1)) ph = ph1; else bad = true;
+        } else {
+            // two tiles in registers: block k+1 in flight while k is processed
+            int id = phys(0);
+            Path::load(ta, tile_k(id), tile_v(id));
+            while (true) {
+                id = phys(k + 1);
+                Path::load(tb, tile_k(id), tile_v(id));
+                Path::process(st, ta, qr, valid(k), sl2);
+                tw.advance(k);
+                if (++k >= n) break;
+                id = phys(k + 1);
+                Path::load(ta, tile_k(id), tile_v(id));
+                Path::process(st, tb, qr, valid(k), sl2);
+                tw.advance(k);
+                if (++k >= n) break;
             }
-            Path::load(ta, kbase + (size_t)ph * blk_stride, vbase + (size_t)ph * blk_stride);
-            Path::process(st, tb, qr, nv, sl2);
-            tw.advance(k);
-            if (++k >= n) break;
         }
     }
 
@@ -637,7 +716,7 @@ extern "C" int pa_decode_v1(float* out, const void* q, const void* k_cache, cons
     p.out = out;
     const long long units = (long long)num_seqs * num_kv_heads * p.head_chunks;
     if (units > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
-    const int nw = pick_waves(units, max_blocks_per_seq);
+    const int nw = PA_V1_WAVES ? PA_V1_WAVES : pick_waves(units, max_blocks_per_seq);
     return launch_decode<false>(p, head_size, nw, (int)units, as_stream(stream));
 }
 
@@ -670,6 +749,6 @@ extern "C" int pa_decode_v2(float* tmp_out, float* exp_sums, float* max_logits, 
     p.partition_size = partition_size;
     const long long units = (long long)num_seqs * num_kv_heads * p.head_chunks * max_num_partitions;
     if (units > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
-    const int nw = pick_waves(units / 2, partition_size / 16);
+    const int nw = PA_V2_WAVES ? PA_V2_WAVES : pick_waves(units / 2, partition_size / 16);
     return launch_decode<true>(p, head_size, nw, (int)units, as_stream(stream));
 }
