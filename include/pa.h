@@ -102,15 +102,19 @@ PA_API int pa_v2_max_partitions(int max_seq_len, int partition_size);
  *
  * Partition p of sequence s covers tokens [p*PS, min((p+1)*PS, L)),
  * p < ceil(L/PS).  For each query head h it writes
- *     max_logits[s,h,p] = m_p = max_t z_t          (z_t = scale * q . K_t)
- *     exp_sums[s,h,p]   = l_p = sum_t exp(z_t - m_p)
- *     tmp_out[s,h,p,:]  = sum_t exp(z_t - m_p) V_t / l_p
+ *     max_logits[s,p,h] = m_p = max_t z_t          (z_t = scale * q . K_t)
+ *     exp_sums[s,p,h]   = l_p = sum_t exp(z_t - m_p)
+ *     tmp_out[s,p,h,:]  = sum_t exp(z_t - m_p) V_t / l_p
  * in natural-log units.  Entries with p >= ceil(L/PS) are not written.
- * pa_reduce merges them into the final output.
+ * pa_reduce merges them into the final output.  The partition index comes
+ * before the head index so that the query heads of one KV group -- the
+ * results of one work unit -- are one contiguous run of whole cache lines:
+ * writes scattered through the K/V read stream cost DRAM read/write
+ * turnarounds.
  *
- *   tmp_out     [num_seqs, num_heads, max_num_partitions, head_size] fp32 scratch
- *   exp_sums    [num_seqs, num_heads, max_num_partitions] fp32 scratch
- *   max_logits  [num_seqs, num_heads, max_num_partitions] fp32 scratch
+ *   tmp_out     [num_seqs, max_num_partitions, num_heads, head_size] fp32 scratch
+ *   exp_sums    [num_seqs, max_num_partitions, num_heads] fp32 scratch
+ *   max_logits  [num_seqs, max_num_partitions, num_heads] fp32 scratch
  *   other arguments as in pa_decode_v1;
  *   partition_size: a positive multiple of 16;
  *   max_num_partitions: >= ceil(L/PS) for every sequence (a longer sequence
@@ -129,7 +133,7 @@ PA_API int pa_decode_v2(float* tmp_out, float* exp_sums, float* max_logits,
  * say only "merged afterwards"; this is the exact merge).
  *
  * With n = ceil(L/PS), M = max_{p<n} m_p and w_p = l_p exp(m_p - M):
- *     out[s,h,:] = sum_{p<n} (w_p / sum_q w_q) tmp_out[s,h,p,:]
+ *     out[s,h,:] = sum_{p<n} (w_p / sum_q w_q) tmp_out[s,p,h,:]
  * n = 0 gives zeros; n > max_num_partitions gives NaN.
  *
  *   out [num_seqs, num_heads, head_size] fp32, written; the other arrays as

@@ -142,15 +142,15 @@ def pa_decode_v1(out, q, k_cache, v_cache, block_tables, seq_lens, scale: float,
 
 def pa_decode_v2(tmp_out, exp_sums, max_logits, q, k_cache, v_cache, block_tables, seq_lens,
                  scale: float, partition_size: int, stream=None):
-    """Per-partition partials (tmp_out[S,H,P,D], exp_sums/max_logits[S,H,P])."""
+    """Per-partition partials (tmp_out[S,P,H,D], exp_sums/max_logits[S,P,H])."""
     S, H, KVH, D, B, NB, MB = _decode_common(q, k_cache, v_cache, block_tables, seq_lens)
     _want(tmp_out, "tmp_out", torch.float32, 4, q.device)
     _want(exp_sums, "exp_sums", torch.float32, 3, q.device)
     _want(max_logits, "max_logits", torch.float32, 3, q.device)
-    P = tmp_out.shape[2]
-    if tuple(tmp_out.shape) != (S, H, P, D) or tuple(exp_sums.shape) != (S, H, P) or \
-            tuple(max_logits.shape) != (S, H, P):
-        raise ValueError("v2 scratch shapes must be [S,H,P,D] and [S,H,P]")
+    P = tmp_out.shape[1]
+    if tuple(tmp_out.shape) != (S, P, H, D) or tuple(exp_sums.shape) != (S, P, H) or \
+            tuple(max_logits.shape) != (S, P, H):
+        raise ValueError("v2 scratch shapes must be [S,P,H,D] and [S,P,H]")
     lib = load_library()
     rc = lib.pa_decode_v2(_p(tmp_out), _p(exp_sums), _p(max_logits), _p(q), _p(k_cache),
                           _p(v_cache), _p(block_tables), _p(seq_lens), S, H, KVH, D, B, MB, NB,
@@ -166,12 +166,13 @@ def pa_reduce(out, tmp_out, exp_sums, max_logits, seq_lens, partition_size: int,
     _want(max_logits, "max_logits", torch.float32, 3, dev)
     _want(seq_lens, "seq_lens", torch.int32, 1, dev)
     _want(out, "out", torch.float32, 3, dev)
-    S, H, P, D = tmp_out.shape
-    if tuple(out.shape) != (S, H, D) or seq_lens.shape[0] != S:
-        raise ValueError("out must be [S,H,D] and seq_lens [S]")
+    S, P, H, D = tmp_out.shape
+    if tuple(out.shape) != (S, H, D) or seq_lens.shape[0] != S or \
+            tuple(exp_sums.shape) != (S, P, H) or tuple(max_logits.shape) != (S, P, H):
+        raise ValueError("out must be [S,H,D], partials [S,P,H,D] / [S,P,H], seq_lens [S]")
     lib = load_library()
-    rc = lib.pa_reduce(_p(out), _p(tmp_out), _p(exp_sums), _p(max_logits), _p(seq_lens), S, H, D, P,
-                       int(partition_size), _stream(out, stream))
+    rc = lib.pa_reduce(_p(out), _p(tmp_out), _p(exp_sums), _p(max_logits), _p(seq_lens), S, H, D,
+                       P, int(partition_size), _stream(out, stream))
     _check(rc, "pa_reduce")
     return out
 
@@ -223,9 +224,9 @@ def paged_attention_v1(q, k_cache, v_cache, block_tables, seq_lens, scale: float
 
 
 def v2_scratch(num_seqs: int, num_heads: int, head_size: int, max_num_partitions: int, device):
-    tmp = torch.empty((num_seqs, num_heads, max_num_partitions, head_size), dtype=torch.float32,
+    tmp = torch.empty((num_seqs, max_num_partitions, num_heads, head_size), dtype=torch.float32,
                       device=device)
-    es = torch.empty((num_seqs, num_heads, max_num_partitions), dtype=torch.float32, device=device)
+    es = torch.empty((num_seqs, max_num_partitions, num_heads), dtype=torch.float32, device=device)
     ml = torch.empty_like(es)
     return tmp, es, ml
 

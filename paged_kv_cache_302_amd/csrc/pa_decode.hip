@@ -82,6 +82,22 @@ __device__ __forceinline__ T ld_stream(const T* p) {
 #endif
 }
 
+// Results are written once and not re-read by this kernel.  Plain stores
+// allocate in L2 and reach HBM mid-stream, where each write burst costs a
+// read/write turnaround: the partials of a 3.5 GB long-context call (27 MB)
+// cost ~9% of its time as plain stores and ~3% as nontemporal ones.
+#ifndef PA_NT_STORES
+#define PA_NT_STORES 1
+#endif
+template <class T>
+__device__ __forceinline__ void st_stream(T* p, T v) {
+#if PA_NT_STORES
+    __builtin_nontemporal_store(v, p);
+#else
+    *p = v;
+#endif
+}
+
 struct DecodeParams {
     float* out;           // v1: out[S,H,D]; v2: tmp_out[S,H,P,D]
     float* exp_sums;      // v2: [S,H,P]
@@ -230,21 +246,6 @@ struct MfmaPath {
     // Per-head totals of the wave: l summed over the four token groups.
     __device__ static float wave_l(const State& st) { return col4_sum(st.l); }
 
-    // Write the wave's normalised result for heads < nh directly.
-    __device__ static void store_direct(const State& st, float ltot, float* dst_head0,
-                                        size_t head_stride, int nh, bool bad) {
-        const int l = lane_id(), i = l & 15, g = l >> 4;
-        if (i >= nh) return;
-        const float inv = 1.f / ltot;
-        float* row = dst_head0 + (size_t)i * head_stride;
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            f32x4 o = st.acc[nt] * inv;
-            if (bad) o = f32x4{NAN, NAN, NAN, NAN};
-            *reinterpret_cast<f32x4*>(row + 16 * nt + 4 * g) = o;
-        }
-    }
-
     // Stage the wave's state for the cross-wave merge: acc[h][d] unnormalised.
     __device__ static void stage(const State& st, float ltot, float* s_acc, float* s_m,
                                  float* s_l, int nh) {
@@ -350,17 +351,6 @@ struct ValuPath {
 
     __device__ static float wave_l(const State& st) { return row16_sum(st.l); }
 
-    __device__ static void store_direct(const State& st, float ltot, float* dst_head0,
-                                        size_t, int, bool bad) {
-        const int l = lane_id();
-        const float inv = 1.f / ltot;
-#pragma unroll
-        for (int c = 0; c < KC; ++c) {
-            const float full = st.acc[c] + dpp<kDppXor1>(st.acc[c]);
-            if ((l & 1) == 0) dst_head0[32 * c + (l >> 1)] = bad ? NAN : full * inv;
-        }
-    }
-
     __device__ static void stage(const State& st, float ltot, float* s_acc, float* s_m,
                                  float* s_l, int) {
         const int l = lane_id();
@@ -458,13 +448,16 @@ __global__ __launch_bounds__(64 * NW) void pa_decode_kernel(DecodeParams p) {
         s = r_unit;
     }
     const int L = p.seq_lens[s];
-    const size_t out_head_stride = V2 ? (size_t)p.max_num_partitions * D : (size_t)D;
-    float* out_h0 = V2 ? p.out + (((size_t)s * p.num_heads + h0) * p.max_num_partitions + part) * D
-                       : p.out + ((size_t)s * p.num_heads + h0) * D;
+    // v1 out[S][H][D]; v2 tmp_out[S][P][H][D]: either way the unit's heads
+    // are consecutive rows, so its result is one contiguous run of memory
+    const size_t out_head_stride = D;
+    const size_t row0 = V2 ? ((size_t)s * p.max_num_partitions + part) * p.num_heads + h0
+                           : (size_t)s * p.num_heads + h0;
+    float* out_h0 = p.out + row0 * D;   // exp_sums / max_logits [S][P][H]: index row0 + j
 
     if (!V2 && L <= 0) {  // empty sequence: zeros (v2 has no partition for it)
         for (int e = threadIdx.x; e < nh * D; e += 64 * NW)
-            out_h0[(size_t)(e / D) * out_head_stride + (e % D)] = 0.f;
+            st_stream(out_h0 + (size_t)(e / D) * out_head_stride + (e % D), 0.f);
         return;
     }
     const int nb_seq = (L + kBlock - 1) / kBlock;
@@ -562,14 +555,30 @@ __global__ __launch_bounds__(64 * NW) void pa_decode_kernel(DecodeParams p) {
 
     const float ltot = Path::wave_l(st);
     if constexpr (NW == 1) {
-        Path::store_direct(st, ltot, out_h0, out_head_stride, nh, bad);
+        // The unit's result (nh rows of D, one contiguous run) goes out as
+        // whole 1 KiB-per-instruction stores: stage the rows in LDS (this
+        // wave only, so program order orders the accesses), then each lane
+        // writes 16 contiguous bytes.  Storing straight from the MFMA layout
+        // would write every cache line in two halves from two instructions.
+        const int HP = Path::kHeads;
+        float* s_o = lds;                 // [nh][D]
+        float* s_m = lds + nh * D;        // [HP]
+        float* s_l = s_m + HP;            // [HP]
+        Path::stage(st, ltot, s_o, s_m, s_l, nh);
+        const f32x4* src = reinterpret_cast<const f32x4*>(s_o);
+        const int nv = nh * D / 4;
+        for (int e = lane_id(); e < nv; e += 64) {
+            const float inv = 1.f / s_l[(4 * e) / D];
+            f32x4 v = src[e] * inv;
+            if (bad) v = f32x4{NAN, NAN, NAN, NAN};
+            st_stream(reinterpret_cast<f32x4*>(out_h0) + e, v);
+        }
         if constexpr (V2) {
+            // lane l < nh holds head l's max and total weight on both paths
             const int l = lane_id();
             if (l < nh) {
-                // lane l < nh holds head l's max and total weight on both paths
-                const size_t idx = ((size_t)s * p.num_heads + h0 + l) * p.max_num_partitions + part;
-                p.max_logits[idx] = bad ? NAN : st.m * p.scale;
-                p.exp_sums[idx] = bad ? NAN : ltot;
+                st_stream(p.max_logits + row0 + l, bad ? NAN : st.m * p.scale);
+                st_stream(p.exp_sums + row0 + l, bad ? NAN : ltot);
             }
         }
         return;
@@ -580,6 +589,7 @@ __global__ __launch_bounds__(64 * NW) void pa_decode_kernel(DecodeParams p) {
         float* s_m = lds + NW * nh * D;                  // [NW][HP]
         float* s_l = s_m + NW * HP;                      // [NW][HP]
         int* s_bad = reinterpret_cast<int*>(s_l + NW * HP);  // [NW]
+        float* s_fin = reinterpret_cast<float*>(s_bad + NW);  // [2][16]: merged m, l
         Path::stage(st, ltot, s_acc + w * nh * D, s_m + w * HP, s_l + w * HP, nh);
         if (lane_id() == 0) s_bad[w] = bad ? 1 : 0;
         __syncthreads();
@@ -598,13 +608,18 @@ __global__ __launch_bounds__(64 * NW) void pa_decode_kernel(DecodeParams p) {
                 num += s_acc[(v * nh + j) * D + d] * f;
                 den += s_l[v * HP + j] * f;
             }
-            out_h0[(size_t)j * out_head_stride + d] = any_bad ? NAN : num / den;
-            if constexpr (V2) {
-                if (d == 0) {
-                    const size_t idx = ((size_t)s * p.num_heads + h0 + j) * p.max_num_partitions + part;
-                    p.max_logits[idx] = any_bad ? NAN : M * p.scale;
-                    p.exp_sums[idx] = any_bad ? NAN : den;
-                }
+            st_stream(out_h0 + (size_t)j * out_head_stride + d, any_bad ? NAN : num / den);
+            if (V2 && d == 0) {
+                s_fin[j] = M;
+                s_fin[16 + j] = den;
+            }
+        }
+        if constexpr (V2) {
+            __syncthreads();
+            const int t = threadIdx.x;
+            if (t < nh) {
+                st_stream(p.max_logits + row0 + t, any_bad ? NAN : s_fin[t] * p.scale);
+                st_stream(p.exp_sums + row0 + t, any_bad ? NAN : s_fin[16 + t]);
             }
         }
     }
@@ -614,8 +629,9 @@ __global__ __launch_bounds__(64 * NW) void pa_decode_kernel(DecodeParams p) {
 // Host side
 // --------------------------------------------------------------------------
 static size_t merge_lds_bytes(int NW, int nh_max, int D, int hp) {
-    if (NW == 1) return 0;
-    return (size_t)NW * ((size_t)nh_max * D + 2 * hp) * sizeof(float) + NW * sizeof(int);
+    // NW == 1: the staging buffer of the final store; NW > 1: the merge
+    return (size_t)NW * ((size_t)nh_max * D + 2 * hp) * sizeof(float) + NW * sizeof(int) +
+           32 * sizeof(float);
 }
 
 template <class Path, int D, bool V2>

@@ -5,11 +5,14 @@
 // over p < ceil(L / PS).  Each weight is divided by the total before the
 // sum, so a single partition comes back bit-exactly (w / w = 1).
 //
-// One workgroup of 4 wavefronts per (sequence, query head).  The partials'
-// m_p and l_p are read by all threads (two short passes: the max, then the
-// weight sum); the o_p rows are split across the waves (wave w takes
-// p = w, w+4, ...), each lane owning D/64 consecutive head dims, with four
-// rows in flight per wave; the four wave sums are added in LDS.
+// The kernel is latency-bound (tens of MB spread over a few hundred rows of
+// partials), so it is built to cost about one memory round trip: one
+// workgroup of 16 wavefronts per (sequence, query head); as soon as the
+// length is known every thread requests its m_p / l_p and every wave requests
+// its (up to 16) o_p rows -- the rows do not depend on the weights -- then
+// the max and the weight sum are reduced through LDS, each wave folds its
+// rows with their weights, and the 16 wave sums are added in LDS.  Sequences
+// with more than 256 partitions loop over further chunks of rows.
 #include <math.h>
 
 #include "pa_device.h"
@@ -17,10 +20,13 @@
 
 namespace pa {
 
-constexpr int kReduceWaves = 4;
+constexpr int kReduceWaves = 16;
+constexpr int kReduceRows = 16;                         // o_p rows per wave per chunk
+constexpr int kReduceThreads = 64 * kReduceWaves;
+constexpr int kReduceChunk = kReduceWaves * kReduceRows;  // partitions per chunk
 
 template <int D>
-__global__ __launch_bounds__(64 * kReduceWaves) void pa_reduce_kernel(
+__global__ __launch_bounds__(kReduceThreads) void pa_reduce_kernel(
     float* __restrict__ out, const float* __restrict__ tmp_out, const float* __restrict__ exp_sums,
     const float* __restrict__ max_logits, const int32_t* __restrict__ seq_lens, int num_heads,
     int max_num_partitions, int partition_size) {
@@ -31,21 +37,41 @@ __global__ __launch_bounds__(64 * kReduceWaves) void pa_reduce_kernel(
 
     const int sh = blockIdx.x;  // s * num_heads + h
     const int s = sh / num_heads;
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int L = seq_lens[s];
     float* orow = out + (size_t)sh * D;
     const int n = L > 0 ? (L - 1) / partition_size + 1 : 0;
     if (n == 0 || n > max_num_partitions) {
-        for (int d = tid; d < D; d += 64 * kReduceWaves) orow[d] = (n == 0) ? 0.f : NAN;
+        for (int d = tid; d < D; d += kReduceThreads) orow[d] = (n == 0) ? 0.f : NAN;
         return;
     }
-    const float* m = max_logits + (size_t)sh * max_num_partitions;
-    const float* l = exp_sums + (size_t)sh * max_num_partitions;
-    const float* o = tmp_out + (size_t)sh * max_num_partitions * D;
+    // partials are [S][P][H](x D): consecutive partitions of one (s, h) are
+    // num_heads entries apart
+    const int h = sh - s * num_heads;
+    const size_t base = (size_t)s * max_num_partitions * num_heads + h;
+    const size_t pstride = num_heads;
+    const float* mp = max_logits + base;
+    const float* lp = exp_sums + base;
+    const float* o = tmp_out + base * D + lane * VEC;
+    auto m = [&](int q) { return mp[(size_t)q * pstride]; };
+    auto l = [&](int q) { return lp[(size_t)q * pstride]; };
+
+    // requests: this thread's m_p / l_p (first 1024 partitions) and this
+    // wave's first chunk of rows, all before any reduction
+    const float m0 = tid < n ? m(tid) : -INFINITY;
+    const float l0 = tid < n ? l(tid) : 0.f;
+    vec_t rows[kReduceRows];
+#pragma unroll
+    for (int j = 0; j < kReduceRows; ++j) {
+        const int p = w + kReduceWaves * j;
+        rows[j] = p < n ? __builtin_nontemporal_load(reinterpret_cast<const vec_t*>(o + (size_t)p * pstride * D))
+                        : vec_t{};
+    }
 
     // M = max_p m_p
-    float mx = -INFINITY;
-    for (int p = tid; p < n; p += 64 * kReduceWaves) mx = fmaxf(mx, m[p]);
+    float mx = m0;
+    for (int p = tid + kReduceThreads; p < n; p += kReduceThreads) mx = fmaxf(mx, m(p));
     mx = wave_max(mx);
     if (lane == 0) s_red[w] = mx;
     __syncthreads();
@@ -55,8 +81,9 @@ __global__ __launch_bounds__(64 * kReduceWaves) void pa_reduce_kernel(
     __syncthreads();
 
     // W = sum_p l_p exp(m_p - M)
-    float ws = 0.f;
-    for (int p = tid; p < n; p += 64 * kReduceWaves) ws += l[p] * exp2_fast((m[p] - M) * kLog2e);
+    float ws = tid < n ? l0 * exp2_fast((m0 - M) * kLog2e) : 0.f;
+    for (int p = tid + kReduceThreads; p < n; p += kReduceThreads)
+        ws += l(p) * exp2_fast((m(p) - M) * kLog2e);
     ws = wave_sum(ws);
     if (lane == 0) s_red[w] = ws;
     __syncthreads();
@@ -66,23 +93,23 @@ __global__ __launch_bounds__(64 * kReduceWaves) void pa_reduce_kernel(
 
     // out = sum_p (w_p / W) o_p
     vec_t acc = {};
-    int p = w;
-    for (; p + 3 * kReduceWaves < n; p += 4 * kReduceWaves) {
-        vec_t r[4];
-        float c[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int pp = p + u * kReduceWaves;
-            r[u] = *reinterpret_cast<const vec_t*>(o + (size_t)pp * D + lane * VEC);
-            c[u] = (l[pp] * exp2_fast((m[pp] - M) * kLog2e)) / W;
+    for (int j = 0; j < kReduceRows; ++j) {
+        const int p = w + kReduceWaves * j;
+        if (p < n) acc += ((l(p) * exp2_fast((m(p) - M) * kLog2e)) / W) * rows[j];
+    }
+    for (int chunk = kReduceChunk; chunk < n; chunk += kReduceChunk) {
+#pragma unroll
+        for (int j = 0; j < kReduceRows; ++j) {
+            const int p = chunk + w + kReduceWaves * j;
+            rows[j] = p < n ? __builtin_nontemporal_load(reinterpret_cast<const vec_t*>(o + (size_t)p * pstride * D))
+                            : vec_t{};
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) acc += c[u] * r[u];
-    }
-    for (; p < n; p += kReduceWaves) {
-        const vec_t r = *reinterpret_cast<const vec_t*>(o + (size_t)p * D + lane * VEC);
-        const float c = (l[p] * exp2_fast((m[p] - M) * kLog2e)) / W;
-        acc += c * r;
+        for (int j = 0; j < kReduceRows; ++j) {
+            const int p = chunk + w + kReduceWaves * j;
+            if (p < n) acc += ((l(p) * exp2_fast((m(p) - M) * kLog2e)) / W) * rows[j];
+        }
     }
     s_acc[w][lane] = acc;
     __syncthreads();
@@ -114,11 +141,11 @@ extern "C" int pa_reduce(float* out, const float* tmp_out, const float* exp_sums
     if (grid > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
     hipStream_t st = as_stream(stream);
     if (head_size == 128)
-        hipLaunchKernelGGL(pa_reduce_kernel<128>, dim3((unsigned)grid), dim3(64 * kReduceWaves), 0,
+        hipLaunchKernelGGL(pa_reduce_kernel<128>, dim3((unsigned)grid), dim3(kReduceThreads), 0,
                            st, out, tmp_out, exp_sums, max_logits, seq_lens, num_heads,
                            max_num_partitions, partition_size);
     else
-        hipLaunchKernelGGL(pa_reduce_kernel<64>, dim3((unsigned)grid), dim3(64 * kReduceWaves), 0,
+        hipLaunchKernelGGL(pa_reduce_kernel<64>, dim3((unsigned)grid), dim3(kReduceThreads), 0,
                            st, out, tmp_out, exp_sums, max_logits, seq_lens, num_heads,
                            max_num_partitions, partition_size);
     return launch_status();

@@ -55,7 +55,9 @@ def run_v2(inp, ps, max_seq_len=None):
                     d["seq_lens"], inp.scale, ps)
     out = torch.empty((S, H, D), dtype=torch.float32, device=device())
     pa.pa_reduce(out, tmp, es, ml, d["seq_lens"], ps)
-    return out.cpu().numpy(), tmp.cpu().numpy(), es.cpu().numpy(), ml.cpu().numpy(), P
+    # partials come back [S,P,H,...]; return them [S,H,P,...] like the oracle
+    return (out.cpu().numpy(), tmp.cpu().numpy().transpose(0, 2, 1, 3),
+            es.cpu().numpy().transpose(0, 2, 1), ml.cpu().numpy().transpose(0, 2, 1), P)
 
 
 def ref_out(inp):
@@ -103,9 +105,9 @@ def test_reduce_alone_on_oracle_partials(case):
                                                     inp.block_tables, inp.seq_lens, inp.scale, 16,
                                                     ps, P)
     dev = device()
-    tmp = to_dev(t_ref.astype(np.float32))
-    es = to_dev(e_ref.astype(np.float32))
-    ml = to_dev(m_ref.astype(np.float32))
+    tmp = to_dev(t_ref.astype(np.float32).transpose(0, 2, 1, 3))   # [S,P,H,D]
+    es = to_dev(e_ref.astype(np.float32).transpose(0, 2, 1))
+    ml = to_dev(m_ref.astype(np.float32).transpose(0, 2, 1))
     out = torch.empty((S, H, D), dtype=torch.float32, device=dev)
     pa.pa_reduce(out, tmp, es, ml, to_dev(inp.seq_lens), ps)
     merged = oracle.lse_merge(t_ref, e_ref, m_ref, inp.seq_lens, ps)
