@@ -55,11 +55,8 @@
 #include "pa_host.h"
 
 // Compile-time tuning knobs (defaults are the measured best on MI355X).
-#ifndef PA_PREFETCH_TILES
-#define PA_PREFETCH_TILES 2   // K/V tiles held in registers per wave (2 = one block ahead)
-#endif
 #ifndef PA_NT_LOADS
-#define PA_NT_LOADS 1         // nontemporal K/V loads (streamed once: +9% on MI355X)
+#define PA_NT_LOADS 3         // nontemporal tile loads: bit 0 = K, bit 1 = V
 #endif
 #ifndef PA_V2_WAVES
 #define PA_V2_WAVES 0         // waves per v2 workgroup (0 = heuristic)
@@ -73,12 +70,30 @@
 
 namespace pa {
 
-template <class T>
+template <bool NT, class T>
 __device__ __forceinline__ T ld_stream(const T* p) {
-#if PA_NT_LOADS
-    return __builtin_nontemporal_load(p);
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+constexpr bool kNtK = (PA_NT_LOADS & 1) != 0;   // K tiles
+constexpr bool kNtV = (PA_NT_LOADS & 2) != 0;   // V tiles
+
+#ifndef PA_CPOL
+#define PA_CPOL -1   // >= 0: tile loads as buffer loads with this cache-policy field
+#endif
+// one lane's piece of a K or V tile: `tile` is the wave-uniform tile base,
+// `off` the lane's byte offset in it
+template <bool NT, class T>
+__device__ __forceinline__ T ld_tile(const f16* tile, int off, int tile_bytes) {
+#if PA_CPOL >= 0
+    __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)tile, 0, tile_bytes, 0x00020000);
+    if constexpr (sizeof(T) == 16)
+        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, PA_CPOL));
+    else
+        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, PA_CPOL));
 #else
-    return *p;
+    (void)tile_bytes;
+    return ld_stream<NT>(reinterpret_cast<const T*>(reinterpret_cast<const char*>(tile) + off));
 #endif
 }
 
@@ -123,42 +138,15 @@ struct DecodeParams {
 // --------------------------------------------------------------------------
 // Block-table access: the wave's blocks k = 0..n-1 (logical block
 // first + k*NW) have their physical ids cached 64 at a time in one VGPR
-// (lane j holds entry k0 + j) and are read back with v_readlane.
+// (lane j of window i holds entry 64i + j, clamped to the last entry) and are
+// read back with v_readlane.  Every lane always loads, so a window is a plain
+// unconditional load with nothing to merge afterwards.
 // --------------------------------------------------------------------------
 template <int NW>
-struct TableWindow {
-    const int32_t* row;
-    int first, n;
-    int k0;
-    int cur, nxt;
-
-    __device__ __forceinline__ int load(int kbase) const {
-        const int j = lane_id();
-        const int k = kbase + j;
-        return (k < n) ? row[first + k * NW] : 0;
-    }
-    __device__ __forceinline__ void init(const int32_t* r, int f, int cnt) {
-        row = r;
-        first = f;
-        n = cnt;
-        k0 = 0;
-        cur = load(0);
-        nxt = (n > 64) ? load(64) : 0;
-    }
-    // physical id of the wave's k-th block; k is wave-uniform and k >= k0
-    __device__ __forceinline__ int get(int k) const {
-        const int d = k - k0;
-        return d < 64 ? __builtin_amdgcn_readlane(cur, d) : __builtin_amdgcn_readlane(nxt, d - 64);
-    }
-    // called once block k has been consumed
-    __device__ __forceinline__ void advance(int k) {
-        if (k + 1 - k0 == 64) {
-            k0 += 64;
-            cur = nxt;
-            nxt = (k0 + 64 < n) ? load(k0 + 64) : 0;
-        }
-    }
-};
+__device__ __forceinline__ int table_window(const int32_t* row, int first, int n, int kbase) {
+    const int k = min(kbase + lane_id(), n - 1);
+    return row[first + k * NW];
+}
 
 // --------------------------------------------------------------------------
 // MFMA path (2 <= G): up to 16 query heads of one KV group per wave
@@ -201,12 +189,11 @@ struct MfmaPath {
 
     __device__ __forceinline__ static void load(Tile& t, const f16* kt, const f16* vt) {
         const int l = lane_id(), i = l & 15, g = l >> 4;
-        const f16x8* kp = reinterpret_cast<const f16x8*>(kt) + l;
-        const f16x4* vp = reinterpret_cast<const f16x4*>(vt) + 4 * i + g;
+        constexpr int TB = D * kBlock * 2;
 #pragma unroll
-        for (int c = 0; c < KC; ++c) t.k[c] = ld_stream(kp + 64 * c);
+        for (int c = 0; c < KC; ++c) t.k[c] = ld_tile<kNtK, f16x8>(kt, 16 * (l + 64 * c), TB);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) t.v[nt] = ld_stream(vp + 64 * nt);
+        for (int nt = 0; nt < NT; ++nt) t.v[nt] = ld_tile<kNtV, f16x4>(vt, 8 * (4 * i + g + 64 * nt), TB);
     }
 
     __device__ __forceinline__ static void process(State& st, Tile& t, const QRegs& qr,
@@ -298,12 +285,11 @@ struct ValuPath {
 
     __device__ __forceinline__ static void load(Tile& t, const f16* kt, const f16* vt) {
         const int l = lane_id();
-        const f16x8* kp = reinterpret_cast<const f16x8*>(kt) + l;
-        const f16x8* vp = reinterpret_cast<const f16x8*>(vt) + l;
+        constexpr int TB = D * kBlock * 2;
 #pragma unroll
-        for (int c = 0; c < KC; ++c) t.k[c] = ld_stream(kp + 64 * c);
+        for (int c = 0; c < KC; ++c) t.k[c] = ld_tile<kNtK, f16x8>(kt, 16 * (l + 64 * c), TB);
 #pragma unroll
-        for (int c = 0; c < KC; ++c) t.v[c] = ld_stream(vp + 64 * c);
+        for (int c = 0; c < KC; ++c) t.v[c] = ld_tile<kNtV, f16x8>(vt, 16 * (l + 64 * c), TB);
     }
 
     __device__ __forceinline__ static void process(State& st, Tile& t, const QRegs& qr,
@@ -415,8 +401,15 @@ __device__ bool find_partition(const DecodeParams& p, int r, int& s_out, int& p_
 // --------------------------------------------------------------------------
 // The kernel
 // --------------------------------------------------------------------------
+#ifndef PA_WAVES_PER_EU
+#define PA_WAVES_PER_EU 0
+#endif
 template <class Path, int D, int NW, bool V2>
-__global__ __launch_bounds__(64 * NW) void pa_decode_kernel(DecodeParams p) {
+__global__ __launch_bounds__(64 * NW)
+#if PA_WAVES_PER_EU
+__attribute__((amdgpu_waves_per_eu(PA_WAVES_PER_EU)))
+#endif
+void pa_decode_kernel(DecodeParams p) {
     extern __shared__ float lds[];
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index, uniform
     const int kvhc_count = p.num_kv_heads * p.head_chunks;
@@ -490,67 +483,53 @@ __global__ __launch_bounds__(64 * NW) void pa_decode_kernel(DecodeParams p) {
     const float sl2 = p.scale_log2;
 
     if (n > 0) {
-        TableWindow<NW> tw;
-        tw.init(row, first, n);
-        int ph = 0;
-        // physical id of the wave's j-th block; past the wave's last block the
-        // previous id is repeated (a re-read that hits the cache), so every
-        // tile request is unconditional and the wait counts before each use
-        // are exact: a conditional request makes the compiler wait on the
-        // newer loads too
-        auto phys = [&](int j) {
-            if (j < n) {
-                const int v = tw.get(j);
-                if (v >= 0 && v < p.num_blocks) ph = v; else bad = true;
-            }
-            return ph;
+        // The wave walks its blocks in windows of 64 table entries: `cur` holds
+        // window kw, `nxt` window kw + 64 (requested one window ahead), and
+        // `pend` window kw + 128 (requested as window kw starts, so it has had
+        // 64 blocks of time when it moves up).  Inside a window the tiles are
+        // double-buffered in registers: block k + 1 is requested before block
+        // k is processed.
+        //
+        // Past the wave's last block the last id is requested again (a re-read
+        // that hits the cache), so every tile request is unconditional and the
+        // wait counts before each use are exact: a conditional request makes
+        // the compiler wait on the newer loads too.  The index is clamped
+        // rather than the previous id kept, so the compiler cannot prove two
+        // requests equal and replace one by a register copy (which drops the
+        // nontemporal hint from the request it keeps and drains the queue).
+        // An id outside the pool marks the unit bad and reads block 0.
+        int cur = table_window<NW>(row, first, n, 0);
+        int nxt = table_window<NW>(row, first, n, 64);
+        auto phys = [&](int kw, int j) {
+            const int d = min(j, n - 1) - kw;
+            const int v = d < 64 ? __builtin_amdgcn_readlane(cur, d) : __builtin_amdgcn_readlane(nxt, d - 64);
+            const bool ok = (unsigned)v < (unsigned)p.num_blocks;
+            bad = bad || !ok;
+            return ok ? v : 0;
         };
         auto tile_k = [&](int id) { return kbase + (size_t)id * blk_stride; };
         auto tile_v = [&](int id) { return vbase + (size_t)id * blk_stride; };
         auto valid = [&](int k) { return min(kBlock, tok_end - (first + k * NW) * kBlock); };
         typename Path::Tile ta, tb;
+        int id = phys(0, 0);
+        Path::load(ta, tile_k(id), tile_v(id));
         int k = 0;
-        if constexpr (PA_PREFETCH_TILES == 3) {
-            // three tiles in registers: blocks k+1 and k+2 in flight while k is processed
-            typename Path::Tile tc;
-            int id = phys(0);
-            Path::load(ta, tile_k(id), tile_v(id));
-            id = phys(1);
-            Path::load(tb, tile_k(id), tile_v(id));
-            while (true) {
-                id = phys(k + 2);
-                Path::load(tc, tile_k(id), tile_v(id));
-                Path::process(st, ta, qr, valid(k), sl2);
-                tw.advance(k);
-                if (++k >= n) break;
-                id = phys(k + 2);
-                Path::load(ta, tile_k(id), tile_v(id));
-                Path::process(st, tb, qr, valid(k), sl2);
-                tw.advance(k);
-                if (++k >= n) break;
-                id = phys(k + 2);
-                Path::load(tb, tile_k(id), tile_v(id));
-                Path::process(st, tc, qr, valid(k), sl2);
-                tw.advance(k);
-                if (++k >= n) break;
-            }
-        } else {
-            // two tiles in registers: block k+1 in flight while k is processed
-            int id = phys(0);
-            Path::load(ta, tile_k(id), tile_v(id));
-            while (true) {
-                id = phys(k + 1);
+        for (int kw = 0;; kw += 64) {
+            const int pend = table_window<NW>(row, first, n, kw + 128);
+            const int kend = min(n, kw + 64) & ~1;   // pairs; an odd last block is the tail
+            for (; k < kend; k += 2) {
+                id = phys(kw, k + 1);
                 Path::load(tb, tile_k(id), tile_v(id));
                 Path::process(st, ta, qr, valid(k), sl2);
-                tw.advance(k);
-                if (++k >= n) break;
-                id = phys(k + 1);
+                id = phys(kw, k + 2);
                 Path::load(ta, tile_k(id), tile_v(id));
-                Path::process(st, tb, qr, valid(k), sl2);
-                tw.advance(k);
-                if (++k >= n) break;
+                Path::process(st, tb, qr, valid(k + 1), sl2);
             }
+            if (kw + 64 >= n) break;
+            cur = nxt;
+            nxt = pend;
         }
+        if (k < n) Path::process(st, ta, qr, valid(k), sl2);   // odd block count
     }
 
     const float ltot = Path::wave_l(st);
@@ -702,13 +681,17 @@ static DecodeParams make_params(const void* q, const void* k_cache, const void* 
     return p;
 }
 
-// Waves per workgroup: enough wavefronts in flight to cover the HBM latency
-// (the unit count alone is too small to fill 256 CUs on short batches), but
-// no more waves than a unit has blocks.
-static int pick_waves(long long units, long long blocks_per_unit) {
-    const long long target = 256LL * 12;  // ~12 resident waves per CU
+// Waves per workgroup.  Each wave keeps two K/V tiles in flight, so
+// covering the loaded HBM latency (~1.2 us at ~6.5 TB/s, i.e. ~8 MB in
+// flight) takes about 8 MiB / (2 tiles) waves; twice that many are asked for
+// because unit sizes vary with the sequence lengths, and the waves of the
+// longest unit set the critical path.  No more waves than a quarter of a
+// unit's blocks.
+static int pick_waves(long long units, long long blocks_per_unit, int head_size) {
+    const long long tile_bytes = 2LL * kBlock * head_size * 2;   // K + V, fp16
+    const long long target = (8LL << 20) / tile_bytes;
     int nw = 1;
-    while (nw < 8 && units * nw < target && (long long)(nw * 2) * 2 <= blocks_per_unit) nw *= 2;
+    while (nw < 8 && units * nw < target && (long long)(nw * 2) * 4 <= blocks_per_unit) nw *= 2;
     return nw;
 }
 
@@ -732,7 +715,7 @@ extern "C" int pa_decode_v1(float* out, const void* q, const void* k_cache, cons
     p.out = out;
     const long long units = (long long)num_seqs * num_kv_heads * p.head_chunks;
     if (units > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
-    const int nw = PA_V1_WAVES ? PA_V1_WAVES : pick_waves(units, max_blocks_per_seq);
+    const int nw = PA_V1_WAVES ? PA_V1_WAVES : pick_waves(units, max_blocks_per_seq, head_size);
     return launch_decode<false>(p, head_size, nw, (int)units, as_stream(stream));
 }
 
@@ -765,6 +748,7 @@ extern "C" int pa_decode_v2(float* tmp_out, float* exp_sums, float* max_logits, 
     p.partition_size = partition_size;
     const long long units = (long long)num_seqs * num_kv_heads * p.head_chunks * max_num_partitions;
     if (units > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
-    const int nw = PA_V2_WAVES ? PA_V2_WAVES : pick_waves(units / 2, partition_size / 16);
+    // a sequence has on average about half of max_num_partitions partitions
+    const int nw = PA_V2_WAVES ? PA_V2_WAVES : pick_waves(units / 2, partition_size / 16, head_size);
     return launch_decode<true>(p, head_size, nw, (int)units, as_stream(stream));
 }

@@ -7,12 +7,14 @@
 //
 // The kernel is latency-bound (tens of MB spread over a few hundred rows of
 // partials), so it is built to cost about one memory round trip: one
-// workgroup of 16 wavefronts per (sequence, query head); as soon as the
-// length is known every thread requests its m_p / l_p and every wave requests
-// its (up to 16) o_p rows -- the rows do not depend on the weights -- then
-// the max and the weight sum are reduced through LDS, each wave folds its
-// rows with their weights, and the 16 wave sums are added in LDS.  Sequences
-// with more than 256 partitions loop over further chunks of rows.
+// workgroup of NWR wavefronts per (sequence, query head), NWR sized to the
+// partition count (one wave when a sequence has at most 16 partitions, up to
+// 16 waves for 256 and more); as soon as the length is known every thread
+// requests its m_p / l_p and every wave requests its (up to 16) o_p rows --
+// the rows do not depend on the weights -- then the max and the weight sum
+// are reduced through LDS, each wave folds its rows with their weights, and
+// the wave sums are added in LDS.  Longer sequences loop over further
+// chunks of rows.
 #include <math.h>
 
 #include "pa_device.h"
@@ -20,17 +22,17 @@
 
 namespace pa {
 
-constexpr int kReduceWaves = 16;
-constexpr int kReduceRows = 16;                         // o_p rows per wave per chunk
-constexpr int kReduceThreads = 64 * kReduceWaves;
-constexpr int kReduceChunk = kReduceWaves * kReduceRows;  // partitions per chunk
+constexpr int kReduceRows = 16;   // o_p rows per wave per chunk
 
-template <int D>
-__global__ __launch_bounds__(kReduceThreads) void pa_reduce_kernel(
+template <int D, int NWR>
+__global__ __launch_bounds__(64 * NWR) void pa_reduce_kernel(
     float* __restrict__ out, const float* __restrict__ tmp_out, const float* __restrict__ exp_sums,
     const float* __restrict__ max_logits, const int32_t* __restrict__ seq_lens, int num_heads,
     int max_num_partitions, int partition_size) {
     constexpr int VEC = D / 64;
+    constexpr int kReduceWaves = NWR;
+    constexpr int kReduceThreads = 64 * NWR;
+    constexpr int kReduceChunk = NWR * kReduceRows;   // partitions per chunk
     typedef float vec_t __attribute__((ext_vector_type(VEC)));
     __shared__ float s_red[kReduceWaves];
     __shared__ vec_t s_acc[kReduceWaves][64];
@@ -140,13 +142,27 @@ extern "C" int pa_reduce(float* out, const float* tmp_out, const float* exp_sums
     const long long grid = (long long)num_seqs * num_heads;
     if (grid > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
     hipStream_t st = as_stream(stream);
-    if (head_size == 128)
-        hipLaunchKernelGGL(pa_reduce_kernel<128>, dim3((unsigned)grid), dim3(kReduceThreads), 0,
-                           st, out, tmp_out, exp_sums, max_logits, seq_lens, num_heads,
-                           max_num_partitions, partition_size);
-    else
-        hipLaunchKernelGGL(pa_reduce_kernel<64>, dim3((unsigned)grid), dim3(kReduceThreads), 0,
-                           st, out, tmp_out, exp_sums, max_logits, seq_lens, num_heads,
-                           max_num_partitions, partition_size);
+    // waves per workgroup: one per 16 partitions, between 1 and 16
+    int nwr = 1;
+    while (nwr < 16 && nwr * kReduceRows < max_num_partitions) nwr *= 2;
+#define PA_REDUCE_LAUNCH(DD, NN)                                                                 \
+    hipLaunchKernelGGL((pa_reduce_kernel<DD, NN>), dim3((unsigned)grid), dim3(64 * NN), 0, st, out, \
+                       tmp_out, exp_sums, max_logits, seq_lens, num_heads, max_num_partitions,    \
+                       partition_size)
+#define PA_REDUCE_BY_WAVES(DD)                  \
+    switch (nwr) {                              \
+        case 1: PA_REDUCE_LAUNCH(DD, 1); break;   \
+        case 2: PA_REDUCE_LAUNCH(DD, 2); break;   \
+        case 4: PA_REDUCE_LAUNCH(DD, 4); break;   \
+        case 8: PA_REDUCE_LAUNCH(DD, 8); break;   \
+        default: PA_REDUCE_LAUNCH(DD, 16); break; \
+    }
+    if (head_size == 128) {
+        PA_REDUCE_BY_WAVES(128)
+    } else {
+        PA_REDUCE_BY_WAVES(64)
+    }
+#undef PA_REDUCE_BY_WAVES
+#undef PA_REDUCE_LAUNCH
     return launch_status();
 }
