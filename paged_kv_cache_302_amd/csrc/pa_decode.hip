@@ -51,12 +51,14 @@
 // gets exactly 1 and a one-token sequence returns its V bit-exactly.
 #include <math.h>
 
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_host.h"
 
 // Compile-time tuning knobs (defaults are the measured best on MI355X).
-#ifndef PA_NT_LOADS
-#define PA_NT_LOADS 3         // nontemporal tile loads: bit 0 = K, bit 1 = V
+#ifndef PA_LOAD_POLICY
+#define PA_LOAD_POLICY 1      // tile loads: 0 = cached, 1 = per unit (see load policy), 2 = nontemporal
 #endif
 #ifndef PA_V2_WAVES
 #define PA_V2_WAVES 0         // waves per v2 workgroup (0 = heuristic)
@@ -70,31 +72,16 @@
 
 namespace pa {
 
+// Tile loads.  K/V that only this unit reads is streamed: nontemporal loads
+// do not allocate in the caches, so they neither evict other data nor force
+// write-backs of dirty lines (+8% on long contexts against cached loads).
+// Blocks that other sequences also reference are read with cached loads,
+// so the other readers hit in L2 (-35% time on a shared-prefix batch).
 template <bool NT, class T>
-__device__ __forceinline__ T ld_stream(const T* p) {
+__device__ __forceinline__ T ld_tile(const f16* tile, int off) {
+    const T* p = reinterpret_cast<const T*>(reinterpret_cast<const char*>(tile) + off);
     if constexpr (NT) return __builtin_nontemporal_load(p);
     else return *p;
-}
-constexpr bool kNtK = (PA_NT_LOADS & 1) != 0;   // K tiles
-constexpr bool kNtV = (PA_NT_LOADS & 2) != 0;   // V tiles
-
-#ifndef PA_CPOL
-#define PA_CPOL -1   // >= 0: tile loads as buffer loads with this cache-policy field
-#endif
-// one lane's piece of a K or V tile: `tile` is the wave-uniform tile base,
-// `off` the lane's byte offset in it
-template <bool NT, class T>
-__device__ __forceinline__ T ld_tile(const f16* tile, int off, int tile_bytes) {
-#if PA_CPOL >= 0
-    __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)tile, 0, tile_bytes, 0x00020000);
-    if constexpr (sizeof(T) == 16)
-        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, PA_CPOL));
-    else
-        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, PA_CPOL));
-#else
-    (void)tile_bytes;
-    return ld_stream<NT>(reinterpret_cast<const T*>(reinterpret_cast<const char*>(tile) + off));
-#endif
 }
 
 // Results are written once and not re-read by this kernel.  Plain stores
@@ -187,13 +174,13 @@ struct MfmaPath {
         st.l = 0.f;
     }
 
+    template <bool NTL>
     __device__ __forceinline__ static void load(Tile& t, const f16* kt, const f16* vt) {
         const int l = lane_id(), i = l & 15, g = l >> 4;
-        constexpr int TB = D * kBlock * 2;
 #pragma unroll
-        for (int c = 0; c < KC; ++c) t.k[c] = ld_tile<kNtK, f16x8>(kt, 16 * (l + 64 * c), TB);
+        for (int c = 0; c < KC; ++c) t.k[c] = ld_tile<NTL, f16x8>(kt, 16 * (l + 64 * c));
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) t.v[nt] = ld_tile<kNtV, f16x4>(vt, 8 * (4 * i + g + 64 * nt), TB);
+        for (int nt = 0; nt < NT; ++nt) t.v[nt] = ld_tile<NTL, f16x4>(vt, 8 * (4 * i + g + 64 * nt));
     }
 
     __device__ __forceinline__ static void process(State& st, Tile& t, const QRegs& qr,
@@ -283,13 +270,13 @@ struct ValuPath {
         st.l = 0.f;
     }
 
+    template <bool NTL>
     __device__ __forceinline__ static void load(Tile& t, const f16* kt, const f16* vt) {
         const int l = lane_id();
-        constexpr int TB = D * kBlock * 2;
 #pragma unroll
-        for (int c = 0; c < KC; ++c) t.k[c] = ld_tile<kNtK, f16x8>(kt, 16 * (l + 64 * c), TB);
+        for (int c = 0; c < KC; ++c) t.k[c] = ld_tile<NTL, f16x8>(kt, 16 * (l + 64 * c));
 #pragma unroll
-        for (int c = 0; c < KC; ++c) t.v[c] = ld_tile<kNtV, f16x8>(vt, 16 * (l + 64 * c), TB);
+        for (int c = 0; c < KC; ++c) t.v[c] = ld_tile<NTL, f16x8>(vt, 16 * (l + 64 * c));
     }
 
     __device__ __forceinline__ static void process(State& st, Tile& t, const QRegs& qr,
@@ -351,6 +338,25 @@ struct ValuPath {
         }
     }
 };
+
+// --------------------------------------------------------------------------
+// Load policy: a unit is taken to read shared blocks when the physical block
+// at its first logical position also sits at that position in the table of
+// the sequence before or after it (forked sequences, parallel samples and
+// beams of one request share their prefix blocks and are batched next to
+// each other).  Only the first block is compared: a shared prefix is a
+// leading run of blocks.
+// --------------------------------------------------------------------------
+__device__ __forceinline__ bool shared_unit(const DecodeParams& p, int s, int blk) {
+    const int32_t* bt = p.block_tables;
+    const size_t w = (size_t)p.max_blocks_per_seq;
+    const int b0 = bt[(size_t)s * w + blk];
+    bool shared = false;
+    if (s > 0 && blk * kBlock < p.seq_lens[s - 1]) shared = bt[(size_t)(s - 1) * w + blk] == b0;
+    if (s + 1 < p.num_seqs && blk * kBlock < p.seq_lens[s + 1])
+        shared = shared || bt[(size_t)(s + 1) * w + blk] == b0;
+    return __builtin_amdgcn_readfirstlane((int)shared) != 0;
+}
 
 // --------------------------------------------------------------------------
 // v2 unit lookup: the r-th existing partition, counting sequences in order
@@ -510,26 +516,35 @@ void pa_decode_kernel(DecodeParams p) {
         auto tile_k = [&](int id) { return kbase + (size_t)id * blk_stride; };
         auto tile_v = [&](int id) { return vbase + (size_t)id * blk_stride; };
         auto valid = [&](int k) { return min(kBlock, tok_end - (first + k * NW) * kBlock); };
-        typename Path::Tile ta, tb;
-        int id = phys(0, 0);
-        Path::load(ta, tile_k(id), tile_v(id));
-        int k = 0;
-        for (int kw = 0;; kw += 64) {
-            const int pend = table_window<NW>(row, first, n, kw + 128);
-            const int kend = min(n, kw + 64) & ~1;   // pairs; an odd last block is the tail
-            for (; k < kend; k += 2) {
-                id = phys(kw, k + 1);
-                Path::load(tb, tile_k(id), tile_v(id));
-                Path::process(st, ta, qr, valid(k), sl2);
-                id = phys(kw, k + 2);
-                Path::load(ta, tile_k(id), tile_v(id));
-                Path::process(st, tb, qr, valid(k + 1), sl2);
+        auto walk = [&](auto nt_tag) {
+            constexpr bool NTL = decltype(nt_tag)::value;
+            typename Path::Tile ta, tb;
+            int id = phys(0, 0);
+            Path::template load<NTL>(ta, tile_k(id), tile_v(id));
+            int k = 0;
+            for (int kw = 0;; kw += 64) {
+                const int pend = table_window<NW>(row, first, n, kw + 128);
+                const int kend = min(n, kw + 64) & ~1;   // pairs; an odd last block is the tail
+                for (; k < kend; k += 2) {
+                    id = phys(kw, k + 1);
+                    Path::template load<NTL>(tb, tile_k(id), tile_v(id));
+                    Path::process(st, ta, qr, valid(k), sl2);
+                    id = phys(kw, k + 2);
+                    Path::template load<NTL>(ta, tile_k(id), tile_v(id));
+                    Path::process(st, tb, qr, valid(k + 1), sl2);
+                }
+                if (kw + 64 >= n) break;
+                cur = nxt;
+                nxt = pend;
             }
-            if (kw + 64 >= n) break;
-            cur = nxt;
-            nxt = pend;
-        }
-        if (k < n) Path::process(st, ta, qr, valid(k), sl2);   // odd block count
+            if (k < n) Path::process(st, ta, qr, valid(k), sl2);   // odd block count
+        };
+#if PA_LOAD_POLICY == 1
+        if (shared_unit(p, s, blk_begin)) walk(std::false_type{});   // cached loads
+        else walk(std::true_type{});
+#else
+        walk(std::integral_constant<bool, PA_LOAD_POLICY == 2>{});
+#endif
     }
 
     const float ltot = Path::wave_l(st);
