@@ -26,6 +26,12 @@ CASES = [
     ("g24_d128", 2, 24, 1, 128, 1, 300, 64),     # two head chunks (16 + 8)
     ("g32_d64", 2, 32, 1, 64, 1, 200, 32),
 ]
+# partition counts that take the reduce's wider paths: ~40 partitions
+# (4 waves of 16 rows) and up to 325 (16 waves, a second chunk of rows)
+REDUCE_CASES = [
+    ("parts40_d128", 3, 4, 4, 128, 900, 1300, 32),
+    ("parts325_d64", 2, 8, 2, 64, 3000, 5200, 16),
+]
 
 
 def make_case(case, seed):
@@ -78,7 +84,7 @@ def test_v1_matches_oracle(case):
     assert_parity(run_v1(inp), ref_out(inp), case[0])
 
 
-@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+@pytest.mark.parametrize("case", CASES + REDUCE_CASES, ids=[c[0] for c in CASES + REDUCE_CASES])
 def test_v2_partials_and_merge_match_oracle(case):
     inp = make_case(case, 3)
     ps = case[7]
@@ -94,7 +100,7 @@ def test_v2_partials_and_merge_match_oracle(case):
     assert_parity(out, ref_out(inp), case[0] + " v2+reduce")
 
 
-@pytest.mark.parametrize("case", CASES[:5], ids=[c[0] for c in CASES[:5]])
+@pytest.mark.parametrize("case", CASES[:5] + REDUCE_CASES, ids=[c[0] for c in CASES[:5] + REDUCE_CASES])
 def test_reduce_alone_on_oracle_partials(case):
     """pa_reduce fed with the oracle's own partials (rounded to fp32)."""
     inp = make_case(case, 4)
@@ -112,6 +118,50 @@ def test_reduce_alone_on_oracle_partials(case):
     pa.pa_reduce(out, tmp, es, ml, to_dev(inp.seq_lens), ps)
     merged = oracle.lse_merge(t_ref, e_ref, m_ref, inp.seq_lens, ps)
     np.testing.assert_allclose(out.cpu().numpy(), merged, rtol=1e-5, atol=1e-6)
+
+
+# One sequence and one KV head give one unit, so the launch uses 8 waves and
+# wave w walks blocks w, w + 8, ...; the wave's block ids are read 64 at a
+# time.  Lengths put 64, 65, 128 and 129+ blocks on a wave, with full and
+# partly filled last blocks.
+WINDOW_LENS = [512 * 16, 512 * 16 + 1, 1024 * 16 - 3, 1024 * 16 + 7, 20000]
+
+
+@pytest.mark.parametrize("H,D", [(4, 64), (1, 128)], ids=["mfma", "valu"])
+@pytest.mark.parametrize("L", WINDOW_LENS)
+def test_long_unit_crosses_table_windows(H, D, L):
+    w = wl.small_workload("windows", num_seqs=1, num_heads=H, num_kv_heads=1, head_size=D,
+                          seq_len_lo=L, seq_len_hi=L, partition_size=16384)
+    inp = wl.make_inputs(w, 21)
+    oracle.poison_unused(inp.k_cache, inp.v_cache, inp.block_tables, inp.seq_lens, 16)
+    ref = ref_out(inp)
+    assert_parity(run_v1(inp), ref, f"v1 L={L}")
+    # v2 with 16K-token partitions: 1024 blocks per unit, 128 per wave
+    assert_parity(run_v2(inp, 16384)[0], ref, f"v2 L={L}")
+
+
+def test_load_policy_does_not_change_results():
+    """Units whose first block also sits in a neighbouring sequence's table
+    read with cached loads, the others with nontemporal loads; the
+    arithmetic is the same.  Three sequences share a prefix with different
+    tails, and the middle one is also computed alone (no neighbours, so the
+    other policy): bit-identical."""
+    w = wl.small_workload("policy", num_seqs=3, num_heads=8, num_kv_heads=2, head_size=128,
+                          seq_len_lo=700, seq_len_hi=900, partition_size=256)
+    inp = wl.make_inputs(w, 22)
+    pre = 20                                   # shared leading blocks
+    bt = inp.block_tables.copy()
+    bt[0, :pre] = bt[1, :pre]
+    bt[2, :pre] = bt[1, :pre]
+    inp.block_tables[:] = bt
+    oracle.poison_unused(inp.k_cache, inp.v_cache, inp.block_tables, inp.seq_lens, 16)
+    both = run_v1(inp), run_v2(inp, 256)[0]
+    alone = wl.DecodeInputs(w, inp.seed, inp.seq_lens[1:2].copy(), bt[1:2].copy(),
+                            inp.num_blocks, inp.q[1:2].copy(), inp.k_cache, inp.v_cache)
+    one = run_v1(alone), run_v2(alone, 256)[0]
+    assert np.array_equal(both[0][1], one[0][0])
+    assert np.array_equal(both[1][1], one[1][0])
+    assert_parity(both[0], ref_out(inp), "shared-prefix v1")
 
 
 def test_v1_equals_v2_within_tolerance():
