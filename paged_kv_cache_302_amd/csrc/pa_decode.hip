@@ -77,11 +77,24 @@ namespace pa {
 // write-backs of dirty lines (+8% on long contexts against cached loads).
 // Blocks that other sequences also reference are read with cached loads,
 // so the other readers hit in L2 (-35% time on a shared-prefix batch).
+//
+// A tile is read through a buffer resource whose base is the (wave-uniform)
+// tile address and whose size is the tile's bytes, or 0 for a request that
+// only keeps the load count of a loop iteration fixed: an out-of-range
+// buffer load returns zeros without touching memory.
+constexpr int kBufferDword3 = 0x00020000;   // raw 32-bit data format, no swizzle
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const f16* tile, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<f16*>(tile), 0, bytes, kBufferDword3);
+}
+
 template <bool NT, class T>
-__device__ __forceinline__ T ld_tile(const f16* tile, int off) {
-    const T* p = reinterpret_cast<const T*>(reinterpret_cast<const char*>(tile) + off);
-    if constexpr (NT) return __builtin_nontemporal_load(p);
-    else return *p;
+__device__ __forceinline__ T ld_tile(__amdgpu_buffer_rsrc_t r, int off) {
+    constexpr int cpol = NT ? 2 : 0;   // 2 = nontemporal
+    if constexpr (sizeof(T) == 16)
+        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, cpol));
+    else
+        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, cpol));
 }
 
 // Results are written once and not re-read by this kernel.  Plain stores
@@ -175,12 +188,13 @@ struct MfmaPath {
     }
 
     template <bool NTL>
-    __device__ __forceinline__ static void load(Tile& t, const f16* kt, const f16* vt) {
+    __device__ __forceinline__ static void load(Tile& t, const f16* kt, const f16* vt, int bytes) {
         const int l = lane_id(), i = l & 15, g = l >> 4;
+        const auto rk = tile_rsrc(kt, bytes), rv = tile_rsrc(vt, bytes);
 #pragma unroll
-        for (int c = 0; c < KC; ++c) t.k[c] = ld_tile<NTL, f16x8>(kt, 16 * (l + 64 * c));
+        for (int c = 0; c < KC; ++c) t.k[c] = ld_tile<NTL, f16x8>(rk, 16 * (l + 64 * c));
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) t.v[nt] = ld_tile<NTL, f16x4>(vt, 8 * (4 * i + g + 64 * nt));
+        for (int nt = 0; nt < NT; ++nt) t.v[nt] = ld_tile<NTL, f16x4>(rv, 8 * (4 * i + g + 64 * nt));
     }
 
     __device__ __forceinline__ static void process(State& st, Tile& t, const QRegs& qr,
@@ -271,12 +285,13 @@ struct ValuPath {
     }
 
     template <bool NTL>
-    __device__ __forceinline__ static void load(Tile& t, const f16* kt, const f16* vt) {
+    __device__ __forceinline__ static void load(Tile& t, const f16* kt, const f16* vt, int bytes) {
         const int l = lane_id();
+        const auto rk = tile_rsrc(kt, bytes), rv = tile_rsrc(vt, bytes);
 #pragma unroll
-        for (int c = 0; c < KC; ++c) t.k[c] = ld_tile<NTL, f16x8>(kt, 16 * (l + 64 * c));
+        for (int c = 0; c < KC; ++c) t.k[c] = ld_tile<NTL, f16x8>(rk, 16 * (l + 64 * c));
 #pragma unroll
-        for (int c = 0; c < KC; ++c) t.v[c] = ld_tile<NTL, f16x8>(vt, 16 * (l + 64 * c));
+        for (int c = 0; c < KC; ++c) t.v[c] = ld_tile<NTL, f16x8>(rv, 16 * (l + 64 * c));
     }
 
     __device__ __forceinline__ static void process(State& st, Tile& t, const QRegs& qr,
@@ -496,14 +511,14 @@ void pa_decode_kernel(DecodeParams p) {
         // double-buffered in registers: block k + 1 is requested before block
         // k is processed.
         //
-        // Past the wave's last block the last id is requested again (a re-read
-        // that hits the cache), so every tile request is unconditional and the
-        // wait counts before each use are exact: a conditional request makes
-        // the compiler wait on the newer loads too.  The index is clamped
-        // rather than the previous id kept, so the compiler cannot prove two
-        // requests equal and replace one by a register copy (which drops the
-        // nontemporal hint from the request it keeps and drains the queue).
-        // An id outside the pool marks the unit bad and reads block 0.
+        // Every loop iteration requests the same number of tiles, so the wait
+        // counts before each use are exact (a request under a branch makes the
+        // compiler wait on the newer loads too): past the wave's last block
+        // the request is an empty one (a zero-size buffer, no memory access).
+        // The table index is clamped rather than the previous id kept, so the
+        // compiler cannot prove two requests equal and replace one by a
+        // register copy (which would drain the load queue).  An id outside
+        // the pool marks the unit bad and reads block 0.
         int cur = table_window<NW>(row, first, n, 0);
         int nxt = table_window<NW>(row, first, n, 64);
         auto phys = [&](int kw, int j) {
@@ -516,21 +531,23 @@ void pa_decode_kernel(DecodeParams p) {
         auto tile_k = [&](int id) { return kbase + (size_t)id * blk_stride; };
         auto tile_v = [&](int id) { return vbase + (size_t)id * blk_stride; };
         auto valid = [&](int k) { return min(kBlock, tok_end - (first + k * NW) * kBlock); };
+        constexpr int TB = D * kBlock * 2;                    // bytes of one K or V tile
+        auto live = [&](int j) { return j < n ? TB : 0; };
         auto walk = [&](auto nt_tag) {
             constexpr bool NTL = decltype(nt_tag)::value;
             typename Path::Tile ta, tb;
             int id = phys(0, 0);
-            Path::template load<NTL>(ta, tile_k(id), tile_v(id));
+            Path::template load<NTL>(ta, tile_k(id), tile_v(id), TB);
             int k = 0;
             for (int kw = 0;; kw += 64) {
                 const int pend = table_window<NW>(row, first, n, kw + 128);
                 const int kend = min(n, kw + 64) & ~1;   // pairs; an odd last block is the tail
                 for (; k < kend; k += 2) {
                     id = phys(kw, k + 1);
-                    Path::template load<NTL>(tb, tile_k(id), tile_v(id));
+                    Path::template load<NTL>(tb, tile_k(id), tile_v(id), TB);
                     Path::process(st, ta, qr, valid(k), sl2);
                     id = phys(kw, k + 2);
-                    Path::template load<NTL>(ta, tile_k(id), tile_v(id));
+                    Path::template load<NTL>(ta, tile_k(id), tile_v(id), live(k + 2));
                     Path::process(st, tb, qr, valid(k + 1), sl2);
                 }
                 if (kw + 64 >= n) break;
