@@ -28,7 +28,7 @@ to the gathered, contiguous K/V.  It does not use the online-softmax
 recurrence; ``online_block_attention`` below writes that recurrence out
 separately, only to cross-check this oracle.
 
-Readings of points the pages leave open (each is also listed in the design doc):
+Readings of points the pages leave open:
 * query head h reads KV head h // (num_heads // num_kv_heads);
 * ``scale`` is an explicit argument (the configs use 1/sqrt(head_size));
 * ``seq_len == 0`` gives an all-zero output row;
