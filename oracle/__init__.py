@@ -24,3 +24,4 @@ from .paged_attention import (  # noqa: F401
     value_vector,
     x_of,
 )
+from .block_manager import BlockManager, BlockManagerError, copy_blocks  # noqa: F401
