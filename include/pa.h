@@ -55,7 +55,8 @@ typedef enum pa_status {
     PA_ERR_INVALID_ARG = -1,  /* null pointer, non-positive or inconsistent size */
     PA_ERR_UNSUPPORTED = -2,  /* head_size not 64/128, block_size not 16        */
     PA_ERR_MISALIGNED = -3,   /* a pointer or stride breaks 16-byte alignment    */
-    PA_ERR_LAUNCH = -4        /* the HIP runtime refused a launch               */
+    PA_ERR_LAUNCH = -4,       /* the HIP runtime refused a launch               */
+    PA_ERR_NO_SPACE = -5      /* block manager: too few free blocks / output too small */
 } pa_status;
 
 /* Version of this ABI (bumped on any signature change). */

@@ -5,6 +5,9 @@ declared in include/pa.h); this package is its thin Python binding.
 """
 from ._lib import (  # noqa: F401
     LIB_PATH,
+    BlockManager,
+    BlockManagerError,
+    copy_blocks,
     PagedAttentionError,
     exported_symbols,
     load_library,

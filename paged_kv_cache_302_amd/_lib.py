@@ -32,6 +32,19 @@ _SIGNATURES = {
     "pa_reduce": ([_ptr] * 5 + [_c_int] * 5 + [_ptr], _c_int),
     "reshape_and_cache": ([_ptr] * 5 + [_c_int] * 5 + [_c_i64, _c_i64, _ptr], _c_int),
     "pa_gather_kv": ([_ptr] * 7 + [_c_int] * 6 + [_ptr], _c_int),
+    # block manager (host) and its device block copy -- include/pa_blocks.h
+    "pa_bm_create": ([_c_int, _c_int], _ptr),
+    "pa_bm_destroy": ([_ptr], None),
+    "pa_bm_add_sequence": ([_ptr, _c_i64, _c_int, _ptr], _c_int),
+    "pa_bm_fork": ([_ptr, _c_i64, _c_i64], _c_int),
+    "pa_bm_free_sequence": ([_ptr, _c_i64], _c_int),
+    "pa_bm_append_slots": ([_ptr, _ptr, _c_int, _ptr, _ptr, _c_int, _ptr], _c_int),
+    "pa_bm_block_tables": ([_ptr, _ptr, _c_int, _ptr, _c_int, ctypes.c_int32, _ptr], _c_int),
+    "pa_bm_num_free_blocks": ([_ptr], _c_int),
+    "pa_bm_num_sequences": ([_ptr], _c_int),
+    "pa_bm_seq_len": ([_ptr, _c_i64], _c_int),
+    "pa_bm_refcount": ([_ptr, _c_int], _c_int),
+    "copy_blocks": ([_ptr] * 3 + [_c_int] * 5 + [_ptr], _c_int),
 }
 
 _lib = None
@@ -252,3 +265,113 @@ def split_kv_cache(kv_cache: torch.Tensor, num_kv_heads: int, head_size: int):
     k = kv_cache[0].view(nb, num_kv_heads, head_size // x, -1, x)
     v = kv_cache[1].view(nb, num_kv_heads, head_size, -1)
     return k, v
+
+
+# -- block manager and copy-on-write -----------------------------------------
+
+PA_ERR_NO_SPACE = -5
+
+
+class BlockManagerError(PagedAttentionError):
+    pass
+
+
+class BlockManager:
+    """Host block manager of libpa.so (include/pa_blocks.h): allocation on
+    demand, fork with reference counts, copy-on-write, release.  Marshalling
+    only -- every rule is applied by the native code."""
+
+    def __init__(self, num_blocks: int, block_size: int = 16):
+        self._lib = load_library()
+        self._h = self._lib.pa_bm_create(int(num_blocks), int(block_size))
+        if not self._h:
+            raise BlockManagerError("pa_bm_create failed (bad sizes or out of host memory)")
+        self.num_blocks = int(num_blocks)
+        self.block_size = int(block_size)
+
+    def __del__(self):
+        h, self._h = getattr(self, "_h", None), None
+        if h:
+            self._lib.pa_bm_destroy(h)
+
+    def _rc(self, rc: int, what: str) -> None:
+        if rc != 0:
+            msg = self._lib.pa_status_str(rc).decode()
+            raise BlockManagerError(f"{what}: status {rc} ({msg})")
+
+    def add_sequence(self, seq_id: int, num_tokens: int):
+        """Allocate a new sequence's blocks; returns the slots of its tokens (int64 array)."""
+        import numpy as np
+        slots = np.empty(max(int(num_tokens), 0), dtype=np.int64)
+        self._rc(self._lib.pa_bm_add_sequence(self._h, int(seq_id), int(num_tokens),
+                                              slots.ctypes.data if slots.size else None),
+                 "add_sequence")
+        return slots
+
+    def fork(self, parent: int, child: int) -> None:
+        self._rc(self._lib.pa_bm_fork(self._h, int(parent), int(child)), "fork")
+
+    def free_sequence(self, seq_id: int) -> None:
+        self._rc(self._lib.pa_bm_free_sequence(self._h, int(seq_id)), "free_sequence")
+
+    def append_slots(self, seq_ids):
+        """One decode step: returns (slots int64 [n], copies int32 [k, 2])."""
+        import numpy as np
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        n = ids.size
+        slots = np.empty(n, dtype=np.int64)
+        copies = np.empty((max(n, 1), 2), dtype=np.int32)
+        nc = ctypes.c_int(0)
+        self._rc(self._lib.pa_bm_append_slots(self._h, ids.ctypes.data if n else None, n,
+                                              slots.ctypes.data if n else None,
+                                              copies.ctypes.data, n, ctypes.byref(nc)),
+                 "append_slots")
+        return slots, copies[:nc.value].copy()
+
+    def block_tables(self, seq_ids, width: int, pad: int = -1):
+        """(tables int32 [n, width], seq_lens int32 [n]) for a batch."""
+        import numpy as np
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        n = ids.size
+        tables = np.empty((n, width), dtype=np.int32)
+        lens = np.empty(n, dtype=np.int32)
+        self._rc(self._lib.pa_bm_block_tables(self._h, ids.ctypes.data if n else None, n,
+                                              tables.ctypes.data if n else None, int(width),
+                                              int(pad), lens.ctypes.data if n else None),
+                 "block_tables")
+        return tables, lens
+
+    def table(self, seq_id: int):
+        n = self.seq_len(seq_id)
+        if n < 0:
+            raise BlockManagerError(f"no sequence {seq_id}")
+        width = max(-(-n // self.block_size), 1)
+        t, _ = self.block_tables([seq_id], width)
+        return [int(x) for x in t[0, :-(-n // self.block_size)]]
+
+    def num_free_blocks(self) -> int:
+        return self._lib.pa_bm_num_free_blocks(self._h)
+
+    def num_sequences(self) -> int:
+        return self._lib.pa_bm_num_sequences(self._h)
+
+    def seq_len(self, seq_id: int) -> int:
+        return self._lib.pa_bm_seq_len(self._h, int(seq_id))
+
+    def refcount_of(self, block: int) -> int:
+        return self._lib.pa_bm_refcount(self._h, int(block))
+
+    @property
+    def refcount(self):
+        return [self.refcount_of(b) for b in range(self.num_blocks)]
+
+
+def copy_blocks(k_cache, v_cache, block_pairs, stream=None):
+    """Copy-on-write on the device: block_pairs int32 [n, 2] (source, destination)."""
+    NB, KVH, D, B = _cache_dims(k_cache, v_cache)
+    _want(block_pairs, "block_pairs", torch.int32, 2, k_cache.device)
+    if block_pairs.shape[1] != 2:
+        raise ValueError("block_pairs must be [num_pairs, 2]")
+    rc = load_library().copy_blocks(_p(k_cache), _p(v_cache), _p(block_pairs),
+                                    block_pairs.shape[0], KVH, D, B, NB, _stream(k_cache, stream))
+    _check(rc, "copy_blocks")

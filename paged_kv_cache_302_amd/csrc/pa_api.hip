@@ -1,7 +1,7 @@
 // ABI version and status strings of libpa.
 #include "pa.h"
 
-extern "C" int pa_abi_version(void) { return 2; }
+extern "C" int pa_abi_version(void) { return 3; }
 
 extern "C" const char* pa_status_str(int status) {
     switch (status) {
@@ -10,6 +10,7 @@ extern "C" const char* pa_status_str(int status) {
         case PA_ERR_UNSUPPORTED: return "unsupported configuration (head_size must be 64/128, block_size 16)";
         case PA_ERR_MISALIGNED: return "misaligned pointer or stride (16-byte alignment required)";
         case PA_ERR_LAUNCH: return "kernel launch failed";
+        case PA_ERR_NO_SPACE: return "not enough free blocks, or an output buffer too small";
         default: return "unknown status";
     }
 }

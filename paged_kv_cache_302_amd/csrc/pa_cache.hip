@@ -11,8 +11,15 @@
 //
 // pa_gather_kv: the inverse, for testing the read-side indirection alone.
 // One thread per (sequence, logical block, token slot, KV head, chunk).
+//
+// copy_blocks: the device half of copy-on-write (page "vLLM 的
+// PagedAttention：KV cache 为什么要分页", §4.2): a whole physical block --
+// every KV head, every slot, K and V -- duplicated into a fresh block.  A
+// block of either pool is one contiguous run of num_kv_heads*head_size*16
+// fp16, so the copy is 16-byte vectors, workgroup (pair, 4 KiB piece).
 #include "pa_device.h"
 #include "pa_host.h"
+#include "pa_blocks.h"
 
 namespace pa {
 
@@ -78,9 +85,42 @@ __global__ __launch_bounds__(256) void gather_kv_kernel(
     *reinterpret_cast<f16x8*>(v_out + row * D + c * kX) = vv;
 }
 
+__global__ __launch_bounds__(256) void copy_blocks_kernel(
+    f16* __restrict__ k_cache, f16* __restrict__ v_cache, const int32_t* __restrict__ pairs,
+    int num_blocks, long long chunks_per_block) {
+    const int src = pairs[2 * blockIdx.x], dst = pairs[2 * blockIdx.x + 1];
+    if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+    const long long c = (long long)blockIdx.y * blockDim.x + threadIdx.x;   // 16-byte chunk
+    if (c >= chunks_per_block) return;
+    const size_t so = (size_t)src * chunks_per_block + c, d = (size_t)dst * chunks_per_block + c;
+    f16x8* kc = reinterpret_cast<f16x8*>(k_cache);
+    f16x8* vc = reinterpret_cast<f16x8*>(v_cache);
+    const f16x8 kv = kc[so], vv = vc[so];
+    kc[d] = kv;
+    vc[d] = vv;
+}
+
 }  // namespace pa
 
 using namespace pa;
+
+extern "C" int copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs, int num_pairs,
+                           int num_kv_heads, int head_size, int block_size, int num_blocks,
+                           void* stream) {
+    int rc = check_head_block(head_size, block_size);
+    if (rc != PA_OK) return rc;
+    if (num_pairs < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PA_ERR_INVALID_ARG;
+    if (!k_cache || !v_cache || !block_pairs) return PA_ERR_INVALID_ARG;
+    if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned4(block_pairs)) return PA_ERR_MISALIGNED;
+    if (num_pairs == 0) return PA_OK;
+    const long long chunks = (long long)num_kv_heads * head_size * kBlock / kX;
+    const long long parts = (chunks + 255) / 256;
+    if (parts > 65535) return PA_ERR_INVALID_ARG;
+    hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)num_pairs, (unsigned)parts), dim3(256), 0,
+                       as_stream(stream), static_cast<f16*>(k_cache), static_cast<f16*>(v_cache),
+                       block_pairs, num_blocks, chunks);
+    return launch_status();
+}
 
 extern "C" int reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
                                  const int64_t* slot_mapping, int num_tokens, int num_kv_heads,

@@ -11,15 +11,16 @@ import paged_kv_cache_302_amd as pa
 from paged_kv_cache_302_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "pa.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("pa.h", "pa_blocks.h")]
 
 CTYPE_OF = {
     "int": ctypes.c_int, "float": ctypes.c_float, "int64_t": ctypes.c_int64,
+    "int32_t": ctypes.c_int32,
 }
 
 
 def header_decls():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     decls = {}
     for m in re.finditer(r"PA_API\s+([\w\s\*]+?)\s*\b(\w+)\s*\(([^)]*)\)\s*;", text):
@@ -39,7 +40,8 @@ def arg_ctype(arg):
 def test_header_lists_the_entry_points():
     names = set(header_decls())
     assert {"pa_decode_v1", "pa_decode_v2", "pa_reduce", "reshape_and_cache", "pa_gather_kv",
-            "pa_v2_max_partitions", "pa_status_str", "pa_abi_version"} <= names
+            "pa_v2_max_partitions", "pa_status_str", "pa_abi_version", "copy_blocks",
+            "pa_bm_create", "pa_bm_append_slots"} <= names
     assert names == set(_lib.exported_symbols())
 
 
@@ -59,9 +61,9 @@ def test_binding_signatures_match_header():
 
 def test_status_strings_and_version():
     lib = pa.load_library()
-    assert lib.pa_abi_version() == 2
+    assert lib.pa_abi_version() == 3
     assert lib.pa_status_str(0) == b"ok"
-    for rc in (-1, -2, -3, -4):
+    for rc in (-1, -2, -3, -4, -5):
         assert len(lib.pa_status_str(rc)) > 5
 
 
@@ -117,3 +119,32 @@ def test_cache_write_rejects_bad_arguments():
     assert lib.reshape_and_cache(A, A, A, A, A, 4, 2, 64, 8, 8, 128, 128, None) == -2
     assert lib.reshape_and_cache(A, A, A, A, A, 0, 2, 128, 16, 8, 256, 256, None) == 0   # no tokens
     assert lib.pa_gather_kv(A, A, A, A, A, A, None, 2, 2, 128, 16, 4, 8, None) == -1
+    assert lib.copy_blocks(A, A, A, 3, 2, 96, 16, 8, None) == -2
+    assert lib.copy_blocks(A, A, None, 3, 2, 128, 16, 8, None) == -1
+    assert lib.copy_blocks(M, A, A, 3, 2, 128, 16, 8, None) == -3
+    assert lib.copy_blocks(A, A, A, 0, 2, 128, 16, 8, None) == 0    # no pairs
+
+
+def test_block_manager_rejects_bad_arguments():
+    lib = pa.load_library()
+    assert not lib.pa_bm_create(0, 16) and not lib.pa_bm_create(8, 0)
+    assert lib.pa_bm_add_sequence(None, 0, 3, None) == -1
+    assert lib.pa_bm_num_free_blocks(None) == -1
+    h = lib.pa_bm_create(4, 16)
+    try:
+        assert lib.pa_bm_add_sequence(h, 0, -1, None) == -1
+        assert lib.pa_bm_add_sequence(h, 0, 65, None) == -5          # 5 blocks, 4 free
+        assert lib.pa_bm_add_sequence(h, 0, 64, None) == 0
+        assert lib.pa_bm_add_sequence(h, 0, 1, None) == -1           # exists
+        nc = ctypes.c_int(0)
+        ids = (ctypes.c_int64 * 1)(0)
+        slots = (ctypes.c_int64 * 1)()
+        assert lib.pa_bm_append_slots(h, ids, 1, slots, None, 0, ctypes.byref(nc)) == -5
+        assert lib.pa_bm_append_slots(h, ids, 1, None, None, 0, ctypes.byref(nc)) == -1
+        assert lib.pa_bm_fork(h, 7, 8) == -1 and lib.pa_bm_free_sequence(h, 7) == -1
+        assert lib.pa_bm_seq_len(h, 0) == 64 and lib.pa_bm_seq_len(h, 7) == -1
+        assert lib.pa_bm_refcount(h, 4) == -1 and lib.pa_bm_refcount(h, 3) == 1
+        tables = (ctypes.c_int32 * 3)()
+        assert lib.pa_bm_block_tables(h, ids, 1, tables, 3, -1, None) == -5   # 4 blocks > width 3
+    finally:
+        lib.pa_bm_destroy(h)

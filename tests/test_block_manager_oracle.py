@@ -25,7 +25,7 @@ from oracle import BlockManager, BlockManagerError
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "cow_scenario.json")
 
 
-def run_golden(make):
+def run_golden(make, error=BlockManagerError):
     d = json.load(open(GOLDEN))
     bm = make(d["num_blocks"], d["block_size"])
     for i, st in enumerate(d["steps"]):
@@ -42,7 +42,7 @@ def run_golden(make):
                 s, c = bm.append_slots(st["seqs"])
                 got["slots"], got["copies"] = list(s), [list(x) for x in c]
             err = False
-        except BlockManagerError:
+        except error:
             err = True
         where = f"step {i} ({op})"
         assert err == st.get("error", False), where
