@@ -163,6 +163,8 @@ PA_API int pa_reduce(float* out, const float* tmp_out, const float* exp_sums,
  *                least num_kv_heads*head_size)
  *   k_cache, v_cache  as in pa_decode_v1, updated in place
  *   slot_mapping [num_tokens] int64
+ * With num_tokens == 0 nothing is enqueued and key, value and slot_mapping
+ * may be NULL.
  */
 PA_API int reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
                       const int64_t* slot_mapping, int num_tokens, int num_kv_heads,

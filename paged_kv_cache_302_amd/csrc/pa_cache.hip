@@ -110,9 +110,10 @@ extern "C" int copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pa
     int rc = check_head_block(head_size, block_size);
     if (rc != PA_OK) return rc;
     if (num_pairs < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PA_ERR_INVALID_ARG;
-    if (!k_cache || !v_cache || !block_pairs) return PA_ERR_INVALID_ARG;
+    if (!k_cache || !v_cache) return PA_ERR_INVALID_ARG;
+    if (num_pairs == 0) return PA_OK;   // block_pairs may be NULL then
+    if (!block_pairs) return PA_ERR_INVALID_ARG;
     if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned4(block_pairs)) return PA_ERR_MISALIGNED;
-    if (num_pairs == 0) return PA_OK;
     const long long chunks = (long long)num_kv_heads * head_size * kBlock / kX;
     const long long parts = (chunks + 255) / 256;
     if (parts > 65535) return PA_ERR_INVALID_ARG;
@@ -131,11 +132,12 @@ extern "C" int reshape_and_cache(const void* key, const void* value, void* k_cac
     if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PA_ERR_INVALID_ARG;
     const int64_t row = (int64_t)num_kv_heads * head_size;
     if (key_stride < row || value_stride < row) return PA_ERR_INVALID_ARG;
-    if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PA_ERR_INVALID_ARG;
+    if (!k_cache || !v_cache) return PA_ERR_INVALID_ARG;
+    if (num_tokens == 0) return PA_OK;   // key, value, slot_mapping may be NULL then
+    if (!key || !value || !slot_mapping) return PA_ERR_INVALID_ARG;
     if (!aligned16(key) || !aligned16(value) || !aligned16(k_cache) || !aligned16(v_cache) ||
         !aligned8(slot_mapping) || key_stride % 8 != 0 || value_stride % 8 != 0)
         return PA_ERR_MISALIGNED;
-    if (num_tokens == 0) return PA_OK;
     const long long items = (long long)num_tokens * num_kv_heads * (head_size / kX);
     const long long grid = (items + 255) / 256;
     if (grid > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
