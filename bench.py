@@ -12,6 +12,11 @@ are resident in HBM before timing starts.
 The metric is effective KV bandwidth: sum_s L_s * 2 * num_kv_heads * head_size
 * 2 bytes per step divided by the step time, also given as a fraction of the
 MI355X HBM peak (8 TB/s).  Rank 0 prints one JSON line.
+
+`--workload fork` times the first decode step after a parallel-sampling fork:
+the native block manager hands out the step's slots, tables and
+copy-on-write pairs before timing, and the step is copy_blocks +
+reshape_and_cache + pa_decode_v2 + pa_reduce.
 """
 from __future__ import annotations
 
@@ -76,31 +81,28 @@ def blas_threads() -> int:
         return 1
 
 
-def cpu_baseline(inp, gpu_out, budget_s: float):
+def cpu_baseline(k_cache, v_cache, block_tables, seq_lens, q, scale, num_kv_heads, block_size,
+                 gpu_out, budget_s: float):
     """The oracle (fp64 NumPy) on a bounded sample of the same workload:
     whole (sequence, KV head) units in order until the time budget is spent.
-    Returns its throughput in the metric's unit, and its agreement with the
-    GPU output on the sampled rows."""
+    The pools must already hold the step's cache writes.  Returns its
+    throughput in the metric's unit, and its agreement with the GPU output
+    on the sampled rows."""
     import oracle
-    import workloads as wl
-    w = inp.workload
-    G = w.num_heads // w.num_kv_heads
-    # the same cache write the GPU step made, so both see the same K/V
-    oracle.reshape_and_cache(inp.key, inp.value, inp.k_cache, inp.v_cache,
-                             wl.new_token_slots(inp), w.block_size, inplace=True)
+    S, H, D = q.shape
+    G = H // num_kv_heads
     done_bytes = 0
     spent = 0.0
     units = 0
     max_err = 0.0
-    for s in range(w.num_seqs):
-        L = int(inp.seq_lens[s])
-        for kvh in range(w.num_kv_heads):
+    for s in range(S):
+        L = int(seq_lens[s])
+        for kvh in range(num_kv_heads):
             t0 = time.perf_counter()
-            K, V = oracle.gather_sequence_fast(inp.k_cache, inp.v_cache, inp.block_tables[s], L,
-                                               kvh, w.block_size)
-            ref = oracle.attention(inp.q[s, kvh * G:(kvh + 1) * G], K, V, inp.scale)
+            K, V = oracle.gather_sequence_fast(k_cache, v_cache, block_tables[s], L, kvh, block_size)
+            ref = oracle.attention(q[s, kvh * G:(kvh + 1) * G], K, V, scale)
             spent += time.perf_counter() - t0
-            done_bytes += L * 2 * w.head_size * 2
+            done_bytes += L * 2 * D * 2
             units += 1
             max_err = max(max_err, float(np.abs(ref - gpu_out[s, kvh * G:(kvh + 1) * G]).max()))
             if spent >= budget_s:
@@ -152,6 +154,172 @@ def read_traffic(kname: str, workload: str):
         return None
 
 
+def timed_steps(args, step, n_events):
+    """Warm-up, then exactly args.steps steps between two synchronisations;
+    returns (ms_per_step, per-step event lists, wall ms per step)."""
+    import torch
+    dev = torch.device("cuda:0")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    scrub_buf = torch.ones(1 << 28, dtype=torch.float32, device=dev) if args.scrub else None
+    scrub_sum = torch.empty((), dtype=torch.float32, device=dev)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_events)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(args.steps):
+        if scrub_buf is not None:
+            torch.sum(scrub_buf, dim=0, out=scrub_sum)
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t_start) * 1e3 / args.steps
+    if scrub_buf is not None:
+        ms = float(np.mean([e[0].elapsed_time(e[-1]) for e in evs]))
+    else:
+        ms = wall
+    return ms, evs, wall
+
+
+def main_fork(args):
+    """First decode step after a parallel-sampling fork (see the module
+    docstring)."""
+    import torch
+
+    import paged_kv_cache_302_amd as pa
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    w = wl.FORK
+    t0 = time.time()
+    fi = wl.make_fork_inputs(w, args.seed)
+    gen_s = time.time() - t0
+    S, H, D, KVH, B = w.num_seqs, w.num_heads, w.head_size, w.num_kv_heads, w.block_size
+    NB = w.pool_blocks
+
+    def t(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    kc = torch.zeros((NB, KVH, D // 8, B, 8), dtype=torch.float16, device=dev)
+    vc = torch.zeros((NB, KVH, D, B), dtype=torch.float16, device=dev)
+    bm = pa.BlockManager(NB, B)
+    seqs, prompt_slots = [], []
+    for g in range(w.groups):
+        root = g * w.samples
+        sl_g = bm.add_sequence(root, w.prompt_len)
+        prompt_slots.append(sl_g)
+        pa.reshape_and_cache(t(fi.prompt_k[g]), t(fi.prompt_v[g]), kc, vc, t(sl_g))
+        for c in range(1, w.samples):
+            bm.fork(root, root + c)
+        seqs += list(range(root, root + w.samples))
+    slots, copies = bm.append_slots(seqs)
+    width = -(-(w.prompt_len + 1) // B)
+    tables, lens = bm.block_tables(seqs, width)
+    q, key, val = t(fi.q), t(fi.key), t(fi.value)
+    pairs_d, slot_d, bt, sl = t(copies), t(slots), t(tables), t(lens)
+    PS = w.partition_size
+    P = pa.pa_v2_max_partitions(int(lens.max()), PS)
+    tmp, es, ml = pa.v2_scratch(S, H, D, P, dev)
+    out = torch.empty((S, H, D), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        # the step is idempotent: the copies read blocks no write of the step
+        # touches before them, and every write lands on the same slot again
+        if ev is not None:
+            ev[0].record(stream)
+        pa.copy_blocks(kc, vc, pairs_d)
+        if ev is not None:
+            ev[1].record(stream)
+        pa.reshape_and_cache(key, val, kc, vc, slot_d)
+        if ev is not None:
+            ev[2].record(stream)
+        pa.pa_decode_v2(tmp, es, ml, q, kc, vc, bt, sl, w.scale, PS)
+        if ev is not None:
+            ev[3].record(stream)
+        pa.pa_reduce(out, tmp, es, ml, sl, PS)
+        if ev is not None:
+            ev[4].record(stream)
+
+    ms_per_step, evs, wall = timed_steps(args, step, 5)
+    med = lambda i: float(np.median([e[i].elapsed_time(e[i + 1]) for e in evs]))
+    copy_s = med(0) / 1e3
+    dec_s = float(np.mean([e[2].elapsed_time(e[3]) for e in evs])) / 1e3
+    block_bytes = KVH * D * B * 2                       # one block of one pool
+    distinct = len(np.unique(tables[tables >= 0]))
+    unique_bytes = distinct * 2 * block_bytes           # whole K and V tiles the decode reads
+    kv_bytes = int(lens.astype(np.int64).sum()) * KVH * D * 4
+    copy_bytes = len(copies) * 2 * block_bytes * 2      # read + write, both pools
+    value = kv_bytes / (ms_per_step / 1e3) / 1e9
+    achieved = unique_bytes / dec_s / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": "fork",
+            "kernel": "copy_blocks + reshape_and_cache + pa_decode_v2 + pa_reduce",
+            "groups": w.groups, "samples": w.samples, "prompt_len": w.prompt_len,
+            "num_seqs": S, "num_heads": H, "num_kv_heads": KVH, "head_size": D,
+            "block_size": B, "partition_size": PS, "num_blocks": NB,
+            "copy_pairs": int(len(copies)), "distinct_blocks": int(distinct),
+            "kv_bytes_per_step": kv_bytes, "unique_kv_bytes_per_step": unique_bytes,
+            "seed": args.seed,
+        },
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "kernels_us": {
+            "copy_blocks": round(med(0) * 1e3, 2),
+            "reshape_and_cache": round(med(1) * 1e3, 2),
+            "pa_decode_v2": round(med(2) * 1e3, 2),
+            "pa_reduce": round(med(3) * 1e3, 2),
+        },
+        "roofline": {
+            "kernel": "pa_decode_v2",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": read_traffic("pa_decode_v2", "fork"),
+            "algorithmic_bytes_per_launch": unique_bytes,
+            "avg_launch_us": round(dec_s * 1e6, 2),
+        },
+        "copy_blocks": {
+            "bytes_per_launch": copy_bytes,
+            "achieved_gbs": round(copy_bytes / copy_s / 1e9, 2),
+            "frac_of_peak": round(copy_bytes / copy_s / 1e9 / HBM_PEAK_GBS, 4),
+        },
+        "timing": ("HIP events per step, 1 GiB read scrub between steps (wall %.4f ms/step incl. scrub)"
+                   % wall) if args.scrub else "wall clock over the timed steps",
+        "input_gen_s": round(gen_s, 2),
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        gpu_out = out.cpu().numpy()
+        # the oracle replays the same writes and copies on host pools
+        hk = np.zeros((NB, KVH, D // 8, B, 8), np.float16)
+        hv = np.zeros((NB, KVH, D, B), np.float16)
+        for g in range(w.groups):
+            oracle.reshape_and_cache(fi.prompt_k[g], fi.prompt_v[g], hk, hv, prompt_slots[g], B,
+                                     inplace=True)
+        oracle.copy_blocks(hk, hv, [tuple(p) for p in copies])
+        oracle.reshape_and_cache(fi.key, fi.value, hk, hv, slots, B, inplace=True)
+        res["cpu_baseline"] = cpu_baseline(hk, hv, tables, lens, fi.q, w.scale, KVH, B, gpu_out,
+                                           args.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -166,6 +334,8 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     dev = torch.device("cuda:0")
+    if args.workload == "fork":
+        return main_fork(args)
     w = wl.WORKLOADS[args.workload]
     t0 = time.time()
     inp = wl.make_inputs(w, args.seed)
@@ -298,8 +468,14 @@ def main():
         "input_gen_s": round(gen_s, 2),
     }
     if not args.no_cpu_baseline:
+        import oracle
         gpu_out = out.cpu().numpy()
-        res["cpu_baseline"] = cpu_baseline(inp, gpu_out, args.cpu_seconds)
+        # the same cache write the GPU step made, so both see the same K/V
+        oracle.reshape_and_cache(inp.key, inp.value, inp.k_cache, inp.v_cache, slots,
+                                 w.block_size, inplace=True)
+        res["cpu_baseline"] = cpu_baseline(inp.k_cache, inp.v_cache, inp.block_tables,
+                                           inp.seq_lens, inp.q, inp.scale, KVH, w.block_size,
+                                           gpu_out, args.cpu_seconds)
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)

@@ -278,3 +278,68 @@ def small_workload(name: str = "small", *, num_seqs=3, num_heads=8, num_kv_heads
     return Workload(name, num_seqs, num_heads, num_kv_heads, head_size, seq_len_lo,
                     seq_len_hi, block_size=block_size, sigma=sigma, num_blocks=num_blocks,
                     partition_size=partition_size, kernels=("v1", "v2"))
+
+
+# -- parallel sampling (fork) ------------------------------------------------
+
+@dataclass(frozen=True)
+class ForkWorkload:
+    """Parallel sampling: `groups` prompts of `prompt_len` tokens, each forked
+    into `samples` sequences that share the prompt's blocks (blog page §4.2).
+    The first decode step after the fork splits every shared, partly filled
+    last prompt block by copy-on-write.  Only the values are drawn here; the
+    slots, tables and copies come from whichever block manager is under test."""
+    name: str = "fork"
+    groups: int = 32
+    samples: int = 8
+    prompt_len: int = 1000           # not a multiple of the block size
+    num_heads: int = 32
+    num_kv_heads: int = 8
+    head_size: int = 128
+    block_size: int = 16
+    partition_size: int = 512
+    sigma: float = 1.0
+
+    @property
+    def num_seqs(self) -> int:
+        return self.groups * self.samples
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_size)
+
+    @property
+    def pool_blocks(self) -> int:
+        """Prompt blocks plus one new block per sequence, with 10% slack."""
+        need = self.groups * -(-self.prompt_len // self.block_size) + self.num_seqs
+        return int(math.ceil(1.1 * need))
+
+
+@dataclass
+class ForkInputs:
+    workload: ForkWorkload
+    seed: int
+    prompt_k: np.ndarray     # [groups, prompt_len, KVH, D] fp16
+    prompt_v: np.ndarray
+    q: np.ndarray            # [num_seqs, H, D] fp16 (sequence g*samples + c)
+    key: np.ndarray          # [num_seqs, KVH, D] fp16: the step's new token
+    value: np.ndarray
+
+
+FORK = ForkWorkload()
+
+
+def make_fork_inputs(w: ForkWorkload, seed: int) -> ForkInputs:
+    """One rng stream, drawn in order: prompt K, prompt V, q, new key, new value."""
+    rng = np.random.default_rng(seed)
+
+    def normal(shape):
+        return (w.sigma * rng.standard_normal(shape)).astype(np.float16)
+
+    KVH, D = w.num_kv_heads, w.head_size
+    pk = normal((w.groups, w.prompt_len, KVH, D))
+    pv = normal((w.groups, w.prompt_len, KVH, D))
+    q = normal((w.num_seqs, w.num_heads, D))
+    key = normal((w.num_seqs, KVH, D))
+    value = normal((w.num_seqs, KVH, D))
+    return ForkInputs(w, seed, pk, pv, q, key, value)
