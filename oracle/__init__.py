@@ -25,3 +25,4 @@ from .paged_attention import (  # noqa: F401
     x_of,
 )
 from .block_manager import BlockManager, BlockManagerError, copy_blocks  # noqa: F401
+from . import fp8  # noqa: F401
