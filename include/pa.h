@@ -25,7 +25,18 @@
  *     row-major with the shapes given below, except key/value rows, whose
  *     token stride is an argument.
  *   - block_size must be 16 and head_size 64 or 128 (PA_ERR_UNSUPPORTED
- *     otherwise).  x = 16 bytes / sizeof(fp16) = 8.
+ *     otherwise).  x = 16 bytes / element size: 8 for fp16 pools, 16 for fp8.
+ *   - kv_cache_dtype selects the pools' element type (§3.2 of the kernel
+ *     page names kv_cache_dtype, k_scale and v_scale but defines no scheme;
+ *     the one taken here): PA_KV_FP16, or PA_KV_FP8_E4M3 -- one byte per
+ *     element in the OCP FP8 E4M3 format (sign, 4 exponent bits with bias 7,
+ *     3 mantissa bits, no infinity, S.1111.111 = NaN, largest finite 448),
+ *     with one fp32 scale per pool: the cache write stores
+ *     code = E4M3(fp32(x) / k_scale) (nearest, ties to even, finite values
+ *     beyond 448 saturated, NaN -> 0x7F) and attention reads K as
+ *     code * k_scale and V as code * v_scale.  For fp16 pools the scales are
+ *     ignored; for fp8 they must be finite and > 0.  Another dtype value is
+ *     PA_ERR_UNSUPPORTED.
  *   - Return value: PA_OK, or a negative pa_status before anything is
  *     enqueued.  PA_ERR_LAUNCH reports a failed launch.  A kernel fault shows
  *     up at the caller's next synchronisation, as HIP does.
@@ -49,6 +60,11 @@
 #ifdef __cplusplus
 extern "C" {
 #endif
+
+typedef enum pa_kv_dtype {
+    PA_KV_FP16 = 0,           /* IEEE binary16 elements                         */
+    PA_KV_FP8_E4M3 = 1        /* OCP FP8 E4M3 codes with per-pool fp32 scales   */
+} pa_kv_dtype;
 
 typedef enum pa_status {
     PA_OK = 0,
@@ -74,12 +90,16 @@ PA_API const char* pa_status_str(int status);
  * the pools (§3.1), and return
  *     out[s,h,:] = sum_t softmax_t(scale * q[s,h,:] . K_t) V_t
  * computed block by block with an online softmax (running max, normaliser
- * and accumulator, §2 flowchart / §3.3), fp32 accumulation.
+ * and accumulator, §2 flowchart / §3.3), fp32 accumulation.  With an fp8
+ * cache, K_t and V_t are the scaled codes (see kv_cache_dtype above); they
+ * are converted to fp16 exactly, and k_scale and v_scale are applied to the
+ * logits and to the final normalisation.
  *
  *   out          [num_seqs, num_heads, head_size] fp32, written
  *   q            [num_seqs, num_heads, head_size] fp16
- *   k_cache      [num_blocks, num_kv_heads, head_size/8, 16, 8] fp16
- *   v_cache      [num_blocks, num_kv_heads, head_size, 16] fp16
+ *   k_cache      [num_blocks, num_kv_heads, head_size/x, 16, x] (x = 8 fp16,
+ *                16 fp8)
+ *   v_cache      [num_blocks, num_kv_heads, head_size, 16]
  *   block_tables [num_seqs, max_blocks_per_seq] int32: physical block ids;
  *                entries past ceil(L/16) are never read
  *   seq_lens     [num_seqs] int32: L <= 0 gives an all-zero row; slots past L
@@ -90,7 +110,8 @@ PA_API int pa_decode_v1(float* out, const void* q, const void* k_cache, const vo
                  const int32_t* block_tables, const int32_t* seq_lens,
                  int num_seqs, int num_heads, int num_kv_heads, int head_size,
                  int block_size, int max_blocks_per_seq, int num_blocks,
-                 float scale, void* stream);
+                 float scale, int kv_cache_dtype, float k_scale, float v_scale,
+                 void* stream);
 
 /* ceil(max_seq_len / partition_size): the partition count v2 scratch is sized
  * for; -1 if an argument is not positive. */
@@ -103,7 +124,8 @@ PA_API int pa_v2_max_partitions(int max_seq_len, int partition_size);
  *
  * Partition p of sequence s covers tokens [p*PS, min((p+1)*PS, L)),
  * p < ceil(L/PS).  For each query head h it writes
- *     max_logits[s,p,h] = m_p = max_t z_t          (z_t = scale * q . K_t)
+ *     max_logits[s,p,h] = m_p = max_t z_t          (z_t = scale * q . K_t,
+ *                                                   K_t scaled for fp8)
  *     exp_sums[s,p,h]   = l_p = sum_t exp(z_t - m_p)
  *     tmp_out[s,p,h,:]  = sum_t exp(z_t - m_p) V_t / l_p
  * in natural-log units.  Entries with p >= ceil(L/PS) are not written.
@@ -127,7 +149,7 @@ PA_API int pa_decode_v2(float* tmp_out, float* exp_sums, float* max_logits,
                  int num_seqs, int num_heads, int num_kv_heads, int head_size,
                  int block_size, int max_blocks_per_seq, int num_blocks,
                  int max_num_partitions, int partition_size, float scale,
-                 void* stream);
+                 int kv_cache_dtype, float k_scale, float v_scale, void* stream);
 
 /*
  * pa_reduce -- v2 second pass: log-sum-exp merge of the partials (the pages
@@ -153,10 +175,12 @@ PA_API int pa_reduce(float* out, const float* tmp_out, const float* exp_sums,
  * direction).
  *
  * For token i with slot = slot_mapping[i], b = slot / 16, o = slot % 16:
- *     k_cache[b, h, d/8, o, d%8] = key[i, h, d]
- *     v_cache[b, h, d, o]        = value[i, h, d]     for every h, d.
- * A bit-exact copy.  slot < 0 skips the token (padding); a slot at or past
- * num_blocks*16 is skipped too.  Two tokens with the same slot race.
+ *     k_cache[b, h, d/x, o, d%x] = key[i, h, d]
+ *     v_cache[b, h, d, o]        = value[i, h, d]     for every h, d,
+ * a bit-exact copy into fp16 pools, or the E4M3 codes of key / k_scale and
+ * value / v_scale into fp8 pools (kv_cache_dtype above).  slot < 0 skips
+ * the token (padding); a slot at or past num_blocks*16 is skipped too.  Two
+ * tokens with the same slot race.
  *
  *   key, value   [num_tokens, num_kv_heads, head_size] fp16, token stride
  *                key_stride / value_stride elements (a multiple of 8, at
@@ -169,22 +193,25 @@ PA_API int pa_reduce(float* out, const float* tmp_out, const float* exp_sums,
 PA_API int reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
                       const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
                       int head_size, int block_size, int num_blocks,
-                      int64_t key_stride, int64_t value_stride, void* stream);
+                      int64_t key_stride, int64_t value_stride,
+                      int kv_cache_dtype, float k_scale, float v_scale, void* stream);
 
 /*
  * pa_gather_kv -- the read-side indirection alone: every sequence's K and V
- * copied bit-exactly, in logical token order, to contiguous arrays.
+ * copied bit-exactly, in logical token order, to contiguous arrays of the
+ * pools' element type (fp16 values or fp8 codes).
  *
- *   k_out, v_out [sum_s L_s, num_kv_heads, head_size] fp16, written: token t
- *                of sequence s goes to row cu_seq_lens[s] + t
+ *   k_out, v_out [sum_s L_s, num_kv_heads, head_size] elements, written:
+ *                token t of sequence s goes to row cu_seq_lens[s] + t
  *   cu_seq_lens  [num_seqs] int64: starting row of each sequence
- *   other arguments as in pa_decode_v1.  A bad block id writes NaN rows.
+ *   other arguments as in pa_decode_v1 (kv_cache_dtype: element type only).
+ *   A bad block id writes NaN rows.
  */
 PA_API int pa_gather_kv(void* k_out, void* v_out, const void* k_cache, const void* v_cache,
                  const int32_t* block_tables, const int32_t* seq_lens,
                  const int64_t* cu_seq_lens, int num_seqs, int num_kv_heads,
                  int head_size, int block_size, int max_blocks_per_seq, int num_blocks,
-                 void* stream);
+                 int kv_cache_dtype, void* stream);
 
 #ifdef __cplusplus
 }

@@ -112,14 +112,15 @@ PA_API int pa_bm_refcount(const pa_block_manager* bm, int block);
  * pa_bm_append_slots never produces); a pair naming an id outside
  * [0, num_blocks) is skipped on the device.
  *
- *   k_cache, v_cache  the pools of pa_decode_v1 (device, updated in place)
+ *   k_cache, v_cache  the pools of pa_decode_v1 (device, updated in place),
+ *                     of element type kv_cache_dtype (pa.h)
  *   block_pairs       [num_pairs][2] int32 (device; may be NULL when
  *                     num_pairs == 0, which enqueues nothing)
  * Enqueued on `stream`; PA_ERR_* as in pa.h for bad host arguments.
  */
 PA_API int copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs, int num_pairs,
                        int num_kv_heads, int head_size, int block_size, int num_blocks,
-                       void* stream);
+                       int kv_cache_dtype, void* stream);
 
 #ifdef __cplusplus
 }

@@ -5,11 +5,14 @@ declared in include/pa.h); this package is its thin Python binding.
 """
 from ._lib import (  # noqa: F401
     LIB_PATH,
+    PA_KV_FP16,
+    PA_KV_FP8_E4M3,
     BlockManager,
     BlockManagerError,
     copy_blocks,
     PagedAttentionError,
     exported_symbols,
+    kv_dtype_of,
     load_library,
     pa_abi_version,
     pa_decode_v1,

@@ -26,12 +26,13 @@ _ptr = ctypes.c_void_p
 _SIGNATURES = {
     "pa_abi_version": ([], _c_int),
     "pa_status_str": ([_c_int], ctypes.c_char_p),
-    "pa_decode_v1": ([_ptr] * 6 + [_c_int] * 7 + [_c_float, _ptr], _c_int),
+    "pa_decode_v1": ([_ptr] * 6 + [_c_int] * 7 + [_c_float, _c_int, _c_float, _c_float, _ptr], _c_int),
     "pa_v2_max_partitions": ([_c_int, _c_int], _c_int),
-    "pa_decode_v2": ([_ptr] * 8 + [_c_int] * 9 + [_c_float, _ptr], _c_int),
+    "pa_decode_v2": ([_ptr] * 8 + [_c_int] * 9 + [_c_float, _c_int, _c_float, _c_float, _ptr], _c_int),
     "pa_reduce": ([_ptr] * 5 + [_c_int] * 5 + [_ptr], _c_int),
-    "reshape_and_cache": ([_ptr] * 5 + [_c_int] * 5 + [_c_i64, _c_i64, _ptr], _c_int),
-    "pa_gather_kv": ([_ptr] * 7 + [_c_int] * 6 + [_ptr], _c_int),
+    "reshape_and_cache": ([_ptr] * 5 + [_c_int] * 5 + [_c_i64, _c_i64, _c_int, _c_float, _c_float,
+                                                         _ptr], _c_int),
+    "pa_gather_kv": ([_ptr] * 7 + [_c_int] * 7 + [_ptr], _c_int),
     # block manager (host) and its device block copy -- include/pa_blocks.h
     "pa_bm_create": ([_c_int, _c_int], _ptr),
     "pa_bm_destroy": ([_ptr], None),
@@ -44,7 +45,7 @@ _SIGNATURES = {
     "pa_bm_num_sequences": ([_ptr], _c_int),
     "pa_bm_seq_len": ([_ptr, _c_i64], _c_int),
     "pa_bm_refcount": ([_ptr, _c_int], _c_int),
-    "copy_blocks": ([_ptr] * 3 + [_c_int] * 5 + [_ptr], _c_int),
+    "copy_blocks": ([_ptr] * 3 + [_c_int] * 6 + [_ptr], _c_int),
 }
 
 _lib = None
@@ -106,13 +107,30 @@ def _p(t: torch.Tensor) -> ctypes.c_void_p:
     return ctypes.c_void_p(t.data_ptr())
 
 
+# kv_cache_dtype codes of include/pa.h
+PA_KV_FP16 = 0
+PA_KV_FP8_E4M3 = 1
+_FP8_STORAGE = (torch.uint8, torch.float8_e4m3fn)
+
+
+def kv_dtype_of(k_cache: torch.Tensor) -> int:
+    """PA_KV_FP16 for fp16 pools, PA_KV_FP8_E4M3 for uint8 / float8_e4m3fn pools."""
+    if k_cache.dtype == torch.float16:
+        return PA_KV_FP16
+    if k_cache.dtype in _FP8_STORAGE:
+        return PA_KV_FP8_E4M3
+    raise TypeError(f"unsupported cache dtype {k_cache.dtype} (fp16, or fp8 E4M3 as uint8/float8_e4m3fn)")
+
+
 def _cache_dims(k_cache: torch.Tensor, v_cache: torch.Tensor):
-    _want(k_cache, "k_cache", torch.float16, 5)
-    _want(v_cache, "v_cache", torch.float16, 4, k_cache.device)
+    kvd = kv_dtype_of(k_cache)
+    _want(k_cache, "k_cache", k_cache.dtype, 5)
+    _want(v_cache, "v_cache", k_cache.dtype, 4, k_cache.device)
     NB, KVH, Dx, B, x = k_cache.shape
     D = Dx * x
-    if x != 8:
-        raise ValueError("k_cache last dim must be x = 8 for fp16")
+    want_x = 8 if kvd == PA_KV_FP16 else 16
+    if x != want_x:
+        raise ValueError(f"k_cache last dim must be x = {want_x} for this dtype")
     if tuple(v_cache.shape) != (NB, KVH, D, B):
         raise ValueError(f"v_cache shape {tuple(v_cache.shape)} does not match k_cache {tuple(k_cache.shape)}")
     return NB, KVH, D, B
@@ -140,21 +158,25 @@ def pa_v2_max_partitions(max_seq_len: int, partition_size: int) -> int:
     return load_library().pa_v2_max_partitions(int(max_seq_len), int(partition_size))
 
 
-def pa_decode_v1(out, q, k_cache, v_cache, block_tables, seq_lens, scale: float, stream=None):
-    """out[S,H,D] fp32 <- paged decode attention (no partitioning)."""
+def pa_decode_v1(out, q, k_cache, v_cache, block_tables, seq_lens, scale: float,
+                 k_scale: float = 1.0, v_scale: float = 1.0, stream=None):
+    """out[S,H,D] fp32 <- paged decode attention (no partitioning).  The
+    scales apply to fp8 pools only."""
     S, H, KVH, D, B, NB, MB = _decode_common(q, k_cache, v_cache, block_tables, seq_lens)
     _want(out, "out", torch.float32, 3, q.device)
     if tuple(out.shape) != (S, H, D):
         raise ValueError("out must be [num_seqs, num_heads, head_size]")
     lib = load_library()
     rc = lib.pa_decode_v1(_p(out), _p(q), _p(k_cache), _p(v_cache), _p(block_tables), _p(seq_lens),
-                          S, H, KVH, D, B, MB, NB, float(scale), _stream(q, stream))
+                          S, H, KVH, D, B, MB, NB, float(scale), kv_dtype_of(k_cache),
+                          float(k_scale), float(v_scale), _stream(q, stream))
     _check(rc, "pa_decode_v1")
     return out
 
 
 def pa_decode_v2(tmp_out, exp_sums, max_logits, q, k_cache, v_cache, block_tables, seq_lens,
-                 scale: float, partition_size: int, stream=None):
+                 scale: float, partition_size: int, k_scale: float = 1.0, v_scale: float = 1.0,
+                 stream=None):
     """Per-partition partials (tmp_out[S,P,H,D], exp_sums/max_logits[S,P,H])."""
     S, H, KVH, D, B, NB, MB = _decode_common(q, k_cache, v_cache, block_tables, seq_lens)
     _want(tmp_out, "tmp_out", torch.float32, 4, q.device)
@@ -167,7 +189,8 @@ def pa_decode_v2(tmp_out, exp_sums, max_logits, q, k_cache, v_cache, block_table
     lib = load_library()
     rc = lib.pa_decode_v2(_p(tmp_out), _p(exp_sums), _p(max_logits), _p(q), _p(k_cache),
                           _p(v_cache), _p(block_tables), _p(seq_lens), S, H, KVH, D, B, MB, NB,
-                          P, int(partition_size), float(scale), _stream(q, stream))
+                          P, int(partition_size), float(scale), kv_dtype_of(k_cache),
+                          float(k_scale), float(v_scale), _stream(q, stream))
     _check(rc, "pa_decode_v2")
 
 
@@ -190,8 +213,10 @@ def pa_reduce(out, tmp_out, exp_sums, max_logits, seq_lens, partition_size: int,
     return out
 
 
-def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, stream=None):
-    """Scatter key/value [T,KVH,D] into the pools at slot_mapping[T] (int64)."""
+def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, k_scale: float = 1.0,
+                      v_scale: float = 1.0, stream=None):
+    """Scatter key/value [T,KVH,D] into the pools at slot_mapping[T] (int64);
+    into fp8 pools as E4M3 codes of key / k_scale and value / v_scale."""
     NB, KVH, D, B = _cache_dims(k_cache, v_cache)
     dev = k_cache.device
     for name, t in (("key", key), ("value", value)):
@@ -206,7 +231,8 @@ def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, stream=None):
     lib = load_library()
     rc = lib.reshape_and_cache(_p(key), _p(value), _p(k_cache), _p(v_cache), _p(slot_mapping), T, KVH,
                                D, B, NB, key.stride(0) if T else KVH * D,
-                               value.stride(0) if T else KVH * D, _stream(key, stream))
+                               value.stride(0) if T else KVH * D, kv_dtype_of(k_cache),
+                               float(k_scale), float(v_scale), _stream(key, stream))
     _check(rc, "reshape_and_cache")
 
 
@@ -217,13 +243,13 @@ def pa_gather_kv(k_out, v_out, k_cache, v_cache, block_tables, seq_lens, cu_seq_
     _want(block_tables, "block_tables", torch.int32, 2, dev)
     _want(seq_lens, "seq_lens", torch.int32, 1, dev)
     _want(cu_seq_lens, "cu_seq_lens", torch.int64, 1, dev)
-    _want(k_out, "k_out", torch.float16, 3, dev)
-    _want(v_out, "v_out", torch.float16, 3, dev)
+    _want(k_out, "k_out", k_cache.dtype, 3, dev)
+    _want(v_out, "v_out", k_cache.dtype, 3, dev)
     S, MB = block_tables.shape
     lib = load_library()
     rc = lib.pa_gather_kv(_p(k_out), _p(v_out), _p(k_cache), _p(v_cache), _p(block_tables),
                           _p(seq_lens), _p(cu_seq_lens), S, KVH, D, B, MB, NB,
-                          _stream(k_cache, stream))
+                          kv_dtype_of(k_cache), _stream(k_cache, stream))
     _check(rc, "pa_gather_kv")
 
 
@@ -231,9 +257,10 @@ def pa_gather_kv(k_out, v_out, k_cache, v_cache, block_tables, seq_lens, cu_seq_
 # Conveniences that allocate their outputs with torch (plumbing only)
 # --------------------------------------------------------------------------
 
-def paged_attention_v1(q, k_cache, v_cache, block_tables, seq_lens, scale: float):
+def paged_attention_v1(q, k_cache, v_cache, block_tables, seq_lens, scale: float,
+                       k_scale: float = 1.0, v_scale: float = 1.0):
     out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
-    return pa_decode_v1(out, q, k_cache, v_cache, block_tables, seq_lens, scale)
+    return pa_decode_v1(out, q, k_cache, v_cache, block_tables, seq_lens, scale, k_scale, v_scale)
 
 
 def v2_scratch(num_seqs: int, num_heads: int, head_size: int, max_num_partitions: int, device):
@@ -245,13 +272,15 @@ def v2_scratch(num_seqs: int, num_heads: int, head_size: int, max_num_partitions
 
 
 def paged_attention_v2(q, k_cache, v_cache, block_tables, seq_lens, scale: float,
-                       partition_size: int = 512, max_seq_len: Optional[int] = None):
+                       partition_size: int = 512, max_seq_len: Optional[int] = None,
+                       k_scale: float = 1.0, v_scale: float = 1.0):
     S, H, D = q.shape
     if max_seq_len is None:
         max_seq_len = block_tables.shape[1] * k_cache.shape[3]
     P = pa_v2_max_partitions(max_seq_len, partition_size)
     tmp, es, ml = v2_scratch(S, H, D, P, q.device)
-    pa_decode_v2(tmp, es, ml, q, k_cache, v_cache, block_tables, seq_lens, scale, partition_size)
+    pa_decode_v2(tmp, es, ml, q, k_cache, v_cache, block_tables, seq_lens, scale, partition_size,
+                 k_scale, v_scale)
     out = torch.empty((S, H, D), dtype=torch.float32, device=q.device)
     return pa_reduce(out, tmp, es, ml, seq_lens, partition_size)
 
@@ -373,5 +402,6 @@ def copy_blocks(k_cache, v_cache, block_pairs, stream=None):
     if block_pairs.shape[1] != 2:
         raise ValueError("block_pairs must be [num_pairs, 2]")
     rc = load_library().copy_blocks(_p(k_cache), _p(v_cache), _p(block_pairs),
-                                    block_pairs.shape[0], KVH, D, B, NB, _stream(k_cache, stream))
+                                    block_pairs.shape[0], KVH, D, B, NB, kv_dtype_of(k_cache),
+                                    _stream(k_cache, stream))
     _check(rc, "copy_blocks")

@@ -7,7 +7,10 @@
 // head dims).  The chunk is one 16-byte load of key; in the x-packed K pool it
 // is one 16-byte store (k_cache[b, h, c, o, 0..7]).  V is stored transposed
 // (v_cache[b, h, d, o]): the same 16-byte load of value becomes eight 2-byte
-// stores 32 bytes apart.  A pure copy, so bit-exact.
+// stores 32 bytes apart.  A pure copy, so bit-exact.  Into an fp8 pool each
+// element becomes its E4M3 code of x / scale (nearest, ties to even,
+// saturated at +-448, NaN -> 0x7F), the division in fp32: the K chunk is an
+// 8-byte store (half of a 16-element x chunk), V eight 1-byte stores.
 //
 // pa_gather_kv: the inverse, for testing the read-side indirection alone.
 // One thread per (sequence, logical block, token slot, KV head, chunk).
@@ -49,12 +52,44 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
 }
 
 template <int D>
+__global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
+    const f16* __restrict__ key, const f16* __restrict__ value, uint8_t* __restrict__ k_cache,
+    uint8_t* __restrict__ v_cache, const int64_t* __restrict__ slot_mapping, int num_tokens,
+    int num_kv_heads, long long num_slots, long long key_stride, long long value_stride,
+    float k_scale, float v_scale) {
+    constexpr int C = D / kX;          // 8-element chunks of a head
+    const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    const long long total = (long long)num_tokens * num_kv_heads * C;
+    if (gid >= total) return;
+    const int c = (int)(gid % C);
+    const int h = (int)((gid / C) % num_kv_heads);
+    const int i = (int)(gid / ((long long)C * num_kv_heads));
+    const long long slot = slot_mapping[i];
+    if (slot < 0 || slot >= num_slots) return;
+    const long long b = slot / kBlock;
+    const int o = (int)(slot % kBlock);
+    const f16x8 kv = *reinterpret_cast<const f16x8*>(key + i * key_stride + h * D + c * kX);
+    const f16x8 vv = *reinterpret_cast<const f16x8*>(value + i * value_stride + h * D + c * kX);
+    u32x2 kc = {0u, 0u};
+#pragma unroll
+    for (int j = 0; j < kX; ++j) kc[j >> 2] |= f32_to_e4m3((float)kv[j] / k_scale) << (8 * (j & 3));
+    const size_t tile = ((size_t)b * num_kv_heads + h) * (size_t)(D * kBlock);   // bytes
+    // d = 8c + j lives in x-chunk d / 16 at element d % 16 = 8(c % 2) + j
+    *reinterpret_cast<u32x2*>(k_cache + tile + ((size_t)(c >> 1) * kBlock + o) * kX8 + 8 * (c & 1)) = kc;
+    uint8_t* vdst = v_cache + tile + (size_t)(c * kX) * kBlock + o;
+#pragma unroll
+    for (int j = 0; j < kX; ++j) vdst[j * kBlock] = (uint8_t)f32_to_e4m3((float)vv[j] / v_scale);
+}
+
+template <int D, class T>
 __global__ __launch_bounds__(256) void gather_kv_kernel(
-    f16* __restrict__ k_out, f16* __restrict__ v_out, const f16* __restrict__ k_cache,
-    const f16* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
+    T* __restrict__ k_out, T* __restrict__ v_out, const T* __restrict__ k_cache,
+    const T* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ seq_lens, const int64_t* __restrict__ cu_seq_lens,
-    int num_kv_heads, int max_blocks_per_seq, int num_blocks, int wgs_per_block) {
-    constexpr int C = D / kX;
+    int num_kv_heads, int max_blocks_per_seq, int num_blocks, int wgs_per_block, T nan) {
+    constexpr int X = 16 / sizeof(T);  // elements per 16-byte K chunk
+    constexpr int C = D / X;
+    typedef T chunk_t __attribute__((ext_vector_type(X)));
     // workgroup -> (sequence, logical block, part of the block's items)
     const int sb = blockIdx.x / wgs_per_block;
     const int part = blockIdx.x - sb * wgs_per_block;
@@ -70,19 +105,18 @@ __global__ __launch_bounds__(256) void gather_kv_kernel(
     if (t >= L || lb >= max_blocks_per_seq) return;
     const int phys = block_tables[(size_t)s * max_blocks_per_seq + lb];
     const size_t row = ((size_t)cu_seq_lens[s] + t) * num_kv_heads + h;
-    f16x8 kv, vv;
+    chunk_t kv, vv;
     if (phys < 0 || phys >= num_blocks) {
-        const f16 nan = __builtin_bit_cast(f16, (unsigned short)0x7E00);
-        for (int j = 0; j < kX; ++j) kv[j] = vv[j] = nan;
+        for (int j = 0; j < X; ++j) kv[j] = vv[j] = nan;
     } else {
         const size_t tile = ((size_t)phys * num_kv_heads + h) * (size_t)(D * kBlock);
-        kv = *reinterpret_cast<const f16x8*>(k_cache + tile + ((size_t)c * kBlock + o) * kX);
-        const f16* vsrc = v_cache + tile + (size_t)(c * kX) * kBlock + o;
+        kv = *reinterpret_cast<const chunk_t*>(k_cache + tile + ((size_t)c * kBlock + o) * X);
+        const T* vsrc = v_cache + tile + (size_t)(c * X) * kBlock + o;
 #pragma unroll
-        for (int j = 0; j < kX; ++j) vv[j] = vsrc[j * kBlock];
+        for (int j = 0; j < X; ++j) vv[j] = vsrc[j * kBlock];
     }
-    *reinterpret_cast<f16x8*>(k_out + row * D + c * kX) = kv;
-    *reinterpret_cast<f16x8*>(v_out + row * D + c * kX) = vv;
+    *reinterpret_cast<chunk_t*>(k_out + row * D + c * X) = kv;
+    *reinterpret_cast<chunk_t*>(v_out + row * D + c * X) = vv;
 }
 
 __global__ __launch_bounds__(256) void copy_blocks_kernel(
@@ -106,15 +140,17 @@ using namespace pa;
 
 extern "C" int copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs, int num_pairs,
                            int num_kv_heads, int head_size, int block_size, int num_blocks,
-                           void* stream) {
+                           int kv_cache_dtype, void* stream) {
     int rc = check_head_block(head_size, block_size);
+    if (rc != PA_OK) return rc;
+    rc = check_kv_dtype(kv_cache_dtype, 1.f, 1.f);
     if (rc != PA_OK) return rc;
     if (num_pairs < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PA_ERR_INVALID_ARG;
     if (!k_cache || !v_cache) return PA_ERR_INVALID_ARG;
     if (num_pairs == 0) return PA_OK;   // block_pairs may be NULL then
     if (!block_pairs) return PA_ERR_INVALID_ARG;
     if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned4(block_pairs)) return PA_ERR_MISALIGNED;
-    const long long chunks = (long long)num_kv_heads * head_size * kBlock / kX;
+    const long long chunks = (long long)num_kv_heads * head_size * kBlock * kv_elem_bytes(kv_cache_dtype) / 16;
     const long long parts = (chunks + 255) / 256;
     if (parts > 65535) return PA_ERR_INVALID_ARG;
     hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)num_pairs, (unsigned)parts), dim3(256), 0,
@@ -126,8 +162,11 @@ extern "C" int copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pa
 extern "C" int reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
                                  const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
                                  int head_size, int block_size, int num_blocks,
-                                 int64_t key_stride, int64_t value_stride, void* stream) {
+                                 int64_t key_stride, int64_t value_stride, int kv_cache_dtype,
+                                 float k_scale, float v_scale, void* stream) {
     int rc = check_head_block(head_size, block_size);
+    if (rc != PA_OK) return rc;
+    rc = check_kv_dtype(kv_cache_dtype, k_scale, v_scale);
     if (rc != PA_OK) return rc;
     if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PA_ERR_INVALID_ARG;
     const int64_t row = (int64_t)num_kv_heads * head_size;
@@ -145,6 +184,19 @@ extern "C" int reshape_and_cache(const void* key, const void* value, void* k_cac
     hipStream_t st = as_stream(stream);
     auto k = static_cast<const f16*>(key);
     auto v = static_cast<const f16*>(value);
+    if (kv_cache_dtype == PA_KV_FP8_E4M3) {
+        auto kc8 = static_cast<uint8_t*>(k_cache);
+        auto vc8 = static_cast<uint8_t*>(v_cache);
+        if (head_size == 128)
+            hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<128>, dim3((unsigned)grid), dim3(256), 0,
+                               st, k, v, kc8, vc8, slot_mapping, num_tokens, num_kv_heads, slots,
+                               (long long)key_stride, (long long)value_stride, k_scale, v_scale);
+        else
+            hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<64>, dim3((unsigned)grid), dim3(256), 0,
+                               st, k, v, kc8, vc8, slot_mapping, num_tokens, num_kv_heads, slots,
+                               (long long)key_stride, (long long)value_stride, k_scale, v_scale);
+        return launch_status();
+    }
     auto kc = static_cast<f16*>(k_cache);
     auto vc = static_cast<f16*>(v_cache);
     if (head_size == 128)
@@ -162,8 +214,10 @@ extern "C" int pa_gather_kv(void* k_out, void* v_out, const void* k_cache, const
                             const int32_t* block_tables, const int32_t* seq_lens,
                             const int64_t* cu_seq_lens, int num_seqs, int num_kv_heads,
                             int head_size, int block_size, int max_blocks_per_seq, int num_blocks,
-                            void* stream) {
+                            int kv_cache_dtype, void* stream) {
     int rc = check_head_block(head_size, block_size);
+    if (rc != PA_OK) return rc;
+    rc = check_kv_dtype(kv_cache_dtype, 1.f, 1.f);
     if (rc != PA_OK) return rc;
     if (num_seqs < 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0)
         return PA_ERR_INVALID_ARG;
@@ -173,22 +227,26 @@ extern "C" int pa_gather_kv(void* k_out, void* v_out, const void* k_cache, const
         !aligned4(block_tables) || !aligned4(seq_lens) || !aligned8(cu_seq_lens))
         return PA_ERR_MISALIGNED;
     if (num_seqs == 0) return PA_OK;
-    const int items = kBlock * num_kv_heads * (head_size / kX);
+    const bool fp8 = kv_cache_dtype == PA_KV_FP8_E4M3;
+    const int items = kBlock * num_kv_heads * (head_size / (fp8 ? kX8 : kX));
     const int wgs = (items + 255) / 256;
     const long long grid = (long long)num_seqs * max_blocks_per_seq * wgs;
     if (grid > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
     hipStream_t st = as_stream(stream);
-    auto ko = static_cast<f16*>(k_out);
-    auto vo = static_cast<f16*>(v_out);
-    auto kc = static_cast<const f16*>(k_cache);
-    auto vc = static_cast<const f16*>(v_cache);
-    if (head_size == 128)
-        hipLaunchKernelGGL(gather_kv_kernel<128>, dim3((unsigned)grid), dim3(256), 0, st, ko, vo,
-                           kc, vc, block_tables, seq_lens, cu_seq_lens, num_kv_heads,
-                           max_blocks_per_seq, num_blocks, wgs);
-    else
-        hipLaunchKernelGGL(gather_kv_kernel<64>, dim3((unsigned)grid), dim3(256), 0, st, ko, vo,
-                           kc, vc, block_tables, seq_lens, cu_seq_lens, num_kv_heads,
-                           max_blocks_per_seq, num_blocks, wgs);
+#define PA_GATHER(DD, T, NANV)                                                                     \
+    hipLaunchKernelGGL((gather_kv_kernel<DD, T>), dim3((unsigned)grid), dim3(256), 0, st,          \
+                       static_cast<T*>(k_out), static_cast<T*>(v_out),                            \
+                       static_cast<const T*>(k_cache), static_cast<const T*>(v_cache),            \
+                       block_tables, seq_lens, cu_seq_lens, num_kv_heads, max_blocks_per_seq,     \
+                       num_blocks, wgs, NANV)
+    const f16 nan16 = __builtin_bit_cast(f16, (unsigned short)0x7E00);
+    if (fp8) {
+        if (head_size == 128) PA_GATHER(128, uint8_t, (uint8_t)0x7F);
+        else PA_GATHER(64, uint8_t, (uint8_t)0x7F);
+    } else {
+        if (head_size == 128) PA_GATHER(128, f16, nan16);
+        else PA_GATHER(64, f16, nan16);
+    }
+#undef PA_GATHER
     return launch_status();
 }

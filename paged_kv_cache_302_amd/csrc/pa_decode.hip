@@ -84,8 +84,8 @@ namespace pa {
 // buffer load returns zeros without touching memory.
 constexpr int kBufferDword3 = 0x00020000;   // raw 32-bit data format, no swizzle
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const f16* tile, int bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<f16*>(tile), 0, bytes, kBufferDword3);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* tile, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(tile), 0, bytes, kBufferDword3);
 }
 
 template <bool NT, class T>
@@ -93,8 +93,10 @@ __device__ __forceinline__ T ld_tile(__amdgpu_buffer_rsrc_t r, int off) {
     constexpr int cpol = NT ? 2 : 0;   // 2 = nontemporal
     if constexpr (sizeof(T) == 16)
         return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, cpol));
-    else
+    else if constexpr (sizeof(T) == 8)
         return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, cpol));
+    else
+        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, cpol));
 }
 
 // Results are written once and not re-read by this kernel.  Plain stores
@@ -118,8 +120,8 @@ struct DecodeParams {
     float* exp_sums;      // v2: [S,H,P]
     float* max_logits;    // v2: [S,H,P]
     const f16* q;
-    const f16* k_cache;
-    const f16* v_cache;
+    const char* k_cache;  // pools as bytes: fp16 or fp8 (E4M3) elements
+    const char* v_cache;
     const int32_t* block_tables;
     const int32_t* seq_lens;
     int num_seqs;
@@ -131,8 +133,9 @@ struct DecodeParams {
     int num_blocks;
     int max_num_partitions;
     int partition_size;   // tokens, multiple of 16 (v2)
-    float scale;          // natural units
+    float scale;          // natural units (fp8: scale * k_scale)
     float scale_log2;     // scale * log2(e)
+    float v_scale;        // fp8: V's per-tensor scale; fp16: 1
 };
 
 // --------------------------------------------------------------------------
@@ -156,6 +159,7 @@ struct MfmaPath {
     static constexpr int KC = D / 32;   // 16x16x32 steps for the scores
     static constexpr int NT = D / 16;   // 16-wide head-dim tiles of the output
     static constexpr int kHeads = 16;
+    static constexpr int kElem = 2;     // bytes per cache element (fp16)
 
     struct Tile {
         f16x8 k[KC];   // lane (g,i): K[t=i][d = 32c + 8g .. +7]
@@ -188,7 +192,7 @@ struct MfmaPath {
     }
 
     template <bool NTL>
-    __device__ __forceinline__ static void load(Tile& t, const f16* kt, const f16* vt, int bytes) {
+    __device__ __forceinline__ static void load(Tile& t, const char* kt, const char* vt, int bytes) {
         const int l = lane_id(), i = l & 15, g = l >> 4;
         const auto rk = tile_rsrc(kt, bytes), rv = tile_rsrc(vt, bytes);
 #pragma unroll
@@ -256,6 +260,7 @@ template <int D>
 struct ValuPath {
     static constexpr int KC = D / 32;
     static constexpr int kHeads = 1;
+    static constexpr int kElem = 2;
 
     struct Tile {
         f16x8 k[KC];   // lane l: K[t = l%16][d = 32c + 8(l/16) .. +7]
@@ -285,7 +290,7 @@ struct ValuPath {
     }
 
     template <bool NTL>
-    __device__ __forceinline__ static void load(Tile& t, const f16* kt, const f16* vt, int bytes) {
+    __device__ __forceinline__ static void load(Tile& t, const char* kt, const char* vt, int bytes) {
         const int l = lane_id();
         const auto rk = tile_rsrc(kt, bytes), rv = tile_rsrc(vt, bytes);
 #pragma unroll
@@ -347,6 +352,207 @@ struct ValuPath {
             const float full = st.acc[c] + dpp<kDppXor1>(st.acc[c]);
             if ((l & 1) == 0) s_acc[32 * c + (l >> 1)] = full;
         }
+        if (l == 0) {
+            s_m[0] = st.m;
+            s_l[0] = ltot;
+        }
+    }
+};
+
+// --------------------------------------------------------------------------
+// fp8 (E4M3) cache, MFMA path.  The K pool packs 16 head dims per token
+// chunk, so lane (g,i) loads token i's dims 16(g + 4r) .. +15 of k-chunk r
+// with one 16-byte request per 64 dims; each 16 dims feed two 16x16x32
+// score steps after an exact E4M3 -> fp16 conversion.  The sum over d does
+// not care which dims a step takes, as long as Q^T is loaded the same way:
+// step c uses d = 16(g + 4(c/2)) + 8(c%2) + e.  V rows are 16 bytes (one per
+// head dim, 16 tokens), and lane (g,i) takes the 4 tokens 4g..4g+3 of row
+// 16nt + i, the A operand of the PV step.  k_scale is folded into the
+// softmax scale and v_scale into the final normalisation.
+// --------------------------------------------------------------------------
+template <int D>
+struct MfmaPath8 : MfmaPath<D> {
+    using Base = MfmaPath<D>;
+    static constexpr int KC = D / 32;
+    static constexpr int KR = D / 64;   // 16-byte K chunks per lane
+    static constexpr int NT = D / 16;
+    static constexpr int kElem = 1;
+
+    struct Tile {
+        u32x4 k[KR];    // lane (g,i): K codes of token i, dims 16(g + 4r) .. +15
+        uint32_t v[NT]; // lane (g,i): V codes of dim 16nt + i, tokens 4g .. 4g+3
+    };
+    struct QRegs {
+        f16x8 q[KC];    // lane (g,i): Q[h = i][d = 16(g + 4(c/2)) + 8(c%2) .. +7]
+    };
+
+    __device__ static void load_q(QRegs& qr, const DecodeParams& p, int s, int h0, int nh) {
+        const int l = lane_id(), i = l & 15, g = l >> 4;
+        const f16* qrow = p.q + ((size_t)s * p.num_heads + h0 + i) * D;
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+            f16x8 z = {};
+            const int d0 = 16 * (g + 4 * (c >> 1)) + 8 * (c & 1);
+            qr.q[c] = (i < nh) ? *reinterpret_cast<const f16x8*>(qrow + d0) : z;
+        }
+    }
+
+    template <bool NTL>
+    __device__ __forceinline__ static void load(Tile& t, const char* kt, const char* vt, int bytes) {
+        const int l = lane_id(), i = l & 15, g = l >> 4;
+        const auto rk = tile_rsrc(kt, bytes), rv = tile_rsrc(vt, bytes);
+#pragma unroll
+        for (int r = 0; r < KR; ++r) t.k[r] = ld_tile<NTL, u32x4>(rk, 16 * (l + 64 * r));
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) t.v[nt] = ld_tile<NTL, uint32_t>(rv, 16 * (16 * nt + i) + 4 * g);
+    }
+
+    __device__ __forceinline__ static void process(typename Base::State& st, Tile& t,
+                                                   const QRegs& qr, int nvalid, float sl2) {
+        const int l = lane_id(), g = l >> 4;
+        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+            const uint32_t w0 = t.k[c >> 1][2 * (c & 1)], w1 = t.k[c >> 1][2 * (c & 1) + 1];
+            const f16x4 a0 = e4m3x4_to_f16x4(w0), a1 = e4m3x4_to_f16x4(w1);
+            const f16x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+            s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qr.q[c], s, 0, 0, 0);
+        }
+        if (nvalid < kBlock) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (4 * g + r >= nvalid) s[r] = -INFINITY;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) t.v[nt] = keep_tokens(t.v[nt], 4 * g, nvalid);
+        }
+        float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+        bm = col4_max(bm);
+        const float mn = fmaxf(st.m, bm);
+        const float corr = exp2_fast((st.m - mn) * sl2);
+        float pr[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pr[r] = exp2_fast((s[r] - mn) * sl2);
+        st.l = st.l * corr + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+        st.m = mn;
+        const f16x4 pv = {(f16)pr[0], (f16)pr[1], (f16)pr[2], (f16)pr[3]};
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            st.acc[nt] *= corr;
+            st.acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(e4m3x4_to_f16x4(t.v[nt]), pv,
+                                                               st.acc[nt], 0, 0, 0);
+        }
+    }
+};
+
+// --------------------------------------------------------------------------
+// fp8 (E4M3) cache, VALU path (G == 1).  Scores as in the fp16 path, with
+// lane l holding token l%16's dims 16(l/16 + 4r) .. +15.  A V row is the 16
+// tokens of one head dim in 16 bytes, so lane l takes whole rows d = 64r + l
+// and needs all 16 weights: the eight fp16 weight pairs are the same for
+// every lane and are read into scalar registers (v_readlane), and each
+// lane's output dims are complete without a cross-lane sum.
+// --------------------------------------------------------------------------
+template <int D>
+struct ValuPath8 {
+    static constexpr int KR = D / 64;
+    static constexpr int kHeads = 1;
+    static constexpr int kElem = 1;
+
+    struct Tile {
+        u32x4 k[KR];   // lane l: K codes of token l%16, dims 16(l/16 + 4r) .. +15
+        u32x4 v[KR];   // lane l: V codes of dim 64r + l, tokens 0..15
+    };
+    struct State {
+        float acc[KR]; // lane l: O[d = 64r + l], unnormalised
+        float m;       // running max of raw dot products
+        float l;       // sum of weights of token l%16 over blocks
+    };
+    struct QRegs {
+        f16x8 q[2 * KR];   // lane l: q[d = 16(l/16 + 4r) + 8j .. +7] at index 2r + j
+    };
+
+    __device__ static void load_q(QRegs& qr, const DecodeParams& p, int s, int h0, int) {
+        const int g = lane_id() >> 4;
+        const f16* qrow = p.q + ((size_t)s * p.num_heads + h0) * D;
+#pragma unroll
+        for (int r = 0; r < KR; ++r)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                qr.q[2 * r + j] = *reinterpret_cast<const f16x8*>(qrow + 16 * (g + 4 * r) + 8 * j);
+    }
+
+    __device__ static void init(State& st) {
+#pragma unroll
+        for (int r = 0; r < KR; ++r) st.acc[r] = 0.f;
+        st.m = -INFINITY;
+        st.l = 0.f;
+    }
+
+    template <bool NTL>
+    __device__ __forceinline__ static void load(Tile& t, const char* kt, const char* vt, int bytes) {
+        const int l = lane_id();
+        const auto rk = tile_rsrc(kt, bytes), rv = tile_rsrc(vt, bytes);
+#pragma unroll
+        for (int r = 0; r < KR; ++r) t.k[r] = ld_tile<NTL, u32x4>(rk, 16 * (l + 64 * r));
+#pragma unroll
+        for (int r = 0; r < KR; ++r) t.v[r] = ld_tile<NTL, u32x4>(rv, 16 * (64 * r + l));
+    }
+
+    __device__ __forceinline__ static void process(State& st, Tile& t, const QRegs& qr,
+                                                   int nvalid, float sl2) {
+        const int l = lane_id(), i = l & 15;
+        float part = 0.f;
+#pragma unroll
+        for (int r = 0; r < KR; ++r)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const f16x8& qh = qr.q[2 * r + (w >> 1)];
+                const int e = 4 * (w & 1);
+                const f16x4 kk = e4m3x4_to_f16x4(t.k[r][w]);
+                part = dot2(f16x2{kk[0], kk[1]}, f16x2{qh[e], qh[e + 1]}, part);
+                part = dot2(f16x2{kk[2], kk[3]}, f16x2{qh[e + 2], qh[e + 3]}, part);
+            }
+        float z = col4_sum(part);               // dot of token i, in every row
+        if (nvalid < kBlock) {
+            if (i >= nvalid) z = -INFINITY;
+#pragma unroll
+            for (int r = 0; r < KR; ++r)
+#pragma unroll
+                for (int w = 0; w < 4; ++w) t.v[r][w] = keep_tokens(t.v[r][w], 4 * w, nvalid);
+        }
+        const float bm = row16_max(z);
+        const float mn = fmaxf(st.m, bm);
+        const float corr = exp2_fast((st.m - mn) * sl2);
+        const float pw = exp2_fast((z - mn) * sl2);
+        st.l = st.l * corr + pw;
+        st.m = mn;
+        // even lane t holds the fp16 pair (p_t, p_{t+1}); every lane needs all
+        // eight pairs, which are wave-uniform
+        const int pair_bits = __builtin_bit_cast(int, pack2(pw, dpp<kDppXor1>(pw)));
+        f16x2 wp[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            wp[k] = __builtin_bit_cast(f16x2, __builtin_amdgcn_readlane(pair_bits, 2 * k));
+#pragma unroll
+        for (int r = 0; r < KR; ++r) {
+            float a = st.acc[r] * corr;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const f16x4 vv = e4m3x4_to_f16x4(t.v[r][w]);
+                a = dot2(f16x2{vv[0], vv[1]}, wp[2 * w], a);
+                a = dot2(f16x2{vv[2], vv[3]}, wp[2 * w + 1], a);
+            }
+            st.acc[r] = a;
+        }
+    }
+
+    __device__ static float wave_l(const State& st) { return row16_sum(st.l); }
+
+    __device__ static void stage(const State& st, float ltot, float* s_acc, float* s_m,
+                                 float* s_l, int) {
+        const int l = lane_id();
+#pragma unroll
+        for (int r = 0; r < KR; ++r) s_acc[64 * r + l] = st.acc[r];
         if (l == 0) {
             s_m[0] = st.m;
             s_l[0] = ltot;
@@ -496,10 +702,10 @@ void pa_decode_kernel(DecodeParams p) {
     // this wave's blocks: blk_begin + w + k*NW, k < n
     const int first = blk_begin + w;
     const int n = first < blk_end ? (blk_end - first + NW - 1) / NW : 0;
-    const size_t tile = (size_t)D * kBlock;
-    const f16* kbase = p.k_cache + (size_t)kvh * tile;
-    const f16* vbase = p.v_cache + (size_t)kvh * tile;
-    const size_t blk_stride = (size_t)p.num_kv_heads * tile;
+    constexpr int TB = D * kBlock * Path::kElem;           // bytes of one K or V tile
+    const char* kbase = p.k_cache + (size_t)kvh * TB;
+    const char* vbase = p.v_cache + (size_t)kvh * TB;
+    const size_t blk_stride = (size_t)p.num_kv_heads * TB;
     const int32_t* row = p.block_tables + (size_t)s * p.max_blocks_per_seq;
     const float sl2 = p.scale_log2;
 
@@ -531,7 +737,6 @@ void pa_decode_kernel(DecodeParams p) {
         auto tile_k = [&](int id) { return kbase + (size_t)id * blk_stride; };
         auto tile_v = [&](int id) { return vbase + (size_t)id * blk_stride; };
         auto valid = [&](int k) { return min(kBlock, tok_end - (first + k * NW) * kBlock); };
-        constexpr int TB = D * kBlock * 2;                    // bytes of one K or V tile
         auto live = [&](int j) { return j < n ? TB : 0; };
         auto walk = [&](auto nt_tag) {
             constexpr bool NTL = decltype(nt_tag)::value;
@@ -579,7 +784,7 @@ void pa_decode_kernel(DecodeParams p) {
         const f32x4* src = reinterpret_cast<const f32x4*>(s_o);
         const int nv = nh * D / 4;
         for (int e = lane_id(); e < nv; e += 64) {
-            const float inv = 1.f / s_l[(4 * e) / D];
+            const float inv = p.v_scale / s_l[(4 * e) / D];
             f32x4 v = src[e] * inv;
             if (bad) v = f32x4{NAN, NAN, NAN, NAN};
             st_stream(reinterpret_cast<f32x4*>(out_h0) + e, v);
@@ -619,7 +824,7 @@ void pa_decode_kernel(DecodeParams p) {
                 num += s_acc[(v * nh + j) * D + d] * f;
                 den += s_l[v * HP + j] * f;
             }
-            st_stream(out_h0 + (size_t)j * out_head_stride + d, any_bad ? NAN : num / den);
+            st_stream(out_h0 + (size_t)j * out_head_stride + d, any_bad ? NAN : num / den * p.v_scale);
             if (V2 && d == 0) {
                 s_fin[j] = M;
                 s_fin[16 + j] = den;
@@ -661,9 +866,17 @@ static int launch_nw(int NW, const DecodeParams& p, int grid, int nh_max, hipStr
 }
 
 template <bool V2>
-static int launch_decode(const DecodeParams& p, int head_size, int NW, int grid, hipStream_t st) {
+static int launch_decode(const DecodeParams& p, int head_size, bool fp8, int NW, int grid,
+                         hipStream_t st) {
     const bool mfma = p.group >= 2;
     const int nh_max = mfma ? (p.group < 16 ? p.group : 16) : 1;
+    if (fp8) {
+        if (head_size == 128)
+            return mfma ? launch_nw<MfmaPath8<128>, 128, V2>(NW, p, grid, nh_max, st)
+                        : launch_nw<ValuPath8<128>, 128, V2>(NW, p, grid, nh_max, st);
+        return mfma ? launch_nw<MfmaPath8<64>, 64, V2>(NW, p, grid, nh_max, st)
+                    : launch_nw<ValuPath8<64>, 64, V2>(NW, p, grid, nh_max, st);
+    }
     if (head_size == 128)
         return mfma ? launch_nw<MfmaPath<128>, 128, V2>(NW, p, grid, nh_max, st)
                     : launch_nw<ValuPath<128>, 128, V2>(NW, p, grid, nh_max, st);
@@ -674,8 +887,11 @@ static int launch_decode(const DecodeParams& p, int head_size, int NW, int grid,
 static int check_decode_args(const void* q, const void* k_cache, const void* v_cache,
                              const int32_t* block_tables, const int32_t* seq_lens, int num_seqs,
                              int num_heads, int num_kv_heads, int head_size, int block_size,
-                             int max_blocks_per_seq, int num_blocks, float scale) {
+                             int max_blocks_per_seq, int num_blocks, float scale,
+                             int kv_cache_dtype, float k_scale, float v_scale) {
     int rc = check_head_block(head_size, block_size);
+    if (rc != PA_OK) return rc;
+    rc = check_kv_dtype(kv_cache_dtype, k_scale, v_scale);
     if (rc != PA_OK) return rc;
     if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
         num_blocks <= 0)
@@ -692,11 +908,15 @@ static int check_decode_args(const void* q, const void* k_cache, const void* v_c
 static DecodeParams make_params(const void* q, const void* k_cache, const void* v_cache,
                                 const int32_t* block_tables, const int32_t* seq_lens,
                                 int num_seqs, int num_heads, int num_kv_heads,
-                                int max_blocks_per_seq, int num_blocks, float scale) {
+                                int max_blocks_per_seq, int num_blocks, float scale,
+                                int kv_cache_dtype, float k_scale, float v_scale) {
     DecodeParams p{};
+    const bool fp8 = kv_cache_dtype == PA_KV_FP8_E4M3;
+    if (fp8) scale *= k_scale;   // logits of the scaled keys: scale * k_scale * (q . code)
+    p.v_scale = fp8 ? v_scale : 1.0f;
     p.q = static_cast<const f16*>(q);
-    p.k_cache = static_cast<const f16*>(k_cache);
-    p.v_cache = static_cast<const f16*>(v_cache);
+    p.k_cache = static_cast<const char*>(k_cache);
+    p.v_cache = static_cast<const char*>(v_cache);
     p.block_tables = block_tables;
     p.seq_lens = seq_lens;
     p.num_seqs = num_seqs;
@@ -719,8 +939,8 @@ static DecodeParams make_params(const void* q, const void* k_cache, const void* 
 // because unit sizes vary with the sequence lengths, and the waves of the
 // longest unit set the critical path.  No more waves than a quarter of a
 // unit's blocks.
-static int pick_waves(long long units, long long blocks_per_unit, int head_size) {
-    const long long tile_bytes = 2LL * kBlock * head_size * 2;   // K + V, fp16
+static int pick_waves(long long units, long long blocks_per_unit, int head_size, int elem) {
+    const long long tile_bytes = 2LL * kBlock * head_size * elem;   // K + V
     const long long target = (8LL << 20) / tile_bytes;
     int nw = 1;
     while (nw < 8 && units * nw < target && (long long)(nw * 2) * 4 <= blocks_per_unit) nw *= 2;
@@ -734,21 +954,25 @@ using namespace pa;
 extern "C" int pa_decode_v1(float* out, const void* q, const void* k_cache, const void* v_cache,
                             const int32_t* block_tables, const int32_t* seq_lens, int num_seqs,
                             int num_heads, int num_kv_heads, int head_size, int block_size,
-                            int max_blocks_per_seq, int num_blocks, float scale, void* stream) {
+                            int max_blocks_per_seq, int num_blocks, float scale,
+                            int kv_cache_dtype, float k_scale, float v_scale, void* stream) {
     int rc = check_decode_args(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_heads,
                                num_kv_heads, head_size, block_size, max_blocks_per_seq, num_blocks,
-                               scale);
+                               scale, kv_cache_dtype, k_scale, v_scale);
     if (rc != PA_OK) return rc;
     if (!out) return PA_ERR_INVALID_ARG;
     if (!aligned16(out)) return PA_ERR_MISALIGNED;
     if (num_seqs == 0) return PA_OK;
     DecodeParams p = make_params(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_heads,
-                                 num_kv_heads, max_blocks_per_seq, num_blocks, scale);
+                                 num_kv_heads, max_blocks_per_seq, num_blocks, scale,
+                                 kv_cache_dtype, k_scale, v_scale);
     p.out = out;
     const long long units = (long long)num_seqs * num_kv_heads * p.head_chunks;
     if (units > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
-    const int nw = PA_V1_WAVES ? PA_V1_WAVES : pick_waves(units, max_blocks_per_seq, head_size);
-    return launch_decode<false>(p, head_size, nw, (int)units, as_stream(stream));
+    const bool fp8 = kv_cache_dtype == PA_KV_FP8_E4M3;
+    const int nw = PA_V1_WAVES ? PA_V1_WAVES
+                               : pick_waves(units, max_blocks_per_seq, head_size, fp8 ? 1 : 2);
+    return launch_decode<false>(p, head_size, fp8, nw, (int)units, as_stream(stream));
 }
 
 extern "C" int pa_v2_max_partitions(int max_seq_len, int partition_size) {
@@ -760,10 +984,11 @@ extern "C" int pa_decode_v2(float* tmp_out, float* exp_sums, float* max_logits, 
                             const void* k_cache, const void* v_cache, const int32_t* block_tables,
                             const int32_t* seq_lens, int num_seqs, int num_heads, int num_kv_heads,
                             int head_size, int block_size, int max_blocks_per_seq, int num_blocks,
-                            int max_num_partitions, int partition_size, float scale, void* stream) {
+                            int max_num_partitions, int partition_size, float scale,
+                            int kv_cache_dtype, float k_scale, float v_scale, void* stream) {
     int rc = check_decode_args(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_heads,
                                num_kv_heads, head_size, block_size, max_blocks_per_seq, num_blocks,
-                               scale);
+                               scale, kv_cache_dtype, k_scale, v_scale);
     if (rc != PA_OK) return rc;
     if (!tmp_out || !exp_sums || !max_logits) return PA_ERR_INVALID_ARG;
     if (max_num_partitions <= 0 || partition_size <= 0 || partition_size % 16 != 0)
@@ -772,7 +997,8 @@ extern "C" int pa_decode_v2(float* tmp_out, float* exp_sums, float* max_logits, 
         return PA_ERR_MISALIGNED;
     if (num_seqs == 0) return PA_OK;
     DecodeParams p = make_params(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_heads,
-                                 num_kv_heads, max_blocks_per_seq, num_blocks, scale);
+                                 num_kv_heads, max_blocks_per_seq, num_blocks, scale,
+                                 kv_cache_dtype, k_scale, v_scale);
     p.out = tmp_out;
     p.exp_sums = exp_sums;
     p.max_logits = max_logits;
@@ -781,6 +1007,8 @@ extern "C" int pa_decode_v2(float* tmp_out, float* exp_sums, float* max_logits, 
     const long long units = (long long)num_seqs * num_kv_heads * p.head_chunks * max_num_partitions;
     if (units > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
     // a sequence has on average about half of max_num_partitions partitions
-    const int nw = PA_V2_WAVES ? PA_V2_WAVES : pick_waves(units / 2, partition_size / 16, head_size);
-    return launch_decode<true>(p, head_size, nw, (int)units, as_stream(stream));
+    const bool fp8 = kv_cache_dtype == PA_KV_FP8_E4M3;
+    const int nw = PA_V2_WAVES ? PA_V2_WAVES
+                               : pick_waves(units / 2, partition_size / 16, head_size, fp8 ? 1 : 2);
+    return launch_decode<true>(p, head_size, fp8, nw, (int)units, as_stream(stream));
 }

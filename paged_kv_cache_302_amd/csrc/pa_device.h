@@ -13,6 +13,8 @@ typedef f16 f16x4 __attribute__((ext_vector_type(4)));
 typedef f16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;        // CDNA wavefront width
 constexpr int kBlock = 16;       // tokens per KV block
@@ -91,6 +93,43 @@ __device__ __forceinline__ float dot2(f16x2 a, f16x2 b, float c) {
 
 __device__ __forceinline__ f16x2 pack2(float a, float b) {
     return f16x2{(f16)a, (f16)b};
+}
+
+// ---------------------------------------------------------------------------
+// fp8 KV cache (OCP E4M3: sign, 4 exponent bits with bias 7, 3 mantissa bits,
+// no infinity, S.1111.111 = NaN, largest finite 448)
+// ---------------------------------------------------------------------------
+constexpr int kX8 = 16;          // fp8 elements per 16-byte K chunk
+constexpr float kE4M3Max = 448.f;
+
+// Two E4M3 codes (bytes 0,1 of w, or 2,3 with HI) -> two fp16, exactly
+// (every E4M3 value is an fp16 value; NaN stays NaN).
+template <bool HI>
+__device__ __forceinline__ f16x2 e4m3x2_to_f16x2(uint32_t w) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI);
+}
+
+// Four codes of a 32-bit word -> four fp16 (byte b -> element b).
+__device__ __forceinline__ f16x4 e4m3x4_to_f16x4(uint32_t w) {
+    const f16x2 lo = e4m3x2_to_f16x2<false>(w), hi = e4m3x2_to_f16x2<true>(w);
+    return f16x4{lo.x, lo.y, hi.x, hi.y};
+}
+
+// The E4M3 code of x: nearest value, ties to even, finite values beyond 448
+// saturated to +-448, NaN -> 0x7F.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+    if (x != x) return 0x7Fu;
+    const float c = fminf(fmaxf(x, -kE4M3Max), kE4M3Max);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false) & 0xFFu;
+}
+
+// Bytes of w at token positions >= n (within the 4 tokens t0..t0+3 the word
+// holds) cleared: masked slots of a partly filled block may hold any bits.
+__device__ __forceinline__ uint32_t keep_tokens(uint32_t w, int t0, int n) {
+    const int k = n - t0;                   // tokens of this word to keep
+    if (k >= 4) return w;
+    if (k <= 0) return 0u;
+    return w & ((1u << (8 * k)) - 1u);
 }
 
 }  // namespace pa

@@ -19,6 +19,19 @@ inline int check_head_block(int head_size, int block_size) {
     return PA_OK;
 }
 
+// kv_cache_dtype: PA_KV_FP16 (scales ignored) or PA_KV_FP8_E4M3 (scales
+// positive and finite)
+inline int check_kv_dtype(int kv_cache_dtype, float k_scale, float v_scale) {
+    if (kv_cache_dtype == PA_KV_FP16) return PA_OK;
+    if (kv_cache_dtype != PA_KV_FP8_E4M3) return PA_ERR_UNSUPPORTED;
+    if (!(k_scale > 0.f) || !(v_scale > 0.f) || !__builtin_isfinite(k_scale) ||
+        !__builtin_isfinite(v_scale))
+        return PA_ERR_INVALID_ARG;
+    return PA_OK;
+}
+
+inline int kv_elem_bytes(int kv_cache_dtype) { return kv_cache_dtype == PA_KV_FP8_E4M3 ? 1 : 2; }
+
 inline int launch_status() {
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;

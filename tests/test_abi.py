@@ -61,7 +61,7 @@ def test_binding_signatures_match_header():
 
 def test_status_strings_and_version():
     lib = pa.load_library()
-    assert lib.pa_abi_version() == 3
+    assert lib.pa_abi_version() == 4
     assert lib.pa_status_str(0) == b"ok"
     for rc in (-1, -2, -3, -4, -5):
         assert len(lib.pa_status_str(rc)) > 5
@@ -82,19 +82,24 @@ M = ctypes.c_void_p(0x10004)      # misaligned
 
 def v1(**kw):
     args = dict(out=A, q=A, k=A, v=A, bt=A, sl=A, S=2, H=8, KVH=2, D=128, B=16, MB=4, NB=10,
-                scale=0.1)
+                scale=0.1, dt=0, ks=1.0, vs=1.0)
     args.update(kw)
     return pa.load_library().pa_decode_v1(args["out"], args["q"], args["k"], args["v"], args["bt"],
                                           args["sl"], args["S"], args["H"], args["KVH"], args["D"],
-                                          args["B"], args["MB"], args["NB"], args["scale"], None)
+                                          args["B"], args["MB"], args["NB"], args["scale"],
+                                          args["dt"], args["ks"], args["vs"], None)
 
 
 @pytest.mark.parametrize("kw,rc", [
     (dict(D=96), -2), (dict(B=32), -2), (dict(H=7), -1), (dict(KVH=0), -1), (dict(NB=0), -1),
     (dict(MB=0), -1), (dict(scale=0.0), -1), (dict(scale=float("inf")), -1), (dict(q=None), -1),
     (dict(out=None), -1), (dict(k=M), -3), (dict(out=M), -3), (dict(S=-1), -1),
+    (dict(dt=2), -2), (dict(dt=1, ks=0.0), -1), (dict(dt=1, vs=float("nan")), -1),
+    (dict(dt=1, ks=float("inf")), -1), (dict(dt=0, ks=0.0), 0),
 ])
 def test_decode_v1_rejects_bad_arguments(kw, rc):
+    if rc == 0:                     # fp16 pools ignore the scales: valid, but S = 0 keeps it host-only
+        kw = dict(kw, S=0)
     assert v1(**kw) == rc
 
 
@@ -105,8 +110,12 @@ def test_empty_batch_is_a_no_op():
 def test_v2_and_reduce_reject_bad_partitioning():
     lib = pa.load_library()
     # partition size not a multiple of 16
-    assert lib.pa_decode_v2(A, A, A, A, A, A, A, A, 2, 8, 2, 128, 16, 4, 10, 2, 100, 0.1, None) == -1
-    assert lib.pa_decode_v2(A, A, A, A, A, A, A, A, 2, 8, 2, 128, 16, 4, 10, 0, 512, 0.1, None) == -1
+    assert lib.pa_decode_v2(A, A, A, A, A, A, A, A, 2, 8, 2, 128, 16, 4, 10, 2, 100, 0.1, 0, 1.0, 1.0,
+                            None) == -1
+    assert lib.pa_decode_v2(A, A, A, A, A, A, A, A, 2, 8, 2, 128, 16, 4, 10, 0, 512, 0.1, 0, 1.0, 1.0,
+                            None) == -1
+    assert lib.pa_decode_v2(A, A, A, A, A, A, A, A, 2, 8, 2, 128, 16, 4, 10, 2, 512, 0.1, 1, -1.0, 1.0,
+                            None) == -1
     assert lib.pa_reduce(A, A, A, A, A, 2, 8, 128, 0, 512, None) == -1
     assert lib.pa_reduce(A, A, A, A, A, 2, 8, 100, 4, 512, None) == -2
     assert lib.pa_reduce(A, M, A, A, A, 2, 8, 128, 4, 512, None) == -3
@@ -114,15 +123,20 @@ def test_v2_and_reduce_reject_bad_partitioning():
 
 def test_cache_write_rejects_bad_arguments():
     lib = pa.load_library()
-    assert lib.reshape_and_cache(A, A, A, A, A, 4, 2, 128, 16, 8, 100, 256, None) == -1  # stride < row
-    assert lib.reshape_and_cache(A, A, A, A, A, 4, 2, 128, 16, 8, 260, 260, None) == -3  # stride % 8
-    assert lib.reshape_and_cache(A, A, A, A, A, 4, 2, 64, 8, 8, 128, 128, None) == -2
-    assert lib.reshape_and_cache(A, A, A, A, A, 0, 2, 128, 16, 8, 256, 256, None) == 0   # no tokens
-    assert lib.pa_gather_kv(A, A, A, A, A, A, None, 2, 2, 128, 16, 4, 8, None) == -1
-    assert lib.copy_blocks(A, A, A, 3, 2, 96, 16, 8, None) == -2
-    assert lib.copy_blocks(A, A, None, 3, 2, 128, 16, 8, None) == -1
-    assert lib.copy_blocks(M, A, A, 3, 2, 128, 16, 8, None) == -3
-    assert lib.copy_blocks(A, A, A, 0, 2, 128, 16, 8, None) == 0    # no pairs
+    rc = lambda *a: lib.reshape_and_cache(*a[:12], a[12] if len(a) > 12 else 0, 1.0, 1.0, None)
+    assert rc(A, A, A, A, A, 4, 2, 128, 16, 8, 100, 256) == -1  # stride < row
+    assert rc(A, A, A, A, A, 4, 2, 128, 16, 8, 260, 260) == -3  # stride % 8
+    assert rc(A, A, A, A, A, 4, 2, 64, 8, 8, 128, 128) == -2
+    assert rc(A, A, A, A, A, 0, 2, 128, 16, 8, 256, 256) == 0   # no tokens
+    assert rc(A, A, A, A, A, 4, 2, 128, 16, 8, 256, 256, 5) == -2   # unknown dtype
+    assert lib.reshape_and_cache(A, A, A, A, A, 4, 2, 128, 16, 8, 256, 256, 1, 0.0, 1.0, None) == -1
+    assert lib.pa_gather_kv(A, A, A, A, A, A, None, 2, 2, 128, 16, 4, 8, 0, None) == -1
+    assert lib.pa_gather_kv(A, A, A, A, A, A, A, 2, 2, 128, 16, 4, 8, 3, None) == -2
+    assert lib.copy_blocks(A, A, A, 3, 2, 96, 16, 8, 0, None) == -2
+    assert lib.copy_blocks(A, A, None, 3, 2, 128, 16, 8, 0, None) == -1
+    assert lib.copy_blocks(M, A, A, 3, 2, 128, 16, 8, 0, None) == -3
+    assert lib.copy_blocks(A, A, A, 0, 2, 128, 16, 8, 1, None) == 0    # no pairs
+    assert lib.copy_blocks(A, A, A, 3, 2, 128, 16, 8, 7, None) == -2
 
 
 def test_block_manager_rejects_bad_arguments():
