@@ -45,6 +45,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long_gqa")
     ap.add_argument("--kernel", default="v2", choices=["v1", "v2"])
+    ap.add_argument("--kv-dtype", default="fp16", choices=["fp16", "fp8"],
+                    help="element type of the K/V pools; fp8 = OCP E4M3 codes with per-pool "
+                         "scales (k_scale = v_scale = 2**-6), written from the same fp16 values "
+                         "by the library's own cache write before timing")
     ap.add_argument("--seed", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -82,7 +86,7 @@ def blas_threads() -> int:
 
 
 def cpu_baseline(k_cache, v_cache, block_tables, seq_lens, q, scale, num_kv_heads, block_size,
-                 gpu_out, budget_s: float):
+                 gpu_out, budget_s: float, fp8_scales=None):
     """The oracle (fp64 NumPy) on a bounded sample of the same workload:
     whole (sequence, KV head) units in order until the time budget is spent.
     The pools must already hold the step's cache writes.  Returns its
@@ -100,6 +104,9 @@ def cpu_baseline(k_cache, v_cache, block_tables, seq_lens, q, scale, num_kv_head
         for kvh in range(num_kv_heads):
             t0 = time.perf_counter()
             K, V = oracle.gather_sequence_fast(k_cache, v_cache, block_tables[s], L, kvh, block_size)
+            if fp8_scales is not None:      # the oracle's own quantization of the fp16 values
+                K = oracle.fp8.dequantize(oracle.fp8.quantize(K, fp8_scales[0]), fp8_scales[0])
+                V = oracle.fp8.dequantize(oracle.fp8.quantize(V, fp8_scales[1]), fp8_scales[1])
             ref = oracle.attention(q[s, kvh * G:(kvh + 1) * G], K, V, scale)
             spent += time.perf_counter() - t0
             done_bytes += L * 2 * D * 2
@@ -152,6 +159,32 @@ def read_traffic(kname: str, workload: str):
         return int(float(fields["traffic_bytes_per_launch"]))
     except (KeyError, ValueError):
         return None
+
+
+def to_fp8_pools(pa, inp, kc16, vc16, bt, sl, k_scale, v_scale, dev):
+    """fp8 pools holding the E4M3 codes of the fp16 pools' live tokens, made by
+    the library itself: gather every sequence's K/V in logical order, then
+    write them through reshape_and_cache into fp8 pools at the same slots."""
+    import torch
+    w = inp.workload
+    B, KVH, D = w.block_size, w.num_kv_heads, w.head_size
+    lens = inp.seq_lens.astype(np.int64)
+    cu = np.concatenate([[0], np.cumsum(lens)[:-1]])
+    total = int(lens.sum())
+    slots = np.empty(total, np.int64)
+    for s in range(w.num_seqs):
+        t = np.arange(lens[s])
+        slots[cu[s]:cu[s] + lens[s]] = inp.block_tables[s, t // B].astype(np.int64) * B + t % B
+    ko = torch.empty((total, KVH, D), dtype=torch.float16, device=dev)
+    vo = torch.empty_like(ko)
+    pa.pa_gather_kv(ko, vo, kc16, vc16, bt, sl, torch.from_numpy(cu).to(dev))
+    NB = inp.num_blocks
+    kc8 = torch.zeros((NB, KVH, D // 16, B, 16), dtype=torch.uint8, device=dev)
+    vc8 = torch.zeros((NB, KVH, D, B), dtype=torch.uint8, device=dev)
+    pa.reshape_and_cache(ko, vo, kc8, vc8, torch.from_numpy(slots).to(dev), k_scale, v_scale)
+    torch.cuda.synchronize()
+    del ko, vo
+    return kc8, vc8
 
 
 def timed_steps(args, step, n_events):
@@ -348,6 +381,10 @@ def main():
 
     q, kc, vc = t(inp.q), t(inp.k_cache), t(inp.v_cache)
     bt, sl = t(inp.block_tables), t(inp.seq_lens)
+    fp8 = args.kv_dtype == "fp8"
+    ks = vs = 2.0 ** -6
+    if fp8:
+        kc, vc = to_fp8_pools(pa, inp, kc, vc, bt, sl, ks, vs, dev)
     # the step's new token per sequence, written at logical position L_s - 1
     slots = wl.new_token_slots(inp)
     key, val, slot_d = t(inp.key), t(inp.value), t(slots)
@@ -361,16 +398,16 @@ def main():
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        pa.reshape_and_cache(key, val, kc, vc, slot_d)
+        pa.reshape_and_cache(key, val, kc, vc, slot_d, ks, vs)
         if ev is not None:
             ev[1].record(stream)
         if args.kernel == "v2":
-            pa.pa_decode_v2(tmp, es, ml, q, kc, vc, bt, sl, inp.scale, PS)
+            pa.pa_decode_v2(tmp, es, ml, q, kc, vc, bt, sl, inp.scale, PS, ks, vs)
             if ev is not None:
                 ev[2].record(stream)
             pa.pa_reduce(out, tmp, es, ml, sl, PS)
         else:
-            pa.pa_decode_v1(out, q, kc, vc, bt, sl, inp.scale)
+            pa.pa_decode_v1(out, q, kc, vc, bt, sl, inp.scale, ks, vs)
             if ev is not None:
                 ev[2].record(stream)
         if ev is not None:
@@ -413,12 +450,13 @@ def main():
     reduce_ms = [e[2].elapsed_time(e[3]) for e in evs]
     dec_avg_s = float(np.mean(decode_ms)) / 1e3
 
-    kv_bytes = inp.kv_bytes
-    unique_bytes = inp.unique_kv_bytes if w.group_size else kv_bytes
+    esz = 1 if fp8 else 2
+    kv_bytes = inp.kv_bytes * esz // 2
+    unique_bytes = (inp.unique_kv_bytes if w.group_size else inp.kv_bytes) * esz // 2
     value = kv_bytes / (ms_per_step / 1e3) / 1e9
     achieved = unique_bytes / dec_avg_s / 1e9
     kname = "pa_decode_v2" if args.kernel == "v2" else "pa_decode_v1"
-    traffic = read_traffic(kname, args.workload)
+    traffic = read_traffic(kname, args.workload + ("_fp8" if fp8 else ""))
 
     res = {
         "metric": METRIC,
@@ -431,10 +469,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": "f8e4m3 K/V, f16 q, f32 accumulate" if fp8 else "f16",
         "data": "synthetic",
         "config": {
-            "workload": args.workload,
+            "workload": args.workload + ("_fp8" if fp8 else ""),
+            "kv_cache_dtype": args.kv_dtype,
+            **({"k_scale": ks, "v_scale": vs} if fp8 else {}),
             "kernel": f"reshape_and_cache + {kname}" + (" + pa_reduce" if args.kernel == "v2" else ""),
             "num_seqs": S, "num_heads": H, "num_kv_heads": KVH, "head_size": D,
             "block_size": w.block_size, "partition_size": PS if args.kernel == "v2" else None,
@@ -445,6 +485,7 @@ def main():
             "unique_kv_bytes_per_step": unique_bytes,
             "num_blocks": inp.num_blocks, "seed": args.seed,
         },
+        "kv_tokens_per_s": round(float(inp.seq_lens.astype(np.int64).sum()) * KVH / (ms_per_step / 1e3), 1),
         "us_per_step": round(ms_per_step * 1e3, 2),
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "kernels_us": {
@@ -475,7 +516,8 @@ def main():
                                  w.block_size, inplace=True)
         res["cpu_baseline"] = cpu_baseline(inp.k_cache, inp.v_cache, inp.block_tables,
                                            inp.seq_lens, inp.q, inp.scale, KVH, w.block_size,
-                                           gpu_out, args.cpu_seconds)
+                                           gpu_out, args.cpu_seconds,
+                                           fp8_scales=(ks, vs) if fp8 else None)
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)
