@@ -16,6 +16,7 @@ from .paged_attention import (  # noqa: F401
     num_partitions,
     online_block_attention,
     paged_decode,
+    paged_prefill,
     partition_partials,
     poison_unused,
     reshape_and_cache,

@@ -167,6 +167,38 @@ def paged_decode(q, k_cache, v_cache, block_tables, seq_lens, scale: float,
     return out
 
 
+def paged_prefill(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, scale: float,
+                  block_size: int) -> np.ndarray:
+    """Multi-token queries with a causal mask -> out [total_q, H, D] float64.
+
+    Sequence s holds L = seq_lens[s] tokens; its last n = query_start_loc[s+1]
+    - query_start_loc[s] tokens have queries (rows query_start_loc[s] + j).
+    Query j sits at position p = L - n + j and attends keys 0..p: the plain
+    definition over the gathered K/V prefix (prefill writes the prompt's K/V
+    and attends causally -- blog page §2; memory page, 自回归推理).  n = 1 is
+    a decode step; n = L a full prefill.
+    """
+    T, H, D = q.shape
+    KVH = k_cache.shape[1]
+    out = np.full((T, H, D), np.nan, dtype=F64)
+    for s in range(len(seq_lens)):
+        L = int(seq_lens[s])
+        q0, q1 = int(query_start_loc[s]), int(query_start_loc[s + 1])
+        n = q1 - q0
+        for kvh in range(KVH):
+            K, V = gather_sequence_fast(k_cache, v_cache, block_tables[s], L, kvh, block_size)
+            hs = [h for h in range(H) if kv_head_of(h, H, KVH) == kvh]
+            for j in range(n):
+                m = visible_keys(L - n + j)
+                out[q0 + j, hs] = attention(q[q0 + j, hs], K[:m], V[:m], scale)
+    return out
+
+
+def visible_keys(p: int) -> int:
+    """Keys a query at position p attends to under the causal mask: 0..p."""
+    return p + 1
+
+
 # ---------------------------------------------------------------------------
 # Partitioned variant and its merge (kernel page §3.3: PARTITION_SIZE)
 # ---------------------------------------------------------------------------
