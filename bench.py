@@ -134,7 +134,7 @@ def cpu_baseline(k_cache, v_cache, block_tables, seq_lens, q, scale, num_kv_head
 def kernel_source_hash() -> str:
     import hashlib
     h = hashlib.sha256()
-    for name in ("pa_decode.hip", "pa_device.h"):
+    for name in ("pa_decode.hip", "pa_paths.h", "pa_device.h"):
         with open(os.path.join(ROOT, "paged_kv_cache_302_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]

@@ -10,7 +10,7 @@
  *   - "KV Cache与PagedAttention内存管理" (aiqz.cc), section 自回归推理 for
  *     softmax(QK^T/sqrt(d_k))V and section 分页机制 for the page map;
  *   - "vLLM 的 PagedAttention：KV cache 为什么要分页" (bhhxx.wiki), §4.3 for
- *     the per-block kernel loop.
+ *     the per-block kernel loop, §2 for prefill and decode.
  *
  * Conventions shared by every call
  *   - Every pointer argument is a DEVICE pointer into memory the caller owns
@@ -167,6 +167,32 @@ PA_API int pa_reduce(float* out, const float* tmp_out, const float* exp_sums,
               const float* max_logits, const int32_t* seq_lens,
               int num_seqs, int num_heads, int head_size,
               int max_num_partitions, int partition_size, void* stream);
+
+/*
+ * pa_prefill -- multi-token queries over the paged cache with a causal mask
+ * (prefill, chunked prefill, speculative verify: the phases around decode).
+ *
+ * Sequence s holds L = seq_lens[s] cached tokens (its K/V already written,
+ * the new tokens' included); its last n = query_start_loc[s+1] -
+ * query_start_loc[s] tokens have queries, rows query_start_loc[s] + j of q
+ * and out.  Query j sits at position p = L - n + j and attends keys 0..p:
+ *     out[r,h,:] = sum_{t<=p} softmax_t(scale * q[r,h,:] . K_t) V_t
+ * with the same head mapping, dtypes and fp8 scaling as pa_decode_v1.  n = 1
+ * is a decode step, n = L a full prefill.
+ *
+ *   out             [total_q, num_heads, head_size] fp32, written
+ *   q               [total_q, num_heads, head_size] fp16
+ *   query_start_loc [num_seqs + 1] int32, non-decreasing, starting at 0
+ *   max_query_len   >= every n (sizes the grid; 0 enqueues nothing)
+ *   other arguments as in pa_decode_v1.  n > L, a block id outside the pool
+ *   or L beyond the table row gives NaN rows for that sequence.
+ */
+PA_API int pa_prefill(float* out, const void* q, const void* k_cache, const void* v_cache,
+               const int32_t* block_tables, const int32_t* seq_lens,
+               const int32_t* query_start_loc, int num_seqs, int num_heads,
+               int num_kv_heads, int head_size, int block_size, int max_blocks_per_seq,
+               int num_blocks, int max_query_len, float scale, int kv_cache_dtype,
+               float k_scale, float v_scale, void* stream);
 
 /*
  * reshape_and_cache -- scatter new tokens' K and V into the pools through

@@ -30,6 +30,7 @@ _SIGNATURES = {
     "pa_v2_max_partitions": ([_c_int, _c_int], _c_int),
     "pa_decode_v2": ([_ptr] * 8 + [_c_int] * 9 + [_c_float, _c_int, _c_float, _c_float, _ptr], _c_int),
     "pa_reduce": ([_ptr] * 5 + [_c_int] * 5 + [_ptr], _c_int),
+    "pa_prefill": ([_ptr] * 7 + [_c_int] * 8 + [_c_float, _c_int, _c_float, _c_float, _ptr], _c_int),
     "reshape_and_cache": ([_ptr] * 5 + [_c_int] * 5 + [_c_i64, _c_i64, _c_int, _c_float, _c_float,
                                                          _ptr], _c_int),
     "pa_gather_kv": ([_ptr] * 7 + [_c_int] * 7 + [_ptr], _c_int),
@@ -192,6 +193,33 @@ def pa_decode_v2(tmp_out, exp_sums, max_logits, q, k_cache, v_cache, block_table
                           P, int(partition_size), float(scale), kv_dtype_of(k_cache),
                           float(k_scale), float(v_scale), _stream(q, stream))
     _check(rc, "pa_decode_v2")
+
+
+def pa_prefill(out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc,
+               max_query_len: int, scale: float, k_scale: float = 1.0, v_scale: float = 1.0,
+               stream=None):
+    """out[T,H,D] fp32 <- causal attention of the last n_s tokens of every
+    sequence (rows query_start_loc[s] ..) over its paged K/V."""
+    NB, KVH, D, B = _cache_dims(k_cache, v_cache)
+    dev = k_cache.device
+    _want(q, "q", torch.float16, 3, dev)
+    _want(out, "out", torch.float32, 3, dev)
+    _want(block_tables, "block_tables", torch.int32, 2, dev)
+    _want(seq_lens, "seq_lens", torch.int32, 1, dev)
+    _want(query_start_loc, "query_start_loc", torch.int32, 1, dev)
+    T, H, Dq = q.shape
+    S = seq_lens.shape[0]
+    if Dq != D or tuple(out.shape) != (T, H, D):
+        raise ValueError("q and out must be [total_q, num_heads, head_size] of the cache's head_size")
+    if block_tables.shape[0] != S or query_start_loc.shape[0] != S + 1:
+        raise ValueError("block_tables [S, ...] and query_start_loc [S + 1] must match seq_lens [S]")
+    lib = load_library()
+    rc = lib.pa_prefill(_p(out), _p(q), _p(k_cache), _p(v_cache), _p(block_tables), _p(seq_lens),
+                        _p(query_start_loc), S, H, KVH, D, B, block_tables.shape[1], NB,
+                        int(max_query_len), float(scale), kv_dtype_of(k_cache), float(k_scale),
+                        float(v_scale), _stream(q, stream))
+    _check(rc, "pa_prefill")
+    return out
 
 
 def pa_reduce(out, tmp_out, exp_sums, max_logits, seq_lens, partition_size: int, stream=None):

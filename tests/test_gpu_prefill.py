@@ -1,0 +1,88 @@
+"""GPU parity of pa_prefill (multi-token queries with a causal mask over the
+paged cache) against the oracle: full prefills, chunks at the end of longer
+contexts and single queries, for every query-tile shape (G = 1, 4, 7, 16,
+24; head sizes 64 and 128), fp16 and fp8 pools, NaN in every unused slot."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import fp8
+import paged_kv_cache_302_amd as pa
+import workloads as wl
+from tests._util import assert_parity, device, to_dev
+from tests.test_gpu_fp8 import k16_to_logical, logical_to_k8
+
+pytestmark = pytest.mark.gpu
+
+# (label, H, KVH, D, lens, query counts)
+CASES = [
+    ("g4_d128", 16, 4, 128, [37, 200, 16, 1], [37, 50, 16, 1]),
+    ("g7_d128", 14, 2, 128, [90, 300], [33, 7]),
+    ("mha_d64", 4, 4, 64, [130, 17, 64], [130, 9, 1]),
+    ("g16_d64", 32, 2, 64, [70, 5], [20, 5]),
+    ("g24_d128", 24, 1, 128, [60, 33], [3, 33]),
+]
+
+
+def make(label, H, KVH, D, lens, nq, seed):
+    w = wl.small_workload(label, num_seqs=len(lens), num_heads=H, num_kv_heads=KVH,
+                          head_size=D, seq_len_lo=max(lens), seq_len_hi=max(lens))
+    inp = wl.make_inputs(w, seed)
+    lens = np.array(lens, np.int32)
+    oracle.poison_unused(inp.k_cache, inp.v_cache, inp.block_tables, lens, 16)
+    qsl = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    q = np.random.default_rng(seed + 7).standard_normal((int(qsl[-1]), H, D)).astype(np.float16)
+    return inp, lens, qsl, q
+
+
+def run(q, kc, vc, bt, lens, qsl, scale, max_q, ks=1.0, vs=1.0):
+    out = torch.empty(q.shape, dtype=torch.float32, device=device())
+    pa.pa_prefill(out, to_dev(q), kc, vc, to_dev(bt), to_dev(lens), to_dev(qsl), max_q, scale,
+                  ks, vs)
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_prefill_matches_oracle(case):
+    inp, lens, qsl, q = make(*case, seed=41)
+    ref = oracle.paged_prefill(q, inp.k_cache, inp.v_cache, inp.block_tables, lens, qsl,
+                               inp.scale, 16)
+    out = run(q, to_dev(inp.k_cache), to_dev(inp.v_cache), inp.block_tables, lens, qsl,
+              inp.scale, int(max(case[5])) + 5)         # extra query tiles exit at once
+    assert_parity(out, ref, case[0])
+
+
+@pytest.mark.parametrize("case", [CASES[0], CASES[2]], ids=["g4", "mha"])
+def test_prefill_fp8_matches_oracle(case):
+    inp, lens, qsl, q = make(*case, seed=42)
+    ks, vs = 0.03, 0.02
+    k8 = logical_to_k8(fp8.quantize(k16_to_logical(inp.k_cache), ks))
+    v8 = fp8.quantize(inp.v_cache, vs)
+    dk, dv = fp8.dequantize_pools(k8, v8, ks, vs)
+    ref = oracle.paged_prefill(q, dk, dv, inp.block_tables, lens, qsl, inp.scale, 16)
+    out = run(q, to_dev(k8), to_dev(v8), inp.block_tables, lens, qsl, inp.scale,
+              int(max(case[5])), ks, vs)
+    assert_parity(out, ref, case[0] + " fp8")
+
+
+def test_single_queries_agree_with_decode():
+    inp, lens, qsl, q = make("one", 16, 4, 128, [300, 45, 1000], [1, 1, 1], seed=43)
+    kc, vc = to_dev(inp.k_cache), to_dev(inp.v_cache)
+    out = run(q, kc, vc, inp.block_tables, lens, qsl, inp.scale, 1)
+    dec = pa.paged_attention_v1(to_dev(q), kc, vc, to_dev(inp.block_tables), to_dev(lens),
+                                inp.scale).cpu().numpy()
+    ref = oracle.paged_decode(q, inp.k_cache, inp.v_cache, inp.block_tables, lens, inp.scale, 16)
+    assert_parity(out, ref, "prefill n=1")
+    assert_parity(dec, ref, "decode")
+
+
+def test_more_queries_than_tokens_gives_nan_rows():
+    inp, lens, qsl, q = make("bad", 8, 2, 64, [10, 30], [4, 12], seed=44)
+    lens = np.array([3, 30], np.int32)              # sequence 0: 4 queries, 3 tokens
+    out = run(q, to_dev(inp.k_cache), to_dev(inp.v_cache), inp.block_tables, lens, qsl,
+              inp.scale, 12)
+    assert np.isnan(out[:4]).all()
+    ref = oracle.paged_prefill(q[4:], inp.k_cache, inp.v_cache, inp.block_tables[1:], lens[1:],
+                               qsl[1:] - qsl[1], inp.scale, 16)
+    assert_parity(out[4:], ref, "other sequence unaffected")
