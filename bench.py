@@ -353,6 +353,134 @@ def main_fork(args):
     print(json.dumps(res), flush=True)
 
 
+def main_prefill(args, w):
+    """Multi-token queries: the step writes the last query_len tokens' K/V of
+    every sequence (reshape_and_cache) and runs their causal attention
+    (pa_prefill).  Metric: attention TFLOP/s (4 H D flops per query-key pair
+    inside the causal mask); MFMA-bound."""
+    import torch
+
+    import paged_kv_cache_302_amd as pa
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    inp = wl.make_inputs(w, args.seed)
+    qh, keyh, valh, slots, qsl = wl.make_chunk(w, inp, args.seed)
+    gen_s = time.time() - t0
+    S, H, D, KVH, B, n = w.num_seqs, w.num_heads, w.head_size, w.num_kv_heads, w.block_size, w.query_len
+
+    def t(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    kc, vc = t(inp.k_cache), t(inp.v_cache)
+    bt, sl = t(inp.block_tables), t(inp.seq_lens)
+    fp8 = args.kv_dtype == "fp8"
+    ks = vs = 2.0 ** -6
+    if fp8:
+        kc, vc = to_fp8_pools(pa, inp, kc, vc, bt, sl, ks, vs, dev)
+    q, key, val, slot_d, qsl_d = t(qh), t(keyh), t(valh), t(slots), t(qsl)
+    out = torch.empty((S * n, H, D), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        pa.reshape_and_cache(key, val, kc, vc, slot_d, ks, vs)
+        if ev is not None:
+            ev[1].record(stream)
+        pa.pa_prefill(out, q, kc, vc, bt, sl, qsl_d, n, inp.scale, ks, vs)
+        if ev is not None:
+            ev[2].record(stream)
+
+    ms_per_step, evs, wall = timed_steps(args, step, 3)
+    pf_s = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) / 1e3
+    # query-key pairs inside the causal mask: sum over queries of (position + 1)
+    pairs = sum(int(n * (int(L) - n) + n * (n + 1) // 2) for L in inp.seq_lens)
+    flops = 4.0 * H * D * pairs
+    kv_bytes = int(inp.seq_lens.astype(np.int64).sum()) * KVH * D * 2 * (1 if fp8 else 2)
+    value = flops / (ms_per_step / 1e3) / 1e12
+    achieved = flops / pf_s / 1e12
+    peak = 2500.0
+    res = {
+        "metric": "paged prefill attention: causal TFLOP/s",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 MFMA, f32 accumulate" + (" (f8e4m3 K/V)" if fp8 else ""),
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload + ("_fp8" if fp8 else ""),
+            "kernel": "reshape_and_cache (query_len tokens) + pa_prefill",
+            "num_seqs": S, "num_heads": H, "num_kv_heads": KVH, "head_size": D,
+            "query_len": n, "seq_lens": [int(inp.seq_lens.min()), int(inp.seq_lens.max())],
+            "causal_pairs": pairs, "flops_per_step": flops, "kv_bytes": kv_bytes,
+            "kv_cache_dtype": args.kv_dtype, "seed": args.seed,
+        },
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "kernels_us": {
+            "reshape_and_cache": round(float(np.median([e[0].elapsed_time(e[1]) for e in evs])) * 1e3, 2),
+            "pa_prefill": round(float(np.median([e[1].elapsed_time(e[2]) for e in evs])) * 1e3, 2),
+        },
+        "roofline": {
+            "kernel": "pa_prefill",
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": None,
+            "algorithmic_flops_per_launch": flops,
+            "avg_launch_us": round(pf_s * 1e6, 2),
+            "hbm_floor_us": round(kv_bytes / 8e12 * 1e6, 2),
+        },
+        "timing": ("HIP events per step, 1 GiB read scrub between steps (wall %.4f ms/step incl. scrub)"
+                   % wall) if args.scrub else "wall clock over the timed steps",
+        "input_gen_s": round(gen_s, 2),
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        gpu_out = out.cpu().numpy()
+        oracle.reshape_and_cache(keyh, valh, inp.k_cache, inp.v_cache, slots, B, inplace=True)
+        G = H // KVH
+        done, spent, rows, max_err = 0.0, 0.0, 0, 0.0
+        L = int(inp.seq_lens[0])
+        for kvh in range(KVH):
+            K, V = oracle.gather_sequence_fast(inp.k_cache, inp.v_cache, inp.block_tables[0], L, kvh, B)
+            if fp8:
+                K = oracle.fp8.dequantize(oracle.fp8.quantize(K, ks), ks)
+                V = oracle.fp8.dequantize(oracle.fp8.quantize(V, vs), vs)
+            for j in range(n - 1, -1, -97):           # query rows spread over the chunk
+                p = L - n + j
+                t1 = time.perf_counter()
+                ref = oracle.attention(qh[j, kvh * G:(kvh + 1) * G], K[:p + 1], V[:p + 1], inp.scale)
+                spent += time.perf_counter() - t1
+                done += 4.0 * G * D * (p + 1)
+                rows += 1
+                max_err = max(max_err, float(np.abs(ref - gpu_out[j, kvh * G:(kvh + 1) * G]).max()))
+                if spent >= args.cpu_seconds:
+                    break
+            if spent >= args.cpu_seconds:
+                break
+        res["cpu_baseline"] = {
+            "value": round(done / spent / 1e12, 6), "unit": "TFLOP/s", "cores": blas_threads(),
+            "kind": "oracle",
+            "sample": f"{rows} (query row, KV head) attentions of sequence 0, fp64 NumPy two-pass softmax",
+            "seconds": round(spent, 3), "host_cpus": os.cpu_count(),
+            "affinity_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(),
+            "max_abs_diff_vs_gpu": max_err,
+        }
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -370,6 +498,8 @@ def main():
     if args.workload == "fork":
         return main_fork(args)
     w = wl.WORKLOADS[args.workload]
+    if w.query_len:
+        return main_prefill(args, w)
     t0 = time.time()
     inp = wl.make_inputs(w, args.seed)
     gen_s = time.time() - t0

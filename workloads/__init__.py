@@ -61,6 +61,9 @@ class Workload:
     # the cache-write step (so L_s = prefix_len + tail + 1)
     group_size: int = 0
     prefix_len: int = 0
+    # multi-token queries: the last `query_len` tokens of every sequence have
+    # queries (a prefill chunk / speculative verify); 0 = one decode query
+    query_len: int = 0
     kernels: tuple = ("v1",)
     note: str = ""
 
@@ -105,6 +108,12 @@ WORKLOADS = {
     "shared_prefix": Workload("shared_prefix", 256, 32, 8, 128, 1, 256,
                               group_size=8, prefix_len=1024,
                               kernels=("cache", "v2")),
+    # prefill-side shapes (multi-token queries over the paged cache)
+    "prefill": Workload("prefill", 8, 32, 8, 128, 2048, 2048, query_len=2048,
+                        kernels=("prefill",), note="full causal prefill of 2K-token prompts"),
+    "chunked_prefill": Workload("chunked_prefill", 16, 32, 8, 128, 4096, 8192, query_len=512,
+                                kernels=("prefill",),
+                                note="512-token chunks at the end of 4K-8K contexts"),
 }
 
 
@@ -343,3 +352,25 @@ def make_fork_inputs(w: ForkWorkload, seed: int) -> ForkInputs:
     key = normal((w.num_seqs, KVH, D))
     value = normal((w.num_seqs, KVH, D))
     return ForkInputs(w, seed, pk, pv, q, key, value)
+
+
+def make_chunk(w: Workload, inp: "DecodeInputs", seed: int):
+    """Queries and the new K/V of the last `query_len` tokens of every
+    sequence, with their slots: q [T, H, D], key/value [T, KVH, D] fp16,
+    slots [T] int64, query_start_loc [S + 1] int32 (T = S * query_len).
+    Drawn from their own stream (seed, 1) so the pools stay as make_inputs
+    drew them."""
+    rng = np.random.default_rng([seed, 1])
+    n = w.query_len
+    S, H, KVH, D, B = w.num_seqs, w.num_heads, w.num_kv_heads, w.head_size, w.block_size
+    T = S * n
+    q = (w.sigma * rng.standard_normal((T, H, D))).astype(np.float16)
+    key = (w.sigma * rng.standard_normal((T, KVH, D))).astype(np.float16)
+    value = (w.sigma * rng.standard_normal((T, KVH, D))).astype(np.float16)
+    slots = np.empty(T, np.int64)
+    for s in range(S):
+        L = int(inp.seq_lens[s])
+        t = np.arange(L - n, L)
+        slots[s * n:(s + 1) * n] = inp.block_tables[s, t // B].astype(np.int64) * B + t % B
+    qsl = (np.arange(S + 1) * n).astype(np.int32)
+    return q, key, value, slots, qsl
