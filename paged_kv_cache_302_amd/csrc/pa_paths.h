@@ -109,11 +109,24 @@ struct MfmaPath {
     static constexpr int NT = D / 16;   // 16-wide head-dim tiles of the output
     static constexpr int kHeads = 16;
     static constexpr int kElem = 2;     // bytes per cache element (fp16)
+    static constexpr int kD = D;
 
     struct Tile {
         f16x8 k[KC];   // lane (g,i): K[t=i][d = 32c + 8g .. +7]
         f16x4 v[NT];   // lane (g,i): V[d = 16nt + i][t = 4g .. 4g+3]
     };
+    // MFMA A operands of score step c and PV step nt (fp16 tiles are used as loaded)
+    __device__ __forceinline__ static f16x8 a_k(const Tile& t, int c) { return t.k[c]; }
+    __device__ __forceinline__ static f16x4 a_v(const Tile& t, int nt) { return t.v[nt]; }
+    // V elements of tokens >= nvalid set to 0 (unused slots may hold NaN)
+    __device__ __forceinline__ static void mask_v(Tile& t, int nvalid) {
+        const int g = lane_id() >> 4;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (4 * g + r >= nvalid) t.v[nt][r] = (f16)0.f;
+    }
     struct State {
         f32x4 acc[NT]; // lane (g,i): O^T[d = 16nt + 4g + r][h = i]
         float m;       // running max of raw dot products of head i
@@ -340,6 +353,19 @@ struct MfmaPath8 : MfmaPath<D> {
         u32x4 k[KR];    // lane (g,i): K codes of token i, dims 16(g + 4r) .. +15
         uint32_t v[NT]; // lane (g,i): V codes of dim 16nt + i, tokens 4g .. 4g+3
     };
+    __device__ __forceinline__ static f16x8 a_k(const Tile& t, int c) {
+        const uint32_t w0 = t.k[c >> 1][2 * (c & 1)], w1 = t.k[c >> 1][2 * (c & 1) + 1];
+        const f16x4 a0 = e4m3x4_to_f16x4(w0), a1 = e4m3x4_to_f16x4(w1);
+        return f16x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+    }
+    __device__ __forceinline__ static f16x4 a_v(const Tile& t, int nt) {
+        return e4m3x4_to_f16x4(t.v[nt]);
+    }
+    __device__ __forceinline__ static void mask_v(Tile& t, int nvalid) {
+        const int g = lane_id() >> 4;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) t.v[nt] = keep_tokens(t.v[nt], 4 * g, nvalid);
+    }
     struct QRegs {
         f16x8 q[KC];    // lane (g,i): Q[h = i][d = 16(g + 4(c/2)) + 8(c%2) .. +7]
     };

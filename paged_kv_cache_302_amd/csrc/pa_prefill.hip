@@ -10,12 +10,12 @@
 // token's, are already in the pools (written by reshape_and_cache).  n_s = 1
 // is a decode step; n_s = L_s is a plain prefill.
 //
-// Work unit: one wavefront per (sequence, 16-row query tile, KV head, head
-// chunk).  The 16 columns of the MFMA score tile S^T = K Q^T are (token,
-// head) pairs of one KV group -- 16/G consecutive query tokens times the G
-// heads, or 16 heads of one token when G >= 16 -- so every K/V tile read
-// serves 16 query rows and the MFMA runs full (MHA included: 16 tokens of
-// one head).  The unit walks blocks 0 .. p_last/16 in order with the decode
+// Work unit: one wavefront per (sequence, query tile, KV head, head chunk).
+// The columns of the MFMA score tiles S^T = K Q^T are (token, head) pairs of
+// one KV group -- 16 NG / G consecutive query tokens times the G heads, or
+// NG tokens of 16 heads when G >= 16 -- in NG groups of 16, so every K/V
+// tile read serves 16 NG query rows and the MFMA runs full (MHA included:
+// 16 NG tokens of one head).  The unit walks blocks 0 .. p_last/16 in order with the decode
 // kernels' table windows and paired tiles; each column's causal limit is a
 // lane-local mask (the softmax state of a column lives in its own lanes),
 // and block 0 -- visible to every column -- comes first, so no column's
@@ -24,12 +24,120 @@
 // same blocks.
 #include "pa_paths.h"
 
+#ifndef PA_PREFILL_GROUPS
+#define PA_PREFILL_GROUPS 2   // 16-column groups per wave (query rows per K/V tile read / 16)
+#endif
+
 namespace pa {
 
-template <class Path, int D>
+constexpr int kPrefillGroups = PA_PREFILL_GROUPS;
+
+// --------------------------------------------------------------------------
+// NG groups of 16 columns per wave: every K/V tile read (and, for fp8
+// pools, converted) once feeds NG score tiles and NG PV updates, so a tile
+// serves 16*NG query rows.  Each group keeps its own lane-local softmax state.
+// --------------------------------------------------------------------------
+template <class Base, int NG>
+struct MfmaGroups {
+    static constexpr int D = Base::kD;
+    static constexpr int KC = D / 32;
+    static constexpr int NT = D / 16;
+    static constexpr int kElem = Base::kElem;
+    using Tile = typename Base::Tile;
+
+    struct State {
+        f32x4 acc[NG][NT];   // lane (g,i): O^T[d = 16nt + 4g + r][column 16gr + i]
+        float m[NG];
+        float l[NG];
+    };
+    struct QRegs {
+        typename Base::QRegs q[NG];
+    };
+
+    __device__ static void init(State& st) {
+#pragma unroll
+        for (int gr = 0; gr < NG; ++gr) {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) st.acc[gr][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            st.m[gr] = -INFINITY;
+            st.l[gr] = 0.f;
+        }
+    }
+
+    template <bool NTL>
+    __device__ __forceinline__ static void load(Tile& t, const char* kt, const char* vt, int bytes) {
+        Base::template load<NTL>(t, kt, vt, bytes);
+    }
+
+    // nvalid: tokens of the block inside the sequence; lim[gr]: the last token
+    // offset this lane's column of group gr may see (causal limit)
+    __device__ __forceinline__ static void process(State& st, Tile& t, const QRegs& qr, int nvalid,
+                                                   float sl2, const int (&lim)[NG]) {
+        const int g = lane_id() >> 4;
+        f32x4 s[NG];
+#pragma unroll
+        for (int gr = 0; gr < NG; ++gr) s[gr] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+            const f16x8 a = Base::a_k(t, c);
+#pragma unroll
+            for (int gr = 0; gr < NG; ++gr)
+                s[gr] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qr.q[gr].q[c], s[gr], 0, 0, 0);
+        }
+        if (nvalid < kBlock) Base::mask_v(t, nvalid);
+        f16x4 pv[NG];
+        float corr[NG];
+#pragma unroll
+        for (int gr = 0; gr < NG; ++gr) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (4 * g + r >= nvalid || 4 * g + r > lim[gr]) s[gr][r] = -INFINITY;
+            float bm = fmaxf(fmaxf(s[gr][0], s[gr][1]), fmaxf(s[gr][2], s[gr][3]));
+            bm = col4_max(bm);
+            const float mn = fmaxf(st.m[gr], bm);
+            corr[gr] = exp2_fast((st.m[gr] - mn) * sl2);
+            float pr[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) pr[r] = exp2_fast((s[gr][r] - mn) * sl2);
+            st.l[gr] = st.l[gr] * corr[gr] + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+            st.m[gr] = mn;
+            pv[gr] = f16x4{(f16)pr[0], (f16)pr[1], (f16)pr[2], (f16)pr[3]};
+        }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const f16x4 a = Base::a_v(t, nt);
+#pragma unroll
+            for (int gr = 0; gr < NG; ++gr) {
+                st.acc[gr][nt] *= corr[gr];
+                st.acc[gr][nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, pv[gr], st.acc[gr][nt], 0, 0, 0);
+            }
+        }
+    }
+
+    // Rows of every group to LDS: s_acc[(16gr + i) * D + d] unnormalised,
+    // s_m / s_l [16gr + i] (l summed over the column's four token groups).
+    __device__ static void stage(const State& st, float* s_acc, float* s_m, float* s_l) {
+        const int l = lane_id(), i = l & 15, g = l >> 4;
+#pragma unroll
+        for (int gr = 0; gr < NG; ++gr) {
+            const float ltot = col4_sum(st.l[gr]);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                *reinterpret_cast<f32x4*>(s_acc + (16 * gr + i) * D + 16 * nt + 4 * g) = st.acc[gr][nt];
+            if (g == 0) {
+                s_m[16 * gr + i] = st.m[gr];
+                s_l[16 * gr + i] = ltot;
+            }
+        }
+    }
+};
+
+template <class Path, int NG>
 __global__ __launch_bounds__(64) void pa_prefill_kernel(DecodeParams p,
                                                         const int32_t* __restrict__ qsl,
                                                         int tpu, int q_tiles) {
+    using G2 = MfmaGroups<Path, NG>;
+    constexpr int D = G2::D;
     extern __shared__ float lds[];
     const int kvhc_count = p.num_kv_heads * p.head_chunks;
     const int kvhc = blockIdx.x % kvhc_count;
@@ -48,21 +156,27 @@ __global__ __launch_bounds__(64) void pa_prefill_kernel(DecodeParams p,
     const int nb_seq = (L + kBlock - 1) / kBlock;
     bool bad = nq > L || nb_seq > p.max_blocks_per_seq;
 
-    // this lane's column: token jj of the tile, head hh
+    // this lane's column in group gr: c = 16 gr + i -> token c / gc, head c % gc
     const int i = lane_id() & 15;
-    const int jj = i / gc;
-    const int hh = kvh * p.group + hc * 16 + (i - jj * gc);
-    const bool col_ok = jj < ntok && i < tpu * gc;
-    const int pos = L - nq + j0 + jj;                  // the column's query position
     const int pos_last = L - nq + j0 + ntok - 1;
-
-    typename Path::State st;
-    Path::init(st);
-    typename Path::QRegs qr;
-    Path::load_q_row(qr, p.q + ((size_t)(q0 + j0 + jj) * p.num_heads + hh) * D, col_ok && !bad);
+    int pos[NG];
+    bool col_ok[NG];
+    typename G2::QRegs qr;
+#pragma unroll
+    for (int gr = 0; gr < NG; ++gr) {
+        const int c = 16 * gr + i;
+        const int jj = c / gc;
+        const int hh = kvh * p.group + hc * 16 + (c - jj * gc);
+        col_ok[gr] = jj < ntok;
+        pos[gr] = L - nq + j0 + jj;
+        Path::load_q_row(qr.q[gr], p.q + ((size_t)(q0 + j0 + jj) * p.num_heads + hh) * D,
+                         col_ok[gr] && !bad);
+    }
+    typename G2::State st;
+    G2::init(st);
 
     const int n = bad ? 0 : pos_last / kBlock + 1;      // blocks 0 .. pos_last / 16
-    constexpr int TB = D * kBlock * Path::kElem;
+    constexpr int TB = D * kBlock * G2::kElem;
     const char* kbase = p.k_cache + (size_t)kvh * TB;
     const char* vbase = p.v_cache + (size_t)kvh * TB;
     const size_t blk_stride = (size_t)p.num_kv_heads * TB;
@@ -84,38 +198,42 @@ __global__ __launch_bounds__(64) void pa_prefill_kernel(DecodeParams p,
         auto tile_k = [&](int id) { return kbase + (size_t)id * blk_stride; };
         auto tile_v = [&](int id) { return vbase + (size_t)id * blk_stride; };
         auto valid = [&](int k) { return min(kBlock, L - k * kBlock); };
-        // the last key offset of block k this column sees (padding columns: all)
-        auto lim = [&](int k) { return col_ok ? min(kBlock - 1, pos - k * kBlock) : kBlock - 1; };
+        auto visit = [&](typename G2::Tile& t, int k) {
+            int lim[NG];   // last visible key offset in block k (padding columns: all)
+#pragma unroll
+            for (int gr = 0; gr < NG; ++gr)
+                lim[gr] = col_ok[gr] ? min(kBlock - 1, pos[gr] - k * kBlock) : kBlock - 1;
+            G2::process(st, t, qr, valid(k), sl2, lim);
+        };
         auto live = [&](int j) { return j < n ? TB : 0; };
-        typename Path::Tile ta, tb;
+        typename G2::Tile ta, tb;
         int id = phys(0, 0);
-        Path::template load<false>(ta, tile_k(id), tile_v(id), TB);
+        G2::template load<false>(ta, tile_k(id), tile_v(id), TB);
         int k = 0;
         for (int kw = 0;; kw += 64) {
             const int pend = table_window<1>(row, 0, n, kw + 128);
             const int kend = min(n, kw + 64) & ~1;
             for (; k < kend; k += 2) {
                 id = phys(kw, k + 1);
-                Path::template load<false>(tb, tile_k(id), tile_v(id), TB);
-                Path::process(st, ta, qr, valid(k), sl2, lim(k));
+                G2::template load<false>(tb, tile_k(id), tile_v(id), TB);
+                visit(ta, k);
                 id = phys(kw, k + 2);
-                Path::template load<false>(ta, tile_k(id), tile_v(id), live(k + 2));
-                Path::process(st, tb, qr, valid(k + 1), sl2, lim(k + 1));
+                G2::template load<false>(ta, tile_k(id), tile_v(id), live(k + 2));
+                visit(tb, k + 1);
             }
             if (kw + 64 >= n) break;
             cur = nxt;
             nxt = pend;
         }
-        if (k < n) Path::process(st, ta, qr, valid(k), sl2, lim(k));
+        if (k < n) visit(ta, k);
     }
 
     // rows of the tile through LDS, then whole 16-byte stores per lane (the
-    // G heads of one token are one contiguous run of G*D floats)
-    const float ltot = Path::wave_l(st);
-    float* s_o = lds;                 // [16][D]
-    float* s_m = lds + 16 * D;        // [16]
-    float* s_l = s_m + 16;            // [16]
-    Path::stage(st, ltot, s_o, s_m, s_l, 16);
+    // heads of one token are one contiguous run of gc*D floats)
+    float* s_o = lds;                 // [16 NG][D]
+    float* s_m = lds + 16 * NG * D;   // [16 NG]
+    float* s_l = s_m + 16 * NG;       // [16 NG]
+    G2::stage(st, s_o, s_m, s_l);
     const f32x4* src = reinterpret_cast<const f32x4*>(s_o);
     const int cols = ntok * gc;       // valid columns: 0 .. cols-1
     for (int e = lane_id(); e < cols * (D / 4); e += 64) {
@@ -152,15 +270,16 @@ extern "C" int pa_prefill(float* out, const void* q, const void* k_cache, const 
     p.out = out;
     const int G = num_heads / num_kv_heads;
     p.head_chunks = G > 16 ? (G + 15) / 16 : 1;
-    const int tpu = G >= 16 ? 1 : 16 / G;               // query tokens per tile
+    constexpr int NG = kPrefillGroups;
+    const int tpu = G >= 16 ? NG : (16 * NG) / G;       // query tokens per tile
     const int q_tiles = (max_query_len + tpu - 1) / tpu;
     const long long grid = (long long)num_seqs * q_tiles * num_kv_heads * p.head_chunks;
     if (grid > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
-    const size_t lds = (16 * (size_t)head_size + 32) * sizeof(float);
+    const size_t lds = (16 * NG * (size_t)head_size + 32 * NG) * sizeof(float);
     hipStream_t st = as_stream(stream);
     const bool fp8 = kv_cache_dtype == PA_KV_FP8_E4M3;
 #define PA_PREFILL(PATH, DD)                                                                   \
-    hipLaunchKernelGGL((pa_prefill_kernel<PATH<DD>, DD>), dim3((unsigned)grid), dim3(64), lds, st, \
+    hipLaunchKernelGGL((pa_prefill_kernel<PATH<DD>, NG>), dim3((unsigned)grid), dim3(64), lds, st, \
                        p, query_start_loc, tpu, q_tiles)
     if (head_size == 128) {
         if (fp8) PA_PREFILL(MfmaPath8, 128);
