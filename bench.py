@@ -187,6 +187,30 @@ def to_fp8_pools(pa, inp, kc16, vc16, bt, sl, k_scale, v_scale, dev):
     return kc8, vc8
 
 
+def pct(ms):
+    """p10 and p90 of per-step kernel times (ms) in microseconds."""
+    return [round(float(np.percentile(ms, 10)) * 1e3, 2), round(float(np.percentile(ms, 90)) * 1e3, 2)]
+
+
+def device_copy_gbs(dev, nbytes=1 << 30, reps=5):
+    """Device-to-device copy bandwidth, (read + write bytes) / time, median of
+    `reps` copies of `nbytes`."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    ms = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        b.synchronize()
+        ms.append(a.elapsed_time(b))
+    del src, dst
+    return 2 * nbytes / (float(np.median(ms)) / 1e3) / 1e9
+
+
 def timed_steps(args, step, n_events):
     """Warm-up, then exactly args.steps steps between two synchronisations;
     returns (ms_per_step, per-step event lists, wall ms per step)."""
@@ -579,6 +603,7 @@ def main():
     decode_ms = [e[1].elapsed_time(e[2]) for e in evs]
     reduce_ms = [e[2].elapsed_time(e[3]) for e in evs]
     dec_avg_s = float(np.mean(decode_ms)) / 1e3
+    copy_gbs = device_copy_gbs(dev)
 
     esz = 1 if fp8 else 2
     kv_bytes = inp.kv_bytes * esz // 2
@@ -623,6 +648,14 @@ def main():
             kname: round(float(np.median(decode_ms)) * 1e3, 2),
             **({"pa_reduce": round(float(np.median(reduce_ms)) * 1e3, 2)} if args.kernel == "v2" else {}),
         },
+        "kernels_us_p10_p90": {
+            "reshape_and_cache": pct(cache_ms),
+            kname: pct(decode_ms),
+            **({"pa_reduce": pct(reduce_ms)} if args.kernel == "v2" else {}),
+        },
+        # second denominator: a measured device-to-device copy (read + write bytes)
+        "device_copy_gbs": round(copy_gbs, 1),
+        "pct_of_device_copy": round(100 * achieved / copy_gbs, 2),
         "roofline": {
             "kernel": kname,
             "bound": "hbm",

@@ -3,14 +3,12 @@
 // slots through slot_mapping, the read path gathers them back through the
 // block table).
 //
-// reshape_and_cache: one thread per (token, KV head, 8-element chunk of the
-// head dims).  The chunk is one 16-byte load of key; in the x-packed K pool it
-// is one 16-byte store (k_cache[b, h, c, o, 0..7]).  V is stored transposed
-// (v_cache[b, h, d, o]): the same 16-byte load of value becomes eight 2-byte
-// stores 32 bytes apart.  A pure copy, so bit-exact.  Into an fp8 pool each
-// element becomes its E4M3 code of x / scale (nearest, ties to even,
-// saturated at +-448, NaN -> 0x7F), the division in fp32: the K chunk is an
-// 8-byte store (half of a 16-element x chunk), V eight 1-byte stores.
+// reshape_and_cache: token i's K and V rows for every KV head go to flat
+// slot slot_mapping[i] (block s / 16, offset s % 16), K into the x-packed
+// k_cache[b, h, d / x, o, d % x], V transposed into v_cache[b, h, d, o].  A
+// pure copy, so bit-exact.  Into an fp8 pool each element becomes its E4M3
+// code of x / scale (nearest, ties to even, saturated at +-448, NaN -> 0x7F),
+// the division in fp32.
 //
 // pa_gather_kv: the inverse, for testing the read-side indirection alone.
 // One thread per (sequence, logical block, token slot, KV head, chunk).
@@ -26,59 +24,91 @@
 
 namespace pa {
 
-template <int D>
+// reshape_and_cache: one workgroup per (16 consecutive tokens, KV head).  The
+// 16 key and value rows are read whole (coalesced 16-byte loads) into LDS.  K
+// chunks then go out with 16 consecutive lanes on the 16 tokens of one chunk
+// (in a block filled in order: 256 contiguous bytes), and V with 16
+// consecutive lanes on the 16 tokens of one dimension row (32 contiguous
+// bytes, 16 for fp8), so the transposed V row of a block is written by one
+// store instruction instead of 16 scattered ones.  Every token still goes to
+// its own slot, so any slot mapping is handled.
+template <int D, bool FP8>
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
-    const f16* __restrict__ key, const f16* __restrict__ value, f16* __restrict__ k_cache,
-    f16* __restrict__ v_cache, const int64_t* __restrict__ slot_mapping, int num_tokens,
-    int num_kv_heads, long long num_slots, long long key_stride, long long value_stride) {
-    constexpr int C = D / kX;
-    const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    const long long total = (long long)num_tokens * num_kv_heads * C;
-    if (gid >= total) return;
-    const int c = (int)(gid % C);
-    const int h = (int)((gid / C) % num_kv_heads);
-    const int i = (int)(gid / ((long long)C * num_kv_heads));
-    const long long slot = slot_mapping[i];
-    if (slot < 0 || slot >= num_slots) return;
-    const long long b = slot / kBlock;
-    const int o = (int)(slot % kBlock);
-    const f16x8 kv = *reinterpret_cast<const f16x8*>(key + i * key_stride + h * D + c * kX);
-    const f16x8 vv = *reinterpret_cast<const f16x8*>(value + i * value_stride + h * D + c * kX);
-    const size_t tile = ((size_t)b * num_kv_heads + h) * (size_t)(D * kBlock);
-    *reinterpret_cast<f16x8*>(k_cache + tile + ((size_t)c * kBlock + o) * kX) = kv;
-    f16* vdst = v_cache + tile + (size_t)(c * kX) * kBlock + o;
-#pragma unroll
-    for (int j = 0; j < kX; ++j) vdst[j * kBlock] = vv[j];
-}
-
-template <int D>
-__global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(
-    const f16* __restrict__ key, const f16* __restrict__ value, uint8_t* __restrict__ k_cache,
-    uint8_t* __restrict__ v_cache, const int64_t* __restrict__ slot_mapping, int num_tokens,
+    const f16* __restrict__ key, const f16* __restrict__ value, void* __restrict__ k_cache,
+    void* __restrict__ v_cache, const int64_t* __restrict__ slot_mapping, int num_tokens,
     int num_kv_heads, long long num_slots, long long key_stride, long long value_stride,
     float k_scale, float v_scale) {
-    constexpr int C = D / kX;          // 8-element chunks of a head
-    const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    const long long total = (long long)num_tokens * num_kv_heads * C;
-    if (gid >= total) return;
-    const int c = (int)(gid % C);
-    const int h = (int)((gid / C) % num_kv_heads);
-    const int i = (int)(gid / ((long long)C * num_kv_heads));
-    const long long slot = slot_mapping[i];
-    if (slot < 0 || slot >= num_slots) return;
-    const long long b = slot / kBlock;
-    const int o = (int)(slot % kBlock);
-    const f16x8 kv = *reinterpret_cast<const f16x8*>(key + i * key_stride + h * D + c * kX);
-    const f16x8 vv = *reinterpret_cast<const f16x8*>(value + i * value_stride + h * D + c * kX);
-    u32x2 kc = {0u, 0u};
+    constexpr int R = D + 8;                       // padded LDS row (elements)
+    __shared__ __align__(16) f16 sk[kBlock * R];
+    __shared__ __align__(16) f16 sv[kBlock * R];
+    __shared__ long long sslot[kBlock];
+    const int t = threadIdx.x;
+    const long long i0 = (long long)blockIdx.x * kBlock;
+    const int h = blockIdx.y;
+    const int nt = (int)min((long long)kBlock, (long long)num_tokens - i0);
+    if (t < kBlock) {
+        long long sl = -1;
+        if (t < nt) {
+            sl = slot_mapping[i0 + t];
+            if (sl >= num_slots) sl = -1;
+        }
+        sslot[t] = sl;
+    }
+    constexpr int CH = D / kX;                     // 16-byte chunks per row
+    for (int e = t; e < kBlock * CH; e += 256) {
+        const int o = e / CH, c = e - o * CH;
+        if (o < nt) {
+            const long long i = i0 + o;
+            *reinterpret_cast<f16x8*>(sk + o * R + c * kX) =
+                *reinterpret_cast<const f16x8*>(key + i * key_stride + h * D + c * kX);
+            *reinterpret_cast<f16x8*>(sv + o * R + c * kX) =
+                *reinterpret_cast<const f16x8*>(value + i * value_stride + h * D + c * kX);
+        }
+    }
+    __syncthreads();
+    const size_t tile_elems = (size_t)D * kBlock;
+    if constexpr (!FP8) {
+        f16* kc = static_cast<f16*>(k_cache);
+        f16* vc = static_cast<f16*>(v_cache);
+        for (int e = t; e < kBlock * CH; e += 256) {
+            const int c = e / kBlock, o = e - c * kBlock;
+            const long long sl = sslot[o];
+            if (sl < 0) continue;
+            const size_t tile = ((size_t)(sl / kBlock) * num_kv_heads + h) * tile_elems;
+            *reinterpret_cast<f16x8*>(kc + tile + ((size_t)c * kBlock + (int)(sl % kBlock)) * kX) =
+                *reinterpret_cast<const f16x8*>(sk + o * R + c * kX);
+        }
+        for (int e = t; e < kBlock * D; e += 256) {
+            const int d = e / kBlock, o = e - d * kBlock;
+            const long long sl = sslot[o];
+            if (sl < 0) continue;
+            const size_t tile = ((size_t)(sl / kBlock) * num_kv_heads + h) * tile_elems;
+            vc[tile + (size_t)d * kBlock + (int)(sl % kBlock)] = sv[o * R + d];
+        }
+    } else {
+        uint8_t* kc = static_cast<uint8_t*>(k_cache);
+        uint8_t* vc = static_cast<uint8_t*>(v_cache);
+        constexpr int CH8 = D / kX8;               // 16-element x chunks of the fp8 pool
+        for (int e = t; e < kBlock * CH8; e += 256) {
+            const int c = e / kBlock, o = e - c * kBlock;
+            const long long sl = sslot[o];
+            if (sl < 0) continue;
+            u32x4 w = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int j = 0; j < kX; ++j) kc[j >> 2] |= f32_to_e4m3((float)kv[j] / k_scale) << (8 * (j & 3));
-    const size_t tile = ((size_t)b * num_kv_heads + h) * (size_t)(D * kBlock);   // bytes
-    // d = 8c + j lives in x-chunk d / 16 at element d % 16 = 8(c % 2) + j
-    *reinterpret_cast<u32x2*>(k_cache + tile + ((size_t)(c >> 1) * kBlock + o) * kX8 + 8 * (c & 1)) = kc;
-    uint8_t* vdst = v_cache + tile + (size_t)(c * kX) * kBlock + o;
-#pragma unroll
-    for (int j = 0; j < kX; ++j) vdst[j * kBlock] = (uint8_t)f32_to_e4m3((float)vv[j] / v_scale);
+            for (int j = 0; j < kX8; ++j)
+                w[j >> 2] |= f32_to_e4m3((float)sk[o * R + c * kX8 + j] / k_scale) << (8 * (j & 3));
+            const size_t tile = ((size_t)(sl / kBlock) * num_kv_heads + h) * tile_elems;
+            *reinterpret_cast<u32x4*>(kc + tile + ((size_t)c * kBlock + (int)(sl % kBlock)) * kX8) = w;
+        }
+        for (int e = t; e < kBlock * D; e += 256) {
+            const int d = e / kBlock, o = e - d * kBlock;
+            const long long sl = sslot[o];
+            if (sl < 0) continue;
+            const size_t tile = ((size_t)(sl / kBlock) * num_kv_heads + h) * tile_elems;
+            vc[tile + (size_t)d * kBlock + (int)(sl % kBlock)] =
+                (uint8_t)f32_to_e4m3((float)sv[o * R + d] / v_scale);
+        }
+    }
 }
 
 template <int D, class T>
@@ -177,36 +207,25 @@ extern "C" int reshape_and_cache(const void* key, const void* value, void* k_cac
     if (!aligned16(key) || !aligned16(value) || !aligned16(k_cache) || !aligned16(v_cache) ||
         !aligned8(slot_mapping) || key_stride % 8 != 0 || value_stride % 8 != 0)
         return PA_ERR_MISALIGNED;
-    const long long items = (long long)num_tokens * num_kv_heads * (head_size / kX);
-    const long long grid = (items + 255) / 256;
-    if (grid > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
+    if (num_kv_heads > 65535) return PA_ERR_INVALID_ARG;   // grid.y
     const long long slots = (long long)num_blocks * kBlock;
     hipStream_t st = as_stream(stream);
     auto k = static_cast<const f16*>(key);
     auto v = static_cast<const f16*>(value);
-    if (kv_cache_dtype == PA_KV_FP8_E4M3) {
-        auto kc8 = static_cast<uint8_t*>(k_cache);
-        auto vc8 = static_cast<uint8_t*>(v_cache);
-        if (head_size == 128)
-            hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<128>, dim3((unsigned)grid), dim3(256), 0,
-                               st, k, v, kc8, vc8, slot_mapping, num_tokens, num_kv_heads, slots,
-                               (long long)key_stride, (long long)value_stride, k_scale, v_scale);
-        else
-            hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<64>, dim3((unsigned)grid), dim3(256), 0,
-                               st, k, v, kc8, vc8, slot_mapping, num_tokens, num_kv_heads, slots,
-                               (long long)key_stride, (long long)value_stride, k_scale, v_scale);
-        return launch_status();
+    const dim3 grid((unsigned)((num_tokens + kBlock - 1) / kBlock), (unsigned)num_kv_heads);
+    const bool f8 = kv_cache_dtype == PA_KV_FP8_E4M3;
+#define PA_CW(DD, F8)                                                                              \
+    hipLaunchKernelGGL((reshape_and_cache_kernel<DD, F8>), grid, dim3(256), 0, st, k, v, k_cache,  \
+                       v_cache, slot_mapping, num_tokens, num_kv_heads, slots,                     \
+                       (long long)key_stride, (long long)value_stride, k_scale, v_scale)
+    if (head_size == 128) {
+        if (f8) PA_CW(128, true);
+        else PA_CW(128, false);
+    } else {
+        if (f8) PA_CW(64, true);
+        else PA_CW(64, false);
     }
-    auto kc = static_cast<f16*>(k_cache);
-    auto vc = static_cast<f16*>(v_cache);
-    if (head_size == 128)
-        hipLaunchKernelGGL(reshape_and_cache_kernel<128>, dim3((unsigned)grid), dim3(256), 0, st, k,
-                           v, kc, vc, slot_mapping, num_tokens, num_kv_heads, slots,
-                           (long long)key_stride, (long long)value_stride);
-    else
-        hipLaunchKernelGGL(reshape_and_cache_kernel<64>, dim3((unsigned)grid), dim3(256), 0, st, k,
-                           v, kc, vc, slot_mapping, num_tokens, num_kv_heads, slots,
-                           (long long)key_stride, (long long)value_stride);
+#undef PA_CW
     return launch_status();
 }
 

@@ -106,3 +106,46 @@ def test_out_of_pool_slot_is_skipped():
     k_ref, _ = oracle.reshape_and_cache(key[[0, 2]], key[[0, 2]], kc_full[:NB], vc_full[:NB],
                                         slots[[0, 2]], 16)
     assert k[:NB].tobytes() == k_ref.tobytes()
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "fp8"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_multi_token_runs_bit_exact(dtype, D):
+    """Prefill-shaped writes: each sequence's tokens fill consecutive slots of
+    its blocks, starting at a block boundary or in the middle of a block (a
+    chunk after cached context), with a padding slot inside a run, a run
+    length that is not a multiple of 16 and strided key rows."""
+    from oracle import fp8
+    rng = np.random.default_rng(D)
+    KVH, B, NB = 3, 16, 40
+    # (first logical position, token count) per sequence
+    runs = [(0, 37), (5, 16), (16, 16), (29, 50), (0, 1), (7, 3)]
+    perm = rng.permutation(NB)
+    slots, nxt = [], 0
+    for start, n in runs:
+        nb = -(-(start + n) // B)
+        blocks = perm[nxt:nxt + nb]
+        nxt += nb
+        slots += [int(blocks[p // B]) * B + p % B for p in range(start, start + n)]
+    slots = np.array(slots, np.int64)
+    slots[20] = -1
+    T = len(slots)
+    key_full = rng.standard_normal((T, KVH * D + 24)).astype(np.float16)
+    key = key_full[:, :KVH * D].reshape(T, KVH, D)
+    value = rng.standard_normal((T, KVH, D)).astype(np.float16)
+    key_dev = to_dev(key_full)[:, :KVH * D].view(T, KVH, D)
+    if dtype == "fp16":
+        kc = rng.standard_normal((NB, KVH, D // 8, B, 8)).astype(np.float16)
+        vc = rng.standard_normal((NB, KVH, D, B)).astype(np.float16)
+        kd, vd = to_dev(kc), to_dev(vc)
+        pa.reshape_and_cache(key_dev, to_dev(value), kd, vd, to_dev(slots))
+        k_ref, v_ref = oracle.reshape_and_cache(np.ascontiguousarray(key), value, kc, vc, slots, B)
+    else:
+        ks, vs = 0.02, 0.05
+        k_ref = rng.integers(0, 256, (NB, KVH, D // 16, B, 16)).astype(np.uint8)
+        v_ref = rng.integers(0, 256, (NB, KVH, D, B)).astype(np.uint8)
+        kd, vd = to_dev(k_ref), to_dev(v_ref)
+        pa.reshape_and_cache(key_dev, to_dev(value), kd, vd, to_dev(slots), ks, vs)
+        fp8.reshape_and_cache_fp8(np.ascontiguousarray(key), value, k_ref, v_ref, slots, B, ks, vs)
+    assert kd.cpu().numpy().tobytes() == k_ref.tobytes()
+    assert vd.cpu().numpy().tobytes() == v_ref.tobytes()
