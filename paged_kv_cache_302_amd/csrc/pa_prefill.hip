@@ -33,9 +33,22 @@ namespace pa {
 constexpr int kPrefillGroups = PA_PREFILL_GROUPS;
 
 // --------------------------------------------------------------------------
-// NG groups of 16 columns per wave: every K/V tile read (and, for fp8
-// pools, converted) once feeds NG score tiles and NG PV updates, so a tile
-// serves 16*NG query rows.  Each group keeps its own lane-local softmax state.
+// NG groups of 16 columns per wave: every K/V tile read (and, for fp8 pools,
+// converted) once feeds NG score tiles and NG PV updates, so a tile serves
+// 16*NG query rows.  Each group keeps its own lane-local softmax state.
+//
+// Blocks are taken in pairs.  The weights of both blocks of a pair share one
+// running max, so PV runs over 32 tokens with one 16x16x32 MFMA per 16 head
+// dims: lane (i, g) supplies V^T rows 16nt+i at tokens 4g..4g+3 of the first
+// block followed by the same tokens of the second, and, as the B operand, its
+// own weights of those eight tokens -- the k-order is permuted identically on
+// both sides, so the contraction is unchanged.
+//
+// The running max is raised lazily: a column's max m (log2 units) changes
+// only when a score exceeds it by more than kLazy, so weights exp2(t - m) stay
+// below 2^kLazy and the accumulator rescale (NT * 4 multiplies per group) is
+// skipped on most blocks.  l and acc are always taken relative to the same m,
+// so acc / l is unchanged up to rounding.
 // --------------------------------------------------------------------------
 template <class Base, int NG>
 struct MfmaGroups {
@@ -43,15 +56,20 @@ struct MfmaGroups {
     static constexpr int KC = D / 32;
     static constexpr int NT = D / 16;
     static constexpr int kElem = Base::kElem;
+    static constexpr float kLazy = 8.f;
     using Tile = typename Base::Tile;
 
     struct State {
         f32x4 acc[NG][NT];   // lane (g,i): O^T[d = 16nt + 4g + r][column 16gr + i]
-        float m[NG];
-        float l[NG];
+        float m[NG];         // running max of the column, log2 units (score * scale * log2 e)
+        float l[NG];         // this lane's share of the column's weight sum
     };
     struct QRegs {
         typename Base::QRegs q[NG];
+    };
+    struct Half {            // the first block of a pair: scores and V operands
+        f32x4 s[NG];
+        f16x4 v[NT];
     };
 
     __device__ static void init(State& st) {
@@ -69,12 +87,13 @@ struct MfmaGroups {
         Base::template load<NTL>(t, kt, vt, bytes);
     }
 
-    // nvalid: tokens of the block inside the sequence; lim[gr]: the last token
-    // offset this lane's column of group gr may see (causal limit)
-    __device__ __forceinline__ static void process(State& st, Tile& t, const QRegs& qr, int nvalid,
-                                                   float sl2, const int (&lim)[NG]) {
+    // Scores of one block in log2 units.  Tokens at or past nvalid are masked,
+    // and, when `causal` (a block that reaches past the earliest column's
+    // position), tokens past lim[gr], the last offset this lane's column of
+    // group gr may see.  For fp16 tiles, masked V entries are cleared too.
+    __device__ __forceinline__ static void scores(f32x4 (&s)[NG], Tile& t, const QRegs& qr, float sl2,
+                                                  int nvalid, bool causal, const int (&lim)[NG]) {
         const int g = lane_id() >> 4;
-        f32x4 s[NG];
 #pragma unroll
         for (int gr = 0; gr < NG; ++gr) s[gr] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -84,39 +103,111 @@ struct MfmaGroups {
             for (int gr = 0; gr < NG; ++gr)
                 s[gr] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qr.q[gr].q[c], s[gr], 0, 0, 0);
         }
+#pragma unroll
+        for (int gr = 0; gr < NG; ++gr) s[gr] *= sl2;
+        if (nvalid < kBlock || causal) {
+#pragma unroll
+            for (int gr = 0; gr < NG; ++gr)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (4 * g + r >= nvalid || 4 * g + r > lim[gr]) s[gr][r] = -INFINITY;
+        }
         if (nvalid < kBlock) Base::mask_v(t, nvalid);
-        f16x4 pv[NG];
-        float corr[NG];
+    }
+
+    // Online-softmax step over NB score tiles per group: raises the running
+    // max where needed (rescaling l and acc), then returns the fp16 weights.
+    template <int NB>
+    __device__ __forceinline__ static void weights(State& st, const f32x4 (&s)[NB][NG],
+                                                   f16x4 (&p)[NB][NG]) {
+        float bm[NG];
+        bool need = false;
 #pragma unroll
         for (int gr = 0; gr < NG; ++gr) {
+            float v = fmaxf(fmaxf(s[0][gr][0], s[0][gr][1]), fmaxf(s[0][gr][2], s[0][gr][3]));
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                if (4 * g + r >= nvalid || 4 * g + r > lim[gr]) s[gr][r] = -INFINITY;
-            float bm = fmaxf(fmaxf(s[gr][0], s[gr][1]), fmaxf(s[gr][2], s[gr][3]));
-            bm = col4_max(bm);
-            const float mn = fmaxf(st.m[gr], bm);
-            corr[gr] = exp2_fast((st.m[gr] - mn) * sl2);
-            float pr[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) pr[r] = exp2_fast((s[gr][r] - mn) * sl2);
-            st.l[gr] = st.l[gr] * corr[gr] + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-            st.m[gr] = mn;
-            pv[gr] = f16x4{(f16)pr[0], (f16)pr[1], (f16)pr[2], (f16)pr[3]};
+            for (int b = 1; b < NB; ++b)
+                v = fmaxf(v, fmaxf(fmaxf(s[b][gr][0], s[b][gr][1]), fmaxf(s[b][gr][2], s[b][gr][3])));
+            bm[gr] = v;
+            need = need || v > st.m[gr] + kLazy;
         }
+        if (__builtin_amdgcn_ballot_w64(need) != 0) {
+#pragma unroll
+            for (int gr = 0; gr < NG; ++gr) {
+                const float mn = fmaxf(st.m[gr], col4_max(bm[gr]));
+                const float corr = exp2_fast(st.m[gr] - mn);   // 0 while m is still -inf
+                st.l[gr] *= corr;
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) st.acc[gr][nt] *= corr;
+                st.m[gr] = mn;
+            }
+        }
+#pragma unroll
+        for (int gr = 0; gr < NG; ++gr) {
+            float sum = 0.f;
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                float pr[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) pr[r] = exp2_fast(s[b][gr][r] - st.m[gr]);
+                sum += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+                p[b][gr] = f16x4{(f16)pr[0], (f16)pr[1], (f16)pr[2], (f16)pr[3]};
+            }
+            st.l[gr] += sum;
+        }
+    }
+
+    // One block alone (the last block of a unit with an odd block count).
+    __device__ __forceinline__ static void single(State& st, Tile& t, const QRegs& qr, float sl2,
+                                                  int nvalid, bool causal, const int (&lim)[NG]) {
+        f32x4 s[1][NG];
+        scores(s[0], t, qr, sl2, nvalid, causal, lim);
+        f16x4 p[1][NG];
+        weights<1>(st, s, p);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             const f16x4 a = Base::a_v(t, nt);
 #pragma unroll
+            for (int gr = 0; gr < NG; ++gr)
+                st.acc[gr][nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, p[0][gr], st.acc[gr][nt], 0, 0, 0);
+        }
+    }
+
+    // First block of a pair: its scores and V operands are kept, so its
+    // registers can take the next tile while the second block is processed.
+    __device__ __forceinline__ static void first(Half& h, Tile& t, const QRegs& qr, float sl2,
+                                                 int nvalid, bool causal, const int (&lim)[NG]) {
+        scores(h.s, t, qr, sl2, nvalid, causal, lim);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) h.v[nt] = Base::a_v(t, nt);
+    }
+
+    // Second block of a pair: weights of both blocks, then PV over 32 tokens.
+    __device__ __forceinline__ static void second(State& st, const Half& h, Tile& t, const QRegs& qr,
+                                                  float sl2, int nvalid, bool causal,
+                                                  const int (&lim)[NG]) {
+        f32x4 s[2][NG];
+#pragma unroll
+        for (int gr = 0; gr < NG; ++gr) s[0][gr] = h.s[gr];
+        scores(s[1], t, qr, sl2, nvalid, causal, lim);
+        f16x4 p[2][NG];
+        weights<2>(st, s, p);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const f16x4 b = Base::a_v(t, nt);
+            const f16x8 a = {h.v[nt][0], h.v[nt][1], h.v[nt][2], h.v[nt][3], b[0], b[1], b[2], b[3]};
+#pragma unroll
             for (int gr = 0; gr < NG; ++gr) {
-                st.acc[gr][nt] *= corr[gr];
-                st.acc[gr][nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, pv[gr], st.acc[gr][nt], 0, 0, 0);
+                const f16x8 w = {p[0][gr][0], p[0][gr][1], p[0][gr][2], p[0][gr][3],
+                                 p[1][gr][0], p[1][gr][1], p[1][gr][2], p[1][gr][3]};
+                st.acc[gr][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, w, st.acc[gr][nt], 0, 0, 0);
             }
         }
     }
 
     // Rows of every group to LDS: s_acc[(16gr + i) * D + d] unnormalised,
-    // s_m / s_l [16gr + i] (l summed over the column's four token groups).
-    __device__ static void stage(const State& st, float* s_acc, float* s_m, float* s_l) {
+    // s_l[16gr + i] the column's weight sum (over its four token groups).
+    __device__ static void stage(const State& st, float* s_acc, float* s_l) {
         const int l = lane_id(), i = l & 15, g = l >> 4;
 #pragma unroll
         for (int gr = 0; gr < NG; ++gr) {
@@ -124,10 +215,7 @@ struct MfmaGroups {
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
                 *reinterpret_cast<f32x4*>(s_acc + (16 * gr + i) * D + 16 * nt + 4 * g) = st.acc[gr][nt];
-            if (g == 0) {
-                s_m[16 * gr + i] = st.m[gr];
-                s_l[16 * gr + i] = ltot;
-            }
+            if (g == 0) s_l[16 * gr + i] = ltot;
         }
     }
 };
@@ -198,15 +286,18 @@ __global__ __launch_bounds__(64) void pa_prefill_kernel(DecodeParams p,
         auto tile_k = [&](int id) { return kbase + (size_t)id * blk_stride; };
         auto tile_v = [&](int id) { return vbase + (size_t)id * blk_stride; };
         auto valid = [&](int k) { return min(kBlock, L - k * kBlock); };
-        auto visit = [&](typename G2::Tile& t, int k) {
-            int lim[NG];   // last visible key offset in block k (padding columns: all)
+        // the earliest column's position: blocks reaching past it need the causal mask
+        const int pos_first = L - nq + j0;
+        auto lims = [&](int k, int (&lim)[NG]) {
 #pragma unroll
             for (int gr = 0; gr < NG; ++gr)
                 lim[gr] = col_ok[gr] ? min(kBlock - 1, pos[gr] - k * kBlock) : kBlock - 1;
-            G2::process(st, t, qr, valid(k), sl2, lim);
         };
+        auto causal = [&](int k) { return k * kBlock + kBlock - 1 > pos_first; };
         auto live = [&](int j) { return j < n ? TB : 0; };
         typename G2::Tile ta, tb;
+        typename G2::Half h;
+        int lim[NG];
         int id = phys(0, 0);
         G2::template load<false>(ta, tile_k(id), tile_v(id), TB);
         int k = 0;
@@ -216,24 +307,28 @@ __global__ __launch_bounds__(64) void pa_prefill_kernel(DecodeParams p,
             for (; k < kend; k += 2) {
                 id = phys(kw, k + 1);
                 G2::template load<false>(tb, tile_k(id), tile_v(id), TB);
-                visit(ta, k);
+                lims(k, lim);
+                G2::first(h, ta, qr, sl2, valid(k), causal(k), lim);
                 id = phys(kw, k + 2);
                 G2::template load<false>(ta, tile_k(id), tile_v(id), live(k + 2));
-                visit(tb, k + 1);
+                lims(k + 1, lim);
+                G2::second(st, h, tb, qr, sl2, valid(k + 1), causal(k + 1), lim);
             }
             if (kw + 64 >= n) break;
             cur = nxt;
             nxt = pend;
         }
-        if (k < n) visit(ta, k);
+        if (k < n) {
+            lims(k, lim);
+            G2::single(st, ta, qr, sl2, valid(k), causal(k), lim);
+        }
     }
 
     // rows of the tile through LDS, then whole 16-byte stores per lane (the
     // heads of one token are one contiguous run of gc*D floats)
     float* s_o = lds;                 // [16 NG][D]
-    float* s_m = lds + 16 * NG * D;   // [16 NG]
-    float* s_l = s_m + 16 * NG;       // [16 NG]
-    G2::stage(st, s_o, s_m, s_l);
+    float* s_l = lds + 16 * NG * D;   // [16 NG]
+    G2::stage(st, s_o, s_l);
     const f32x4* src = reinterpret_cast<const f32x4*>(s_o);
     const int cols = ntok * gc;       // valid columns: 0 .. cols-1
     for (int e = lane_id(); e < cols * (D / 4); e += 64) {
@@ -275,7 +370,7 @@ extern "C" int pa_prefill(float* out, const void* q, const void* k_cache, const 
     const int q_tiles = (max_query_len + tpu - 1) / tpu;
     const long long grid = (long long)num_seqs * q_tiles * num_kv_heads * p.head_chunks;
     if (grid > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
-    const size_t lds = (16 * NG * (size_t)head_size + 32 * NG) * sizeof(float);
+    const size_t lds = (16 * NG * (size_t)head_size + 16 * NG) * sizeof(float);
     hipStream_t st = as_stream(stream);
     const bool fp8 = kv_cache_dtype == PA_KV_FP8_E4M3;
 #define PA_PREFILL(PATH, DD)                                                                   \

@@ -86,3 +86,20 @@ def test_more_queries_than_tokens_gives_nan_rows():
     ref = oracle.paged_prefill(q[4:], inp.k_cache, inp.v_cache, inp.block_tables[1:], lens[1:],
                                qsl[1:] - qsl[1], inp.scale, 16)
     assert_parity(out[4:], ref, "other sequence unaffected")
+
+
+@pytest.mark.parametrize("grow", [0.05, 0.6])
+def test_prefill_with_growing_scores(grow):
+    """Keys whose magnitude grows along the sequence push every column's
+    running max up block after block (by more or less than the kernel's
+    lazy-rescale margin); the first block's scores are the smallest."""
+    inp, lens, qsl, q = make("grow", 16, 4, 128, [300, 77, 150], [300, 40, 150], seed=45)
+    k = inp.k_cache.astype(np.float64)
+    for s, L in enumerate(lens):
+        for t in range(int(L)):
+            b, o = inp.block_tables[s, t // 16], t % 16
+            k[b, :, :, o, :] *= 1.0 + grow * t / 16
+    kc = k.astype(np.float16)
+    ref = oracle.paged_prefill(q, kc, inp.v_cache, inp.block_tables, lens, qsl, inp.scale, 16)
+    out = run(q, to_dev(kc), to_dev(inp.v_cache), inp.block_tables, lens, qsl, inp.scale, 300)
+    assert_parity(out, ref, f"grow {grow}")
