@@ -168,19 +168,18 @@ struct MfmaPath {
     }
 
     // nvalid: tokens of the block inside the sequence (the rest is never
-    // read); lim: the last token offset this lane's column may see (a causal
-    // limit; kBlock - 1 = no limit), masked to -inf before the softmax.
+    // read), masked to -inf before the softmax.
     __device__ __forceinline__ static void process(State& st, Tile& t, const QRegs& qr,
-                                                   int nvalid, float sl2, int lim = kBlock - 1) {
+                                                   int nvalid, float sl2) {
         const int l = lane_id(), g = l >> 4;
         f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < KC; ++c)
             s = __builtin_amdgcn_mfma_f32_16x16x32_f16(t.k[c], qr.q[c], s, 0, 0, 0);
-        if (nvalid < kBlock || lim < kBlock - 1) {
+        if (nvalid < kBlock) {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                if (4 * g + r >= nvalid || 4 * g + r > lim) s[r] = -INFINITY;
+                if (4 * g + r >= nvalid) s[r] = -INFINITY;
         }
         if (nvalid < kBlock) {
 #pragma unroll
@@ -395,8 +394,7 @@ struct MfmaPath8 : MfmaPath<D> {
     }
 
     __device__ __forceinline__ static void process(typename Base::State& st, Tile& t,
-                                                   const QRegs& qr, int nvalid, float sl2,
-                                                   int lim = kBlock - 1) {
+                                                   const QRegs& qr, int nvalid, float sl2) {
         const int l = lane_id(), g = l >> 4;
         f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -406,10 +404,10 @@ struct MfmaPath8 : MfmaPath<D> {
             const f16x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
             s = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qr.q[c], s, 0, 0, 0);
         }
-        if (nvalid < kBlock || lim < kBlock - 1) {
+        if (nvalid < kBlock) {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                if (4 * g + r >= nvalid || 4 * g + r > lim) s[r] = -INFINITY;
+                if (4 * g + r >= nvalid) s[r] = -INFINITY;
         }
         if (nvalid < kBlock) {
 #pragma unroll

@@ -87,7 +87,7 @@ struct MfmaGroups {
         Base::template load<NTL>(t, kt, vt, bytes);
     }
 
-    // Scores of one block in log2 units.  Tokens at or past nvalid are masked,
+    // Raw scores of one block (q . k).  Tokens at or past nvalid are masked,
     // and, when `causal` (a block that reaches past the earliest column's
     // position), tokens past lim[gr], the last offset this lane's column of
     // group gr may see.  For fp16 tiles, masked V entries are cleared too.
@@ -103,8 +103,6 @@ struct MfmaGroups {
             for (int gr = 0; gr < NG; ++gr)
                 s[gr] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qr.q[gr].q[c], s[gr], 0, 0, 0);
         }
-#pragma unroll
-        for (int gr = 0; gr < NG; ++gr) s[gr] *= sl2;
         if (nvalid < kBlock || causal) {
 #pragma unroll
             for (int gr = 0; gr < NG; ++gr)
@@ -115,10 +113,12 @@ struct MfmaGroups {
         if (nvalid < kBlock) Base::mask_v(t, nvalid);
     }
 
-    // Online-softmax step over NB score tiles per group: raises the running
-    // max where needed (rescaling l and acc), then returns the fp16 weights.
+    // Online-softmax step over NB raw score tiles per group: raises the
+    // running max where needed (rescaling l and acc), then returns the fp16
+    // weights exp2(s * sl2 - m).  sl2 > 0, so the max of the scaled scores is
+    // the scaled max.
     template <int NB>
-    __device__ __forceinline__ static void weights(State& st, const f32x4 (&s)[NB][NG],
+    __device__ __forceinline__ static void weights(State& st, const f32x4 (&s)[NB][NG], float sl2,
                                                    f16x4 (&p)[NB][NG]) {
         float bm[NG];
         bool need = false;
@@ -128,8 +128,8 @@ struct MfmaGroups {
 #pragma unroll
             for (int b = 1; b < NB; ++b)
                 v = fmaxf(v, fmaxf(fmaxf(s[b][gr][0], s[b][gr][1]), fmaxf(s[b][gr][2], s[b][gr][3])));
-            bm[gr] = v;
-            need = need || v > st.m[gr] + kLazy;
+            bm[gr] = v * sl2;
+            need = need || bm[gr] > st.m[gr] + kLazy;
         }
         if (__builtin_amdgcn_ballot_w64(need) != 0) {
 #pragma unroll
@@ -145,11 +145,12 @@ struct MfmaGroups {
 #pragma unroll
         for (int gr = 0; gr < NG; ++gr) {
             float sum = 0.f;
+            const float nm = -st.m[gr];
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
                 float pr[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) pr[r] = exp2_fast(s[b][gr][r] - st.m[gr]);
+                for (int r = 0; r < 4; ++r) pr[r] = exp2_fast(fmaf(s[b][gr][r], sl2, nm));
                 sum += (pr[0] + pr[1]) + (pr[2] + pr[3]);
                 p[b][gr] = f16x4{(f16)pr[0], (f16)pr[1], (f16)pr[2], (f16)pr[3]};
             }
@@ -163,7 +164,7 @@ struct MfmaGroups {
         f32x4 s[1][NG];
         scores(s[0], t, qr, sl2, nvalid, causal, lim);
         f16x4 p[1][NG];
-        weights<1>(st, s, p);
+        weights<1>(st, s, sl2, p);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             const f16x4 a = Base::a_v(t, nt);
@@ -191,7 +192,7 @@ struct MfmaGroups {
         for (int gr = 0; gr < NG; ++gr) s[0][gr] = h.s[gr];
         scores(s[1], t, qr, sl2, nvalid, causal, lim);
         f16x4 p[2][NG];
-        weights<2>(st, s, p);
+        weights<2>(st, s, sl2, p);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             const f16x4 b = Base::a_v(t, nt);
@@ -341,6 +342,7 @@ __global__ __launch_bounds__(64) void pa_prefill_kernel(DecodeParams p,
         st_stream(reinterpret_cast<f32x4*>(orow) + (e - c * (D / 4)), v);
     }
 }
+
 
 }  // namespace pa
 

@@ -22,6 +22,8 @@ CASES = [
     ("mha_d64", 4, 4, 64, [130, 17, 64], [130, 9, 1]),
     ("g16_d64", 32, 2, 64, [70, 5], [20, 5]),
     ("g24_d128", 24, 1, 128, [60, 33], [3, 33]),
+    # more than 128 blocks: the block-table window moves during the walk
+    ("long_g4", 8, 2, 128, [2300, 1100, 2049], [40, 70, 9]),
 ]
 
 
