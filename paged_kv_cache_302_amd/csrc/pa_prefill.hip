@@ -96,13 +96,17 @@ struct MfmaGroups {
         const int g = lane_id() >> 4;
 #pragma unroll
         for (int gr = 0; gr < NG; ++gr) s[gr] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // group by group, so one group's scores are complete (and its softmax
+        // can start) while the next group's MFMAs run; K operands (converted
+        // once for fp8 tiles) are shared by the groups
+        f16x8 a[KC];
 #pragma unroll
-        for (int c = 0; c < KC; ++c) {
-            const f16x8 a = Base::a_k(t, c);
+        for (int c = 0; c < KC; ++c) a[c] = Base::a_k(t, c);
 #pragma unroll
-            for (int gr = 0; gr < NG; ++gr)
-                s[gr] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qr.q[gr].q[c], s[gr], 0, 0, 0);
-        }
+        for (int gr = 0; gr < NG; ++gr)
+#pragma unroll
+            for (int c = 0; c < KC; ++c)
+                s[gr] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[c], qr.q[gr].q[c], s[gr], 0, 0, 0);
         if (nvalid < kBlock || causal) {
 #pragma unroll
             for (int gr = 0; gr < NG; ++gr)
@@ -113,49 +117,38 @@ struct MfmaGroups {
         if (nvalid < kBlock) Base::mask_v(t, nvalid);
     }
 
-    // Online-softmax step over NB raw score tiles per group: raises the
-    // running max where needed (rescaling l and acc), then returns the fp16
-    // weights exp2(s * sl2 - m).  sl2 > 0, so the max of the scaled scores is
-    // the scaled max.
+    // Online-softmax step of group gr over NB raw score tiles: raises the
+    // column's running max where a wave-wide ballot finds a score more than
+    // kLazy above it (rescaling l and acc), then returns the fp16 weights
+    // exp2(s * sl2 - m).  sl2 > 0, so the max of the scaled scores is the
+    // scaled max.
     template <int NB>
-    __device__ __forceinline__ static void weights(State& st, const f32x4 (&s)[NB][NG], float sl2,
-                                                   f16x4 (&p)[NB][NG]) {
-        float bm[NG];
-        bool need = false;
+    __device__ __forceinline__ static void weights_group(State& st, int gr, const f32x4 (&s)[NB][NG],
+                                                         float sl2, f16x4 (&p)[NB]) {
+        float v = fmaxf(fmaxf(s[0][gr][0], s[0][gr][1]), fmaxf(s[0][gr][2], s[0][gr][3]));
 #pragma unroll
-        for (int gr = 0; gr < NG; ++gr) {
-            float v = fmaxf(fmaxf(s[0][gr][0], s[0][gr][1]), fmaxf(s[0][gr][2], s[0][gr][3]));
+        for (int b = 1; b < NB; ++b)
+            v = fmaxf(v, fmaxf(fmaxf(s[b][gr][0], s[b][gr][1]), fmaxf(s[b][gr][2], s[b][gr][3])));
+        const float bm = v * sl2;
+        if (__builtin_amdgcn_ballot_w64(bm > st.m[gr] + kLazy) != 0) {
+            const float mn = fmaxf(st.m[gr], col4_max(bm));
+            const float corr = exp2_fast(st.m[gr] - mn);
+            st.l[gr] *= corr;
 #pragma unroll
-            for (int b = 1; b < NB; ++b)
-                v = fmaxf(v, fmaxf(fmaxf(s[b][gr][0], s[b][gr][1]), fmaxf(s[b][gr][2], s[b][gr][3])));
-            bm[gr] = v * sl2;
-            need = need || bm[gr] > st.m[gr] + kLazy;
+            for (int nt = 0; nt < NT; ++nt) st.acc[gr][nt] *= corr;
+            st.m[gr] = mn;
         }
-        if (__builtin_amdgcn_ballot_w64(need) != 0) {
+        float sum = 0.f;
+        const float nm = -st.m[gr];
 #pragma unroll
-            for (int gr = 0; gr < NG; ++gr) {
-                const float mn = fmaxf(st.m[gr], col4_max(bm[gr]));
-                const float corr = exp2_fast(st.m[gr] - mn);   // 0 while m is still -inf
-                st.l[gr] *= corr;
+        for (int b = 0; b < NB; ++b) {
+            float pr[4];
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) st.acc[gr][nt] *= corr;
-                st.m[gr] = mn;
-            }
+            for (int r = 0; r < 4; ++r) pr[r] = exp2_fast(fmaf(s[b][gr][r], sl2, nm));
+            sum += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+            p[b] = f16x4{(f16)pr[0], (f16)pr[1], (f16)pr[2], (f16)pr[3]};
         }
-#pragma unroll
-        for (int gr = 0; gr < NG; ++gr) {
-            float sum = 0.f;
-            const float nm = -st.m[gr];
-#pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                float pr[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) pr[r] = exp2_fast(fmaf(s[b][gr][r], sl2, nm));
-                sum += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-                p[b][gr] = f16x4{(f16)pr[0], (f16)pr[1], (f16)pr[2], (f16)pr[3]};
-            }
-            st.l[gr] += sum;
-        }
+        st.l[gr] += sum;
     }
 
     // One block alone (the last block of a unit with an odd block count).
@@ -163,14 +156,13 @@ struct MfmaGroups {
                                                   int nvalid, bool causal, const int (&lim)[NG]) {
         f32x4 s[1][NG];
         scores(s[0], t, qr, sl2, nvalid, causal, lim);
-        f16x4 p[1][NG];
-        weights<1>(st, s, sl2, p);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            const f16x4 a = Base::a_v(t, nt);
+        for (int gr = 0; gr < NG; ++gr) {
+            f16x4 p[1];
+            weights_group<1>(st, gr, s, sl2, p);
 #pragma unroll
-            for (int gr = 0; gr < NG; ++gr)
-                st.acc[gr][nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, p[0][gr], st.acc[gr][nt], 0, 0, 0);
+            for (int nt = 0; nt < NT; ++nt)
+                st.acc[gr][nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(Base::a_v(t, nt), p[0], st.acc[gr][nt], 0, 0, 0);
         }
     }
 
@@ -191,18 +183,22 @@ struct MfmaGroups {
 #pragma unroll
         for (int gr = 0; gr < NG; ++gr) s[0][gr] = h.s[gr];
         scores(s[1], t, qr, sl2, nvalid, causal, lim);
-        f16x4 p[2][NG];
-        weights<2>(st, s, sl2, p);
+        // group by group: the PV MFMAs of one group run while the VALU
+        // computes the next group's weights (7-9% over all weights first)
+        f16x8 a[NT];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             const f16x4 b = Base::a_v(t, nt);
-            const f16x8 a = {h.v[nt][0], h.v[nt][1], h.v[nt][2], h.v[nt][3], b[0], b[1], b[2], b[3]};
+            a[nt] = f16x8{h.v[nt][0], h.v[nt][1], h.v[nt][2], h.v[nt][3], b[0], b[1], b[2], b[3]};
+        }
 #pragma unroll
-            for (int gr = 0; gr < NG; ++gr) {
-                const f16x8 w = {p[0][gr][0], p[0][gr][1], p[0][gr][2], p[0][gr][3],
-                                 p[1][gr][0], p[1][gr][1], p[1][gr][2], p[1][gr][3]};
-                st.acc[gr][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, w, st.acc[gr][nt], 0, 0, 0);
-            }
+        for (int gr = 0; gr < NG; ++gr) {
+            f16x4 p[2];
+            weights_group<2>(st, gr, s, sl2, p);
+            const f16x8 w = {p[0][0], p[0][1], p[0][2], p[0][3], p[1][0], p[1][1], p[1][2], p[1][3]};
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                st.acc[gr][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[nt], w, st.acc[gr][nt], 0, 0, 0);
         }
     }
 
