@@ -183,7 +183,9 @@ PA_API int pa_reduce(float* out, const float* tmp_out, const float* exp_sums,
  *   out             [total_q, num_heads, head_size] fp32, written
  *   q               [total_q, num_heads, head_size] fp16
  *   query_start_loc [num_seqs + 1] int32, non-decreasing, starting at 0
- *   max_query_len   >= every n (sizes the grid; 0 enqueues nothing)
+ *   max_query_len   >= every n (sizes the grid; 0 enqueues nothing); rows of a
+ *                   sequence beyond the first max_query_len (rounded up to
+ *                   the tile) are set to NaN
  *   other arguments as in pa_decode_v1.  n > L, a block id outside the pool
  *   or L beyond the table row gives NaN rows for that sequence.
  */

@@ -337,6 +337,17 @@ __global__ __launch_bounds__(64) void pa_prefill_kernel(DecodeParams p,
         float* orow = p.out + ((size_t)(q0 + j0 + cj) * p.num_heads + ch) * D;
         st_stream(reinterpret_cast<f32x4*>(orow) + (e - c * (D / 4)), v);
     }
+    // more queries than max_query_len allowed for: the rows no tile covers get
+    // NaN from the sequence's last tile (for this unit's heads)
+    const int covered = q_tiles * tpu;
+    if (qt == q_tiles - 1 && nq > covered) {
+        const int per_row = gc * D;
+        for (int e = lane_id(); e < (nq - covered) * per_row; e += 64) {
+            const int r = e / per_row, hd = e - r * per_row;
+            const int hh = kvh * p.group + hc * 16 + hd / D;
+            p.out[((size_t)(q0 + covered + r) * p.num_heads + hh) * D + (hd % D)] = NAN;
+        }
+    }
 }
 
 

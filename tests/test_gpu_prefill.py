@@ -105,3 +105,16 @@ def test_prefill_with_growing_scores(grow):
     ref = oracle.paged_prefill(q, kc, inp.v_cache, inp.block_tables, lens, qsl, inp.scale, 16)
     out = run(q, to_dev(kc), to_dev(inp.v_cache), inp.block_tables, lens, qsl, inp.scale, 300)
     assert_parity(out, ref, f"grow {grow}")
+
+
+def test_max_query_len_too_small_gives_nan_rows():
+    """A sequence with more queries than max_query_len: the rows no query tile
+    covers come back NaN; the covered rows and the other sequences are right."""
+    inp, lens, qsl, q = make("short", 8, 2, 128, [90, 40], [60, 5], seed=46)
+    ref = oracle.paged_prefill(q, inp.k_cache, inp.v_cache, inp.block_tables, lens, qsl, inp.scale, 16)
+    out = run(q, to_dev(inp.k_cache), to_dev(inp.v_cache), inp.block_tables, lens, qsl,
+              inp.scale, 20)
+    # G = 4: 8 query tokens per tile, so max_query_len 20 covers 24 rows
+    assert np.isnan(out[24:60]).all()
+    assert_parity(out[:24], ref[:24], "covered rows")
+    assert_parity(out[60:], ref[60:], "other sequence")
