@@ -85,6 +85,26 @@ def blas_threads() -> int:
         return 1
 
 
+class Parity:
+    """GPU output against the oracle on the sampled rows: max-abs, relative L2,
+    and whether every element is within 2e-3 + 1e-2 |ref| and the relative L2
+    within 1e-2."""
+
+    def __init__(self):
+        self.max_abs, self.err2, self.ref2, self.within = 0.0, 0.0, 0.0, True
+
+    def add(self, ref, gpu):
+        diff = ref - gpu
+        self.max_abs = max(self.max_abs, float(np.abs(diff).max()))
+        self.err2 += float((diff ** 2).sum())
+        self.ref2 += float((ref ** 2).sum())
+        self.within = self.within and bool((np.abs(diff) <= 2e-3 + 1e-2 * np.abs(ref)).all())
+
+    def result(self):
+        rel = (self.err2 / self.ref2) ** 0.5 if self.ref2 > 0 else 0.0
+        return {"max_abs": self.max_abs, "rel_l2": rel, "pass": self.within and rel <= 1e-2}
+
+
 def cpu_baseline(k_cache, v_cache, block_tables, seq_lens, q, scale, num_kv_heads, block_size,
                  gpu_out, budget_s: float, fp8_scales=None):
     """The oracle (fp64 NumPy) on a bounded sample of the same workload:
@@ -98,7 +118,8 @@ def cpu_baseline(k_cache, v_cache, block_tables, seq_lens, q, scale, num_kv_head
     done_bytes = 0
     spent = 0.0
     units = 0
-    max_err = 0.0
+    par = Parity()
+    esz = 1 if fp8_scales is not None else 2     # bytes per element, as in the metric
     for s in range(S):
         L = int(seq_lens[s])
         for kvh in range(num_kv_heads):
@@ -109,9 +130,9 @@ def cpu_baseline(k_cache, v_cache, block_tables, seq_lens, q, scale, num_kv_head
                 V = oracle.fp8.dequantize(oracle.fp8.quantize(V, fp8_scales[1]), fp8_scales[1])
             ref = oracle.attention(q[s, kvh * G:(kvh + 1) * G], K, V, scale)
             spent += time.perf_counter() - t0
-            done_bytes += L * 2 * D * 2
+            done_bytes += L * 2 * D * esz
             units += 1
-            max_err = max(max_err, float(np.abs(ref - gpu_out[s, kvh * G:(kvh + 1) * G]).max()))
+            par.add(ref, gpu_out[s, kvh * G:(kvh + 1) * G])
             if spent >= budget_s:
                 break
         if spent >= budget_s:
@@ -127,20 +148,26 @@ def cpu_baseline(k_cache, v_cache, block_tables, seq_lens, q, scale, num_kv_head
         "host_cpus": os.cpu_count(),
         "affinity_cpus": len(os.sched_getaffinity(0)),
         "cpu_model": cpu_model(),
-        "max_abs_diff_vs_gpu": max_err,
+        "max_abs_diff_vs_gpu": par.max_abs,
+        "parity": par.result(),
     }
 
 
-def kernel_source_hash() -> str:
+DECODE_SOURCES = ("pa_decode.hip", "pa_paths.h", "pa_device.h")
+PREFILL_SOURCES = ("pa_prefill.hip", "pa_paths.h", "pa_device.h")
+
+
+def kernel_source_hash(names=DECODE_SOURCES) -> str:
+    """First 16 hex digits of the SHA-256 of the kernel sources `names`."""
     import hashlib
     h = hashlib.sha256()
-    for name in ("pa_decode.hip", "pa_paths.h", "pa_device.h"):
+    for name in names:
         with open(os.path.join(ROOT, "paged_kv_cache_302_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def read_traffic(kname: str, workload: str):
+def read_traffic(kname: str, workload: str, sources=DECODE_SOURCES):
     """HBM bytes per launch from the committed rocprofv3 counter summary
     (profiles/traffic_<kernel>_<workload>.txt), or None when there is none or
     the kernel source changed since the counters were taken."""
@@ -153,7 +180,7 @@ def read_traffic(kname: str, workload: str):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 fields[k.strip()] = v.strip()
-    if fields.get("kernel_source_sha256_16") != kernel_source_hash():
+    if fields.get("kernel_source_sha256_16") != kernel_source_hash(sources):
         return None
     try:
         return int(float(fields["traffic_bytes_per_launch"]))
@@ -190,6 +217,20 @@ def to_fp8_pools(pa, inp, kc16, vc16, bt, sl, k_scale, v_scale, dev):
 def pct(ms):
     """p10 and p90 of per-step kernel times (ms) in microseconds."""
     return [round(float(np.percentile(ms, 10)) * 1e3, 2), round(float(np.percentile(ms, 90)) * 1e3, 2)]
+
+
+def copy_calibration(dev):
+    """Three device copies of exactly 1 GiB, so that a rocprofv3 --pmc run of
+    the same process can scale FETCH_SIZE / WRITE_SIZE by what the counters
+    read for a copy of known size."""
+    import torch
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def device_copy_gbs(dev, nbytes=1 << 30, reps=5):
@@ -298,6 +339,8 @@ def main_fork(args):
             ev[4].record(stream)
 
     ms_per_step, evs, wall = timed_steps(args, step, 5)
+    if args.copy_calibration:
+        copy_calibration(dev)
     med = lambda i: float(np.median([e[i].elapsed_time(e[i + 1]) for e in evs]))
     copy_s = med(0) / 1e3
     dec_s = float(np.mean([e[2].elapsed_time(e[3]) for e in evs])) / 1e3
@@ -418,6 +461,8 @@ def main_prefill(args, w):
             ev[2].record(stream)
 
     ms_per_step, evs, wall = timed_steps(args, step, 3)
+    if args.copy_calibration:
+        copy_calibration(dev)
     pf_s = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) / 1e3
     # query-key pairs inside the causal mask: sum over queries of (position + 1)
     pairs = sum(int(n * (int(L) - n) + n * (n + 1) // 2) for L in inp.seq_lens)
@@ -459,8 +504,13 @@ def main_prefill(args, w):
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
-            "traffic": None,
+            "traffic": read_traffic("pa_prefill", args.workload + ("_fp8" if fp8 else ""),
+                                    PREFILL_SOURCES),
             "algorithmic_flops_per_launch": flops,
+            "kv_bytes_per_launch": kv_bytes,
+            # q and the contexts' K/V, each read once; out (fp32) is written once
+            "read_bytes_per_launch": kv_bytes + S * n * H * D * 2,
+            "write_bytes_per_launch": S * n * H * D * 4,
             "avg_launch_us": round(pf_s * 1e6, 2),
             "hbm_floor_us": round(kv_bytes / 8e12 * 1e6, 2),
         },
@@ -473,21 +523,27 @@ def main_prefill(args, w):
         gpu_out = out.cpu().numpy()
         oracle.reshape_and_cache(keyh, valh, inp.k_cache, inp.v_cache, slots, B, inplace=True)
         G = H // KVH
-        done, spent, rows, max_err = 0.0, 0.0, 0, 0.0
-        L = int(inp.seq_lens[0])
-        for kvh in range(KVH):
-            K, V = oracle.gather_sequence_fast(inp.k_cache, inp.v_cache, inp.block_tables[0], L, kvh, B)
-            if fp8:
-                K = oracle.fp8.dequantize(oracle.fp8.quantize(K, ks), ks)
-                V = oracle.fp8.dequantize(oracle.fp8.quantize(V, vs), vs)
-            for j in range(n - 1, -1, -97):           # query rows spread over the chunk
-                p = L - n + j
-                t1 = time.perf_counter()
-                ref = oracle.attention(qh[j, kvh * G:(kvh + 1) * G], K[:p + 1], V[:p + 1], inp.scale)
-                spent += time.perf_counter() - t1
-                done += 4.0 * G * D * (p + 1)
-                rows += 1
-                max_err = max(max_err, float(np.abs(ref - gpu_out[j, kvh * G:(kvh + 1) * G]).max()))
+        done, spent, rows = 0.0, 0.0, 0
+        par = Parity()
+        # query rows spread over each chunk, sequence by sequence, until the budget is spent
+        for s in range(S):
+            L = int(inp.seq_lens[s])
+            for kvh in range(KVH):
+                K, V = oracle.gather_sequence_fast(inp.k_cache, inp.v_cache, inp.block_tables[s], L, kvh, B)
+                if fp8:
+                    K = oracle.fp8.dequantize(oracle.fp8.quantize(K, ks), ks)
+                    V = oracle.fp8.dequantize(oracle.fp8.quantize(V, vs), vs)
+                for j in range(n - 1 - (s + kvh) % 13, -1, -13):
+                    p = L - n + j
+                    row = int(qsl[s]) + j
+                    t1 = time.perf_counter()
+                    ref = oracle.attention(qh[row, kvh * G:(kvh + 1) * G], K[:p + 1], V[:p + 1], inp.scale)
+                    spent += time.perf_counter() - t1
+                    done += 4.0 * G * D * (p + 1)
+                    rows += 1
+                    par.add(ref, gpu_out[row, kvh * G:(kvh + 1) * G])
+                    if spent >= args.cpu_seconds:
+                        break
                 if spent >= args.cpu_seconds:
                     break
             if spent >= args.cpu_seconds:
@@ -495,10 +551,12 @@ def main_prefill(args, w):
         res["cpu_baseline"] = {
             "value": round(done / spent / 1e12, 6), "unit": "TFLOP/s", "cores": blas_threads(),
             "kind": "oracle",
-            "sample": f"{rows} (query row, KV head) attentions of sequence 0, fp64 NumPy two-pass softmax",
+            "sample": f"{rows} (query row, KV head) attentions, every 13th query row of each chunk "
+                      f"from sequence 0 on, fp64 NumPy two-pass softmax",
             "seconds": round(spent, 3), "host_cpus": os.cpu_count(),
             "affinity_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(),
-            "max_abs_diff_vs_gpu": max_err,
+            "max_abs_diff_vs_gpu": par.max_abs,
+            "parity": par.result(),
         }
     else:
         res["cpu_baseline"] = None
@@ -591,13 +649,7 @@ def main():
         ms_per_step = wall_ms_per_step
 
     if args.copy_calibration:
-        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_calibration(dev)
 
     cache_ms = [e[0].elapsed_time(e[1]) for e in evs]
     decode_ms = [e[1].elapsed_time(e[2]) for e in evs]
