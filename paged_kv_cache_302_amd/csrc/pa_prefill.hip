@@ -10,7 +10,12 @@
 // token's, are already in the pools (written by reshape_and_cache).  n_s = 1
 // is a decode step; n_s = L_s is a plain prefill.
 //
-// Work unit: one wavefront per (sequence, query tile, KV head, head chunk).
+// Two forms.  fp16 pools: one wavefront per (sequence, query tile, KV head,
+// head chunk), its tiles loaded straight into registers.  fp8 pools: a
+// workgroup of four such wavefronts on consecutive query tiles sharing K/V
+// through LDS (pa_prefill_wg_kernel below).
+//
+// Work unit of a wavefront:
 // The columns of the MFMA score tiles S^T = K Q^T are (token, head) pairs of
 // one KV group -- 16 NG / G consecutive query tokens times the G heads, or
 // NG tokens of 16 heads when G >= 16 -- in NG groups of 16, so every K/V
@@ -31,6 +36,7 @@
 namespace pa {
 
 constexpr int kPrefillGroups = PA_PREFILL_GROUPS;
+constexpr int kStageBlocks = 4;   // blocks per LDS stage of the workgroup form
 
 // --------------------------------------------------------------------------
 // NG groups of 16 columns per wave: every K/V tile read (and, for fp8 pools,
@@ -202,6 +208,21 @@ struct MfmaGroups {
         }
     }
 
+    // Rows of group gr to LDS: s_acc[i * D + d] unnormalised, s_l[i] the
+    // column's weight sum.
+    __device__ static void stage_group(const State& st, int gr, float* s_acc, float* s_l) {
+        const int l = lane_id(), i = l & 15, g = l >> 4;
+#pragma unroll
+        for (int x = 0; x < NG; ++x) {
+            if (x != gr) continue;
+            const float ltot = col4_sum(st.l[x]);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                *reinterpret_cast<f32x4*>(s_acc + i * D + 16 * nt + 4 * g) = st.acc[x][nt];
+            if (g == 0) s_l[i] = ltot;
+        }
+    }
+
     // Rows of every group to LDS: s_acc[(16gr + i) * D + d] unnormalised,
     // s_l[16gr + i] the column's weight sum (over its four token groups).
     __device__ static void stage(const State& st, float* s_acc, float* s_l) {
@@ -351,6 +372,230 @@ __global__ __launch_bounds__(64) void pa_prefill_kernel(DecodeParams p,
 }
 
 
+
+// --------------------------------------------------------------------------
+// Workgroup form: W waves on consecutive query tiles of one (sequence, KV
+// head, head chunk) share K/V through a two-slot LDS ring of 4-block stages.
+// While the waves compute stage j from LDS, every thread holds its share of
+// stage j + 1 (16-byte loads issued a whole stage ahead) and writes it to the
+// other slot; one barrier per stage.  K tiles keep their pool layout in LDS
+// (lane l reads 16 bytes at 16 (l + 64c): conflict-free); V tiles are stored
+// with the piece of lane (i, g) -- head dim 16nt + i, tokens 4g .. 4g + 3 --
+// at index 16g + i + 64nt, so a wave's V operand read is consecutive too.
+// --------------------------------------------------------------------------
+// A tile from an LDS stage: K in pool layout, V with lane (i, g)'s piece at
+// index 16g + i + 64nt.
+template <class Path>
+__device__ __forceinline__ void lds_tile(typename Path::Tile& t, const char* kt, const char* vt) {
+    constexpr int D = Path::kD;
+    const int l = lane_id();
+    if constexpr (Path::kElem == 2) {
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c) t.k[c] = *reinterpret_cast<const f16x8*>(kt + 16 * (l + 64 * c));
+#pragma unroll
+        for (int nt = 0; nt < D / 16; ++nt) t.v[nt] = *reinterpret_cast<const f16x4*>(vt + 8 * (l + 64 * nt));
+    } else {
+#pragma unroll
+        for (int r = 0; r < D / 64; ++r) t.k[r] = *reinterpret_cast<const u32x4*>(kt + 16 * (l + 64 * r));
+#pragma unroll
+        for (int nt = 0; nt < D / 16; ++nt) t.v[nt] = *reinterpret_cast<const uint32_t*>(vt + 4 * (l + 64 * nt));
+    }
+}
+
+template <class Path, int NG, int W>
+// (two resident waves per SIMD asked of the register allocator: at most 256 VGPRs)
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) void pa_prefill_wg_kernel(DecodeParams p,
+                                                               const int32_t* __restrict__ qsl,
+                                                               int tpu, int q_tiles) {
+    using G2 = MfmaGroups<Path, NG>;
+    constexpr int D = G2::D;
+    constexpr int NT = D / 16;
+    constexpr int EB = G2::kElem;                  // bytes per element
+    constexpr int TB = D * kBlock * EB;            // bytes of one K (or V) tile
+    constexpr int SB = kStageBlocks;
+    constexpr int STAGE = 2 * SB * TB;             // K and V of SB blocks
+    constexpr int CPT = STAGE / (16 * 64 * W);     // 16-byte pieces per thread per stage
+    static_assert(CPT >= 1 && STAGE % (16 * 64 * W) == 0, "stage copy does not tile the workgroup");
+    extern __shared__ __align__(16) char smem[];   // ring[2][STAGE]; after the walk, per-wave staging
+    const int wave = threadIdx.x >> 6;
+    const int kvhc_count = p.num_kv_heads * p.head_chunks;
+    const int kvhc = blockIdx.x % kvhc_count;
+    const int sq = blockIdx.x / kvhc_count;
+    const int s = sq / q_tiles, qt = sq - s * q_tiles;
+    const int kvh = kvhc / p.head_chunks;
+    const int hc = kvhc - kvh * p.head_chunks;
+    const int gleft = p.group - hc * 16;
+    const int gc = gleft < 16 ? gleft : 16;        // heads of this chunk
+    const int q0 = qsl[s];
+    const int nq = qsl[s + 1] - q0;
+    const int jw = qt * W * tpu;                   // first query token of the workgroup
+    if (jw >= nq) return;                          // the whole workgroup
+    const int j0 = jw + wave * tpu;                // first query token of this wave
+    const int ntok = max(0, min(tpu, nq - j0));
+    const int L = p.seq_lens[s];
+    const int nb_seq = (L + kBlock - 1) / kBlock;
+    bool bad = nq > L || nb_seq > p.max_blocks_per_seq;
+
+    const int i = lane_id() & 15;
+    int pos[NG];
+    bool col_ok[NG];
+    typename G2::QRegs qr;
+#pragma unroll
+    for (int gr = 0; gr < NG; ++gr) {
+        const int c = 16 * gr + i;
+        const int jj = c / gc;
+        const int hh = kvh * p.group + hc * 16 + (c - jj * gc);
+        col_ok[gr] = jj < ntok;
+        pos[gr] = L - nq + j0 + jj;
+        Path::load_q_row(qr.q[gr], p.q + ((size_t)(q0 + j0 + jj) * p.num_heads + hh) * D,
+                         col_ok[gr] && !bad);
+    }
+    typename G2::State st;
+    G2::init(st);
+
+    const int ntok_wg = min(W * tpu, nq - jw);
+    const int n = bad ? 0 : (L - nq + jw + ntok_wg - 1) / kBlock + 1;        // blocks of the workgroup
+    const int n_w = ntok == 0 ? 0 : (L - nq + j0 + ntok - 1) / kBlock + 1;   // blocks of this wave
+    const char* kbase = p.k_cache + (size_t)kvh * TB;
+    const char* vbase = p.v_cache + (size_t)kvh * TB;
+    const size_t blk_stride = (size_t)p.num_kv_heads * TB;
+    const int32_t* row = p.block_tables + (size_t)s * p.max_blocks_per_seq;
+    const float sl2 = p.scale_log2;
+    const int pos_first = L - nq + j0;
+
+    if (n > 0) {
+        int kw = 0;                                // cur: blocks [kw, kw + 64), nxt the next 64
+        int cur = table_window<1>(row, 0, n, 0);
+        int nxt = table_window<1>(row, 0, n, 64);
+        int pend = table_window<1>(row, 0, n, 128);
+        const unsigned num_blocks = (unsigned)p.num_blocks;
+        const int nst = (n + SB - 1) / SB;
+        u32x4 stg[CPT];
+        typename G2::Half h;
+        typename G2::Tile ta, tb;
+        int lim[NG];
+        // stage j of the K/V walk from global memory into stg (16-byte pieces:
+        // piece e is tile e / (TB / 16) -- block q / 2, K if q is even -- at
+        // byte (e % (TB / 16)) * 16); blocks past the walk read nothing
+#define PA_FETCH(J)                                                                                \
+        _Pragma("unroll") for (int u = 0; u < CPT; ++u) {                                          \
+            const int e = (int)threadIdx.x + 64 * W * u;                                           \
+            const int q = e / (TB / 16);                                                           \
+            const int o = (e - q * (TB / 16)) * 16;                                                \
+            const int k = SB * (J) + (q >> 1);                                                     \
+            const int d = min(k, n - 1) - kw;                                                      \
+            const int v = d < 64 ? __builtin_amdgcn_readlane(cur, d)                               \
+                                 : __builtin_amdgcn_readlane(nxt, d - 64);                         \
+            const bool ok = (unsigned)v < num_blocks;                                              \
+            bad = bad || !ok;                                                                      \
+            const char* src = ((q & 1) ? vbase : kbase) + (size_t)(ok ? v : 0) * blk_stride + o;  \
+            stg[u] = k < n ? *reinterpret_cast<const u32x4*>(src) : u32x4{0u, 0u, 0u, 0u};        \
+        }
+        // stg into LDS slot SLOT (V pieces rearranged for the operand reads)
+#define PA_COMMIT(SLOT)                                                                            \
+        _Pragma("unroll") for (int u = 0; u < CPT; ++u) {                                          \
+            const int e = (int)threadIdx.x + 64 * W * u;                                           \
+            const int q = e / (TB / 16);                                                           \
+            const int o = (e - q * (TB / 16)) * 16;                                                \
+            char* tile = smem + (SLOT) * STAGE + q * TB;                                           \
+            if (!(q & 1)) {                                                                        \
+                *reinterpret_cast<u32x4*>(tile + o) = stg[u];                                      \
+            } else if constexpr (EB == 2) {                                                        \
+                /* head dim d, tokens 8h .. 8h + 7: pieces g = 2h, 2h + 1 */                       \
+                const int dd = o >> 5, hh = (o >> 4) & 1;                                          \
+                const int base = (dd & 15) + 64 * (dd >> 4);                                       \
+                *reinterpret_cast<u32x2*>(tile + 8 * (32 * hh + base)) = u32x2{stg[u][0], stg[u][1]};      \
+                *reinterpret_cast<u32x2*>(tile + 8 * (32 * hh + 16 + base)) = u32x2{stg[u][2], stg[u][3]}; \
+            } else {                                                                               \
+                /* head dim d, all 16 tokens: pieces g = 0 .. 3 */                                 \
+                const int dd = o >> 4;                                                             \
+                const int base = (dd & 15) + 64 * (dd >> 4);                                       \
+                *reinterpret_cast<uint32_t*>(tile + 4 * (base)) = stg[u][0];                       \
+                *reinterpret_cast<uint32_t*>(tile + 4 * (16 + base)) = stg[u][1];                  \
+                *reinterpret_cast<uint32_t*>(tile + 4 * (32 + base)) = stg[u][2];                  \
+                *reinterpret_cast<uint32_t*>(tile + 4 * (48 + base)) = stg[u][3];                  \
+            }                                                                                      \
+        }
+        PA_FETCH(0)
+        PA_COMMIT(0)
+        __syncthreads();
+        for (int j = 0; j < nst; ++j) {
+            if (SB * (j + 1) + SB - 1 >= kw + 128) {   // the next stage leaves the table window
+                kw += 64;
+                cur = nxt;
+                nxt = pend;
+                pend = table_window<1>(row, 0, n, kw + 128);
+            }
+            if (j + 1 < nst) {
+                PA_FETCH(j + 1)
+            }
+            const char* ring = smem + (j & 1) * STAGE;
+#pragma unroll 1
+            for (int pr = 0; pr < SB / 2; ++pr) {
+                const int k = SB * j + 2 * pr;
+                if (k < n_w) {
+                    lds_tile<Path>(ta, ring + (4 * pr) * TB, ring + (4 * pr + 1) * TB);
+#pragma unroll
+                    for (int gr = 0; gr < NG; ++gr)
+                        lim[gr] = col_ok[gr] ? min(kBlock - 1, pos[gr] - k * kBlock) : kBlock - 1;
+                    const int va = min(kBlock, L - k * kBlock);
+                    const bool ca = k * kBlock + kBlock - 1 > pos_first;
+                    if (k + 1 < n_w) {
+                        G2::first(h, ta, qr, sl2, va, ca, lim);
+                        lds_tile<Path>(tb, ring + (4 * pr + 2) * TB, ring + (4 * pr + 3) * TB);
+#pragma unroll
+                        for (int gr = 0; gr < NG; ++gr)
+                            lim[gr] = col_ok[gr] ? min(kBlock - 1, pos[gr] - (k + 1) * kBlock) : kBlock - 1;
+                        G2::second(st, h, tb, qr, sl2, min(kBlock, L - (k + 1) * kBlock),
+                                   (k + 1) * kBlock + kBlock - 1 > pos_first, lim);
+                    } else {
+                        G2::single(st, ta, qr, sl2, va, ca, lim);
+                    }
+                }
+            }
+            if (j + 1 < nst) {
+                PA_COMMIT((j + 1) & 1)
+            }
+            __syncthreads();
+        }
+#undef PA_FETCH
+#undef PA_COMMIT
+    }
+
+    // per wave and group: rows through LDS, then whole 16-byte stores
+    float* s_o = reinterpret_cast<float*>(smem) + wave * (16 * D + 16);
+    float* s_l = s_o + 16 * D;
+    const int cols = ntok * gc;
+    const f32x4* src = reinterpret_cast<const f32x4*>(s_o);
+#pragma unroll
+    for (int gr = 0; gr < NG; ++gr) {
+        if (16 * gr >= cols) break;
+        G2::stage_group(st, gr, s_o, s_l);
+        const int cg = min(16, cols - 16 * gr);
+        for (int e = lane_id(); e < cg * (D / 4); e += 64) {
+            const int ci = (4 * e) / D;
+            const int c = 16 * gr + ci;
+            const int cj = c / gc;
+            const int ch = kvh * p.group + hc * 16 + (c - cj * gc);
+            f32x4 v = src[e] * (p.v_scale / s_l[ci]);
+            if (bad) v = f32x4{NAN, NAN, NAN, NAN};
+            float* orow = p.out + ((size_t)(q0 + j0 + cj) * p.num_heads + ch) * D;
+            st_stream(reinterpret_cast<f32x4*>(orow) + (e - ci * (D / 4)), v);
+        }
+    }
+    // more queries than max_query_len allowed for: the last workgroup of the
+    // sequence sets the uncovered rows (this unit's heads) to NaN
+    const int covered = q_tiles * W * tpu;
+    if (qt == q_tiles - 1 && wave == 0 && nq > covered) {
+        const int per_row = gc * D;
+        for (int e = lane_id(); e < (nq - covered) * per_row; e += 64) {
+            const int r = e / per_row, hd = e - r * per_row;
+            const int hh = kvh * p.group + hc * 16 + hd / D;
+            p.out[((size_t)(q0 + covered + r) * p.num_heads + hh) * D + (hd % D)] = NAN;
+        }
+    }
+}
+
 }  // namespace pa
 
 using namespace pa;
@@ -375,23 +620,36 @@ extern "C" int pa_prefill(float* out, const void* q, const void* k_cache, const 
     const int G = num_heads / num_kv_heads;
     p.head_chunks = G > 16 ? (G + 15) / 16 : 1;
     constexpr int NG = kPrefillGroups;
-    const int tpu = G >= 16 ? NG : (16 * NG) / G;       // query tokens per tile
-    const int q_tiles = (max_query_len + tpu - 1) / tpu;
+    const bool fp8 = kv_cache_dtype == PA_KV_FP8_E4M3;
+    // fp8 pools: four waves share 4-block K/V stages through LDS (1.2-1.3x
+    // over one wave); fp16 pools: one wave per unit with its tiles in
+    // registers (the shared form needs 256 VGPRs there and runs slower)
+    constexpr int W8 = 4;
+    const int W = fp8 ? W8 : 1;
+    const int tpu = G >= 16 ? NG : (16 * NG) / G;       // query tokens per wave
+    const int q_tiles = (max_query_len + W * tpu - 1) / (W * tpu);
     const long long grid = (long long)num_seqs * q_tiles * num_kv_heads * p.head_chunks;
     if (grid > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
-    const size_t lds = (16 * NG * (size_t)head_size + 16 * NG) * sizeof(float);
+    const size_t ring = 2 * 2 * kStageBlocks * (size_t)head_size * kBlock * kv_elem_bytes(kv_cache_dtype);
+    const size_t stage = W * (16 * (size_t)head_size + 16) * sizeof(float);
+    const size_t lds = W == 1 ? (16 * NG * (size_t)head_size + 16 * NG) * sizeof(float)
+                              : (ring > stage ? ring : stage);
     hipStream_t st = as_stream(stream);
-    const bool fp8 = kv_cache_dtype == PA_KV_FP8_E4M3;
-#define PA_PREFILL(PATH, DD)                                                                   \
-    hipLaunchKernelGGL((pa_prefill_kernel<PATH<DD>, NG>), dim3((unsigned)grid), dim3(64), lds, st, \
-                       p, query_start_loc, tpu, q_tiles)
+    const dim3 g((unsigned)grid);
     if (head_size == 128) {
-        if (fp8) PA_PREFILL(MfmaPath8, 128);
-        else PA_PREFILL(MfmaPath, 128);
+        if (fp8)
+            hipLaunchKernelGGL((pa_prefill_wg_kernel<MfmaPath8<128>, NG, W8>), g, dim3(64 * W8), lds, st,
+                               p, query_start_loc, tpu, q_tiles);
+        else
+            hipLaunchKernelGGL((pa_prefill_kernel<MfmaPath<128>, NG>), g, dim3(64), lds, st,
+                               p, query_start_loc, tpu, q_tiles);
     } else {
-        if (fp8) PA_PREFILL(MfmaPath8, 64);
-        else PA_PREFILL(MfmaPath, 64);
+        if (fp8)
+            hipLaunchKernelGGL((pa_prefill_wg_kernel<MfmaPath8<64>, NG, W8>), g, dim3(64 * W8), lds, st,
+                               p, query_start_loc, tpu, q_tiles);
+        else
+            hipLaunchKernelGGL((pa_prefill_kernel<MfmaPath<64>, NG>), g, dim3(64), lds, st,
+                               p, query_start_loc, tpu, q_tiles);
     }
-#undef PA_PREFILL
     return launch_status();
 }

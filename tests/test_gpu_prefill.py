@@ -55,8 +55,10 @@ def test_prefill_matches_oracle(case):
     assert_parity(out, ref, case[0])
 
 
-@pytest.mark.parametrize("case", [CASES[0], CASES[2]], ids=["g4", "mha"])
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_prefill_fp8_matches_oracle(case):
+    """fp8 pools take the workgroup form (four waves sharing K/V stages through
+    LDS): every query-tile shape, the table-window crossing, extra tiles."""
     inp, lens, qsl, q = make(*case, seed=42)
     ks, vs = 0.03, 0.02
     k8 = logical_to_k8(fp8.quantize(k16_to_logical(inp.k_cache), ks))
@@ -64,7 +66,7 @@ def test_prefill_fp8_matches_oracle(case):
     dk, dv = fp8.dequantize_pools(k8, v8, ks, vs)
     ref = oracle.paged_prefill(q, dk, dv, inp.block_tables, lens, qsl, inp.scale, 16)
     out = run(q, to_dev(k8), to_dev(v8), inp.block_tables, lens, qsl, inp.scale,
-              int(max(case[5])), ks, vs)
+              int(max(case[5])) + 40, ks, vs)                  # extra workgroups exit at once
     assert_parity(out, ref, case[0] + " fp8")
 
 
@@ -118,3 +120,22 @@ def test_max_query_len_too_small_gives_nan_rows():
     assert np.isnan(out[24:60]).all()
     assert_parity(out[:24], ref[:24], "covered rows")
     assert_parity(out[60:], ref[60:], "other sequence")
+
+
+def test_fp8_invalid_shapes_give_nan_rows():
+    """The workgroup form's NaN rows: more queries than tokens, and more queries
+    than max_query_len allows for (4 waves x 8 tokens = 32 rows per tile)."""
+    inp, lens, qsl, q = make("bad8", 8, 2, 128, [10, 200, 90], [4, 70, 12], seed=47)
+    lens = np.array([3, 200, 90], np.int32)         # sequence 0: 4 queries, 3 tokens
+    ks, vs = 0.03, 0.02
+    k8 = logical_to_k8(fp8.quantize(k16_to_logical(inp.k_cache), ks))
+    v8 = fp8.quantize(inp.v_cache, vs)
+    dk, dv = fp8.dequantize_pools(k8, v8, ks, vs)
+    out = run(q, to_dev(k8), to_dev(v8), inp.block_tables, lens, qsl, inp.scale, 40, ks, vs)
+    assert np.isnan(out[:4]).all()
+    ref = oracle.paged_prefill(q[4:], dk, dv, inp.block_tables[1:], lens[1:], qsl[1:] - qsl[1],
+                               inp.scale, 16)
+    # sequence 1: rows 0..63 covered (2 tiles of 32), 64..69 NaN; sequence 2 whole
+    assert np.isnan(out[4 + 64:4 + 70]).all()
+    assert_parity(out[4:4 + 64], ref[:64], "covered rows")
+    assert_parity(out[4 + 70:], ref[70:], "other sequence")
