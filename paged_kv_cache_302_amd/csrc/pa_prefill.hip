@@ -58,6 +58,8 @@ constexpr int kStageBlocks = 4;   // blocks per LDS stage of the workgroup form
 // --------------------------------------------------------------------------
 template <class Base, int NG>
 struct MfmaGroups {
+    using Path = Base;
+    static constexpr int kNG = NG;
     static constexpr int D = Base::kD;
     static constexpr int KC = D / 32;
     static constexpr int NT = D / 16;
@@ -223,20 +225,69 @@ struct MfmaGroups {
         }
     }
 
-    // Rows of every group to LDS: s_acc[(16gr + i) * D + d] unnormalised,
-    // s_l[16gr + i] the column's weight sum (over its four token groups).
-    __device__ static void stage(const State& st, float* s_acc, float* s_l) {
-        const int l = lane_id(), i = l & 15, g = l >> 4;
+};
+
+
+// The (token, head) columns of one wave: lane column c = 16 gr + i is query
+// token j0 + c / gc and head c % gc of the chunk.  Loads the Q operands (zeros
+// for padding columns or a bad sequence) and each column's position.
+template <class G2>
+__device__ __forceinline__ void load_columns(typename G2::QRegs& qr, int (&pos)[G2::kNG],
+                                             bool (&col_ok)[G2::kNG], const f16* q, int num_heads,
+                                             int head0, int gc, int q0, int j0, int ntok, int L,
+                                             int nq, bool bad) {
+    constexpr int D = G2::D;
+    const int i = lane_id() & 15;
 #pragma unroll
-        for (int gr = 0; gr < NG; ++gr) {
-            const float ltot = col4_sum(st.l[gr]);
+    for (int gr = 0; gr < G2::kNG; ++gr) {
+        const int c = 16 * gr + i;
+        const int jj = c / gc;
+        col_ok[gr] = jj < ntok;
+        pos[gr] = L - nq + j0 + jj;
+        G2::Path::load_q_row(qr.q[gr], q + ((size_t)(q0 + j0 + jj) * num_heads + head0 + (c - jj * gc)) * D,
+                             col_ok[gr] && !bad);
+    }
+}
+
+// The wave's result rows, group by group through its LDS area s_o (16 D + 16
+// floats), then whole 16-byte stores (the heads of one token are one
+// contiguous run of gc D floats); NaN rows for a bad sequence.
+template <class G2>
+__device__ __forceinline__ void store_rows(const typename G2::State& st, float* s_o, float* out,
+                                           int num_heads, int head0, int gc, int q0, int j0,
+                                           int ntok, float v_scale, bool bad) {
+    constexpr int D = G2::D;
+    float* s_l = s_o + 16 * D;
+    const int cols = ntok * gc;
+    const f32x4* src = reinterpret_cast<const f32x4*>(s_o);
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-                *reinterpret_cast<f32x4*>(s_acc + (16 * gr + i) * D + 16 * nt + 4 * g) = st.acc[gr][nt];
-            if (g == 0) s_l[16 * gr + i] = ltot;
+    for (int gr = 0; gr < G2::kNG; ++gr) {
+        if (16 * gr >= cols) break;
+        G2::stage_group(st, gr, s_o, s_l);
+        const int cg = min(16, cols - 16 * gr);
+        for (int e = lane_id(); e < cg * (D / 4); e += 64) {
+            const int ci = (4 * e) / D;
+            const int c = 16 * gr + ci;
+            const int cj = c / gc;
+            f32x4 v = src[e] * (v_scale / s_l[ci]);
+            if (bad) v = f32x4{NAN, NAN, NAN, NAN};
+            float* orow = out + ((size_t)(q0 + j0 + cj) * num_heads + head0 + (c - cj * gc)) * D;
+            st_stream(reinterpret_cast<f32x4*>(orow) + (e - ci * (D / 4)), v);
         }
     }
-};
+}
+
+// Query rows covered + 0 .. nq - 1 of a sequence with more queries than the
+// grid's tiles cover: NaN for this unit's heads.
+template <int D>
+__device__ __forceinline__ void nan_rows(float* out, int num_heads, int head0, int gc, int q0,
+                                         int covered, int nq) {
+    const int per_row = gc * D;
+    for (int e = lane_id(); e < (nq - covered) * per_row; e += 64) {
+        const int r = e / per_row, hd = e - r * per_row;
+        out[((size_t)(q0 + covered + r) * num_heads + head0 + hd / D) * D + (hd % D)] = NAN;
+    }
+}
 
 template <class Path, int NG>
 __global__ __launch_bounds__(64) void pa_prefill_kernel(DecodeParams p,
@@ -262,22 +313,12 @@ __global__ __launch_bounds__(64) void pa_prefill_kernel(DecodeParams p,
     const int nb_seq = (L + kBlock - 1) / kBlock;
     bool bad = nq > L || nb_seq > p.max_blocks_per_seq;
 
-    // this lane's column in group gr: c = 16 gr + i -> token c / gc, head c % gc
-    const int i = lane_id() & 15;
+    const int head0 = kvh * p.group + hc * 16;
     const int pos_last = L - nq + j0 + ntok - 1;
     int pos[NG];
     bool col_ok[NG];
     typename G2::QRegs qr;
-#pragma unroll
-    for (int gr = 0; gr < NG; ++gr) {
-        const int c = 16 * gr + i;
-        const int jj = c / gc;
-        const int hh = kvh * p.group + hc * 16 + (c - jj * gc);
-        col_ok[gr] = jj < ntok;
-        pos[gr] = L - nq + j0 + jj;
-        Path::load_q_row(qr.q[gr], p.q + ((size_t)(q0 + j0 + jj) * p.num_heads + hh) * D,
-                         col_ok[gr] && !bad);
-    }
+    load_columns<G2>(qr, pos, col_ok, p.q, p.num_heads, head0, gc, q0, j0, ntok, L, nq, bad);
     typename G2::State st;
     G2::init(st);
 
@@ -342,33 +383,11 @@ __global__ __launch_bounds__(64) void pa_prefill_kernel(DecodeParams p,
         }
     }
 
-    // rows of the tile through LDS, then whole 16-byte stores per lane (the
-    // heads of one token are one contiguous run of gc*D floats)
-    float* s_o = lds;                 // [16 NG][D]
-    float* s_l = lds + 16 * NG * D;   // [16 NG]
-    G2::stage(st, s_o, s_l);
-    const f32x4* src = reinterpret_cast<const f32x4*>(s_o);
-    const int cols = ntok * gc;       // valid columns: 0 .. cols-1
-    for (int e = lane_id(); e < cols * (D / 4); e += 64) {
-        const int c = (4 * e) / D;
-        const int cj = c / gc;
-        const int ch = kvh * p.group + hc * 16 + (c - cj * gc);
-        f32x4 v = src[e] * (p.v_scale / s_l[c]);
-        if (bad) v = f32x4{NAN, NAN, NAN, NAN};
-        float* orow = p.out + ((size_t)(q0 + j0 + cj) * p.num_heads + ch) * D;
-        st_stream(reinterpret_cast<f32x4*>(orow) + (e - c * (D / 4)), v);
-    }
-    // more queries than max_query_len allowed for: the rows no tile covers get
-    // NaN from the sequence's last tile (for this unit's heads)
-    const int covered = q_tiles * tpu;
-    if (qt == q_tiles - 1 && nq > covered) {
-        const int per_row = gc * D;
-        for (int e = lane_id(); e < (nq - covered) * per_row; e += 64) {
-            const int r = e / per_row, hd = e - r * per_row;
-            const int hh = kvh * p.group + hc * 16 + hd / D;
-            p.out[((size_t)(q0 + covered + r) * p.num_heads + hh) * D + (hd % D)] = NAN;
-        }
-    }
+    store_rows<G2>(st, lds, p.out, p.num_heads, head0, gc, q0, j0, ntok, p.v_scale, bad);
+    // more queries than max_query_len allowed for: the sequence's last tile
+    // sets the rows no tile covers to NaN
+    if (qt == q_tiles - 1 && nq > q_tiles * tpu)
+        nan_rows<D>(p.out, p.num_heads, head0, gc, q0, q_tiles * tpu, nq);
 }
 
 
@@ -436,20 +455,11 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     const int nb_seq = (L + kBlock - 1) / kBlock;
     bool bad = nq > L || nb_seq > p.max_blocks_per_seq;
 
-    const int i = lane_id() & 15;
+    const int head0 = kvh * p.group + hc * 16;
     int pos[NG];
     bool col_ok[NG];
     typename G2::QRegs qr;
-#pragma unroll
-    for (int gr = 0; gr < NG; ++gr) {
-        const int c = 16 * gr + i;
-        const int jj = c / gc;
-        const int hh = kvh * p.group + hc * 16 + (c - jj * gc);
-        col_ok[gr] = jj < ntok;
-        pos[gr] = L - nq + j0 + jj;
-        Path::load_q_row(qr.q[gr], p.q + ((size_t)(q0 + j0 + jj) * p.num_heads + hh) * D,
-                         col_ok[gr] && !bad);
-    }
+    load_columns<G2>(qr, pos, col_ok, p.q, p.num_heads, head0, gc, q0, j0, ntok, L, nq, bad);
     typename G2::State st;
     G2::init(st);
 
@@ -562,38 +572,14 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
 #undef PA_COMMIT
     }
 
-    // per wave and group: rows through LDS, then whole 16-byte stores
-    float* s_o = reinterpret_cast<float*>(smem) + wave * (16 * D + 16);
-    float* s_l = s_o + 16 * D;
-    const int cols = ntok * gc;
-    const f32x4* src = reinterpret_cast<const f32x4*>(s_o);
-#pragma unroll
-    for (int gr = 0; gr < NG; ++gr) {
-        if (16 * gr >= cols) break;
-        G2::stage_group(st, gr, s_o, s_l);
-        const int cg = min(16, cols - 16 * gr);
-        for (int e = lane_id(); e < cg * (D / 4); e += 64) {
-            const int ci = (4 * e) / D;
-            const int c = 16 * gr + ci;
-            const int cj = c / gc;
-            const int ch = kvh * p.group + hc * 16 + (c - cj * gc);
-            f32x4 v = src[e] * (p.v_scale / s_l[ci]);
-            if (bad) v = f32x4{NAN, NAN, NAN, NAN};
-            float* orow = p.out + ((size_t)(q0 + j0 + cj) * p.num_heads + ch) * D;
-            st_stream(reinterpret_cast<f32x4*>(orow) + (e - ci * (D / 4)), v);
-        }
-    }
-    // more queries than max_query_len allowed for: the last workgroup of the
-    // sequence sets the uncovered rows (this unit's heads) to NaN
-    const int covered = q_tiles * W * tpu;
-    if (qt == q_tiles - 1 && wave == 0 && nq > covered) {
-        const int per_row = gc * D;
-        for (int e = lane_id(); e < (nq - covered) * per_row; e += 64) {
-            const int r = e / per_row, hd = e - r * per_row;
-            const int hh = kvh * p.group + hc * 16 + hd / D;
-            p.out[((size_t)(q0 + covered + r) * p.num_heads + hh) * D + (hd % D)] = NAN;
-        }
-    }
+    // per wave: its rows through its own LDS area (the ring is free after the
+    // last barrier)
+    store_rows<G2>(st, reinterpret_cast<float*>(smem) + wave * (16 * D + 16), p.out, p.num_heads,
+                   head0, gc, q0, j0, ntok, p.v_scale, bad);
+    // more queries than max_query_len allowed for: the sequence's last
+    // workgroup sets the rows no tile covers to NaN
+    if (qt == q_tiles - 1 && wave == 0 && nq > q_tiles * W * tpu)
+        nan_rows<D>(p.out, p.num_heads, head0, gc, q0, q_tiles * W * tpu, nq);
 }
 
 }  // namespace pa
@@ -632,8 +618,7 @@ extern "C" int pa_prefill(float* out, const void* q, const void* k_cache, const 
     if (grid > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
     const size_t ring = 2 * 2 * kStageBlocks * (size_t)head_size * kBlock * kv_elem_bytes(kv_cache_dtype);
     const size_t stage = W * (16 * (size_t)head_size + 16) * sizeof(float);
-    const size_t lds = W == 1 ? (16 * NG * (size_t)head_size + 16 * NG) * sizeof(float)
-                              : (ring > stage ? ring : stage);
+    const size_t lds = W == 1 ? stage : (ring > stage ? ring : stage);
     hipStream_t st = as_stream(stream);
     const dim3 g((unsigned)grid);
     if (head_size == 128) {
