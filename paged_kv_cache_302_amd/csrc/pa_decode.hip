@@ -51,6 +51,7 @@
 // gets exactly 1 and a one-token sequence returns its V bit-exactly.
 #include <math.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "pa_device.h"
@@ -64,39 +65,60 @@
 #ifndef PA_V1_WAVES
 #define PA_V1_WAVES 0         // waves per v1 workgroup (0 = heuristic)
 #endif
-#ifndef PA_UNIT_ORDER
-#define PA_UNIT_ORDER 0       // v2 grid order: 0 = KV heads fastest, 1 = partitions fastest
-#endif
 
 namespace pa {
 
 // --------------------------------------------------------------------------
-// v2 unit lookup: the r-th existing partition, counting sequences in order
-// and partitions p < ceil(L_s / PS) (capped at max_num_partitions).
+// v2 unit order.  The existing partitions (p < ceil(L_s / PS), capped at
+// max_num_partitions) are numbered largest first: every full partition in
+// (sequence, partition) order, then each sequence's partly filled last
+// partition by decreasing block count, ties in sequence order (when the
+// whole grid fits on the device at once; otherwise (sequence, partition)
+// order).
+// Workgroups that run at the same time are spread round robin over the CUs
+// (workgroup b lands on CU b mod #CUs), and a CU's units share its memory
+// path; the kernel takes consecutive ranks in a snake over the CUs (forward,
+// then backward inside each XCD), so the CUs that got one more full unit get
+// the smallest tails and every CU ends up with about the same number of
+// blocks.  With more than 64 blocks per partition the tails are not sorted.
 // --------------------------------------------------------------------------
+// MI355X places consecutive workgroups on its 8 XCDs in turn.
+constexpr int kXcds = 8;
+
 __device__ __forceinline__ int n_parts(int L, int PS, int Pmax) {
     if (L <= 0) return 0;
     const int n = (L - 1) / PS + 1;
     return n < Pmax ? n : Pmax;
 }
 
-__device__ int total_partitions(const DecodeParams& p) {
-    int total = 0;
-    for (int s0 = 0; s0 < p.num_seqs; s0 += 64) {
-        const int s = s0 + lane_id();
-        float np = (s < p.num_seqs) ? (float)n_parts(p.seq_lens[s], p.partition_size, p.max_num_partitions) : 0.f;
-        total += (int)wave_sum(np);
-    }
-    return __builtin_amdgcn_readfirstlane(total);
+struct SeqParts {
+    int len;    // L_s (0 past the last sequence)
+    int np;     // partitions enumerated
+    int tail;   // blocks of the last partition when it is partly filled, else 0
+};
+
+__device__ __forceinline__ SeqParts seq_parts(const DecodeParams& p, int s, int PB, bool sorted) {
+    SeqParts r;
+    r.len = s < p.num_seqs ? p.seq_lens[s] : 0;
+    r.np = n_parts(r.len, p.partition_size, p.max_num_partitions);
+    const int nb = r.len > 0 ? (r.len - 1) / kBlock + 1 : 0;
+    const int last = nb - (r.np - 1) * PB;   // blocks of partition np - 1 (if not capped)
+    const bool capped = r.len > 0 && (r.len - 1) / p.partition_size + 1 > r.np;
+    r.tail = (sorted && r.np > 0 && !capped && last < PB) ? last : 0;
+    return r;
 }
 
-__device__ bool find_partition(const DecodeParams& p, int r, int& s_out, int& p_out) {
+__device__ bool find_partition(const DecodeParams& p, int r, bool sort_tails, int& s_out,
+                               int& p_out, int& L_out) {
     const int lane = lane_id();
-    int base = 0;  // partitions of the sequences before this chunk (uniform)
+    const int PB = p.partition_size / kBlock;
+    const bool sorted = sort_tails && PB <= 64;
+    // 1. full partitions (every partition when the tails are not sorted)
+    int base = 0;
     for (int s0 = 0; s0 < p.num_seqs; s0 += 64) {
-        const int s = s0 + lane;
-        const int np = (s < p.num_seqs) ? n_parts(p.seq_lens[s], p.partition_size, p.max_num_partitions) : 0;
-        int incl = np;
+        const SeqParts q = seq_parts(p, s0 + lane, PB, sorted);
+        const int nfull = q.np - (q.tail > 0 ? 1 : 0);
+        int incl = nfull;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
             const int t = __shfl_up(incl, off);
@@ -106,12 +128,52 @@ __device__ bool find_partition(const DecodeParams& p, int r, int& s_out, int& p_
         if (r < base + total) {
             const unsigned long long mask = __ballot(base + incl > r);
             const int first = __ffsll((long long)mask) - 1;
-            const int excl = __builtin_amdgcn_readlane(incl - np, first);
             s_out = s0 + first;
-            p_out = r - base - excl;
+            p_out = r - base - __builtin_amdgcn_readlane(incl - nfull, first);
+            // the length came with the prefix sum: no second, dependent load
+            L_out = __builtin_amdgcn_readlane(q.len, first);
             return true;
         }
         base += total;
+    }
+    if (!sorted) return false;
+    // 2. tails: lane c counts the tails of c blocks (1 <= c < PB <= 64)
+    int j = r - base;
+    int hist = 0;
+    for (int s0 = 0; s0 < p.num_seqs; s0 += 64) {
+        const SeqParts q = seq_parts(p, s0 + lane, PB, true);
+        for (int c = 1; c < PB; ++c) {
+            const int cnt = __popcll(__ballot(q.tail == c));
+            if (lane == c) hist += cnt;
+        }
+    }
+    // tails of more than c blocks come before class c: a suffix sum over lanes
+    int incl = hist;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_down(incl, off);
+        if (lane + off < 64) incl += t;
+    }
+    const int above = incl - hist;
+    const unsigned long long hit = __ballot(lane >= 1 && lane < PB && j >= above && j < above + hist);
+    if (hit == 0) return false;
+    const int cls = __ffsll((long long)hit) - 1;
+    j -= __builtin_amdgcn_readlane(above, cls);
+    // 3. the j-th sequence (in order) whose tail has cls blocks
+    for (int s0 = 0; s0 < p.num_seqs; s0 += 64) {
+        const SeqParts q = seq_parts(p, s0 + lane, PB, true);
+        const unsigned long long m = __ballot(q.tail == cls);
+        const int pc = __popcll(m);
+        if (j < pc) {
+            const int below = __popcll(m & ((1ull << lane) - 1ull));
+            const unsigned long long pick = __ballot(q.tail == cls && below == j);
+            const int first = __ffsll((long long)pick) - 1;
+            s_out = s0 + first;
+            p_out = __builtin_amdgcn_readlane(q.np, first) - 1;
+            L_out = __builtin_amdgcn_readlane(q.len, first);
+            return true;
+        }
+        j -= pc;
     }
     return false;
 }
@@ -131,34 +193,33 @@ void pa_decode_kernel(DecodeParams p) {
     extern __shared__ float lds[];
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index, uniform
     const int kvhc_count = p.num_kv_heads * p.head_chunks;
-#if PA_UNIT_ORDER == 1
-    int kvhc, r_unit;
+    int u = blockIdx.x;
+    bool sorted = false;   // v2: largest-first order with the snake over the CUs
     if constexpr (V2) {
-        const int R = total_partitions(p);
-        if ((int)blockIdx.x >= R * kvhc_count) return;
-        kvhc = blockIdx.x / R;
-        r_unit = blockIdx.x % R;
-    } else {
-        kvhc = blockIdx.x % kvhc_count;
-        r_unit = blockIdx.x / kvhc_count;
+        sorted = p.resident > 0;
+        if (sorted) {
+            // a backward round reverses the CUs inside each XCD (workgroups
+            // alternate over the 8 XCDs), so a unit keeps its XCD and L2
+            const int per = p.unit_period, k = u / per, c = u - k * per;
+            const bool back = (k & 1) && per >= kXcds;   // period 1: plain order
+            u = k * per + (back ? per - kXcds - (c & ~(kXcds - 1)) + (c & (kXcds - 1)) : c);
+        }
     }
-#else
-    const int kvhc = blockIdx.x % kvhc_count;
-    const int r_unit = blockIdx.x / kvhc_count;
-#endif
+    const int kvhc = u % kvhc_count;
+    const int r_unit = u / kvhc_count;
     const int kvh = kvhc / p.head_chunks;
     const int hc = kvhc - kvh * p.head_chunks;
     const int h0 = kvh * p.group + hc * Path::kHeads;
     const int nh_left = p.group - hc * Path::kHeads;
     const int nh = nh_left < Path::kHeads ? nh_left : Path::kHeads;
 
-    int s, part = 0;
+    int s, part = 0, L;
     if constexpr (V2) {
-        if (!find_partition(p, r_unit, s, part)) return;
+        if (!find_partition(p, r_unit, sorted, s, part, L)) return;
     } else {
         s = r_unit;
+        L = p.seq_lens[s];
     }
-    const int L = p.seq_lens[s];
     // v1 out[S][H][D]; v2 tmp_out[S][P][H][D]: either way the unit's heads
     // are consecutive rows, so its result is one contiguous run of memory
     const size_t out_head_stride = D;
@@ -166,20 +227,41 @@ void pa_decode_kernel(DecodeParams p) {
                            : (size_t)s * p.num_heads + h0;
     float* out_h0 = p.out + row0 * D;   // exp_sums / max_logits [S][P][H]: index row0 + j
 
-    if (!V2 && L <= 0) {  // empty sequence: zeros (v2 has no partition for it)
-        for (int e = threadIdx.x; e < nh * D; e += 64 * NW)
-            st_stream(out_h0 + (size_t)(e / D) * out_head_stride + (e % D), 0.f);
-        return;
-    }
-    const int nb_seq = (L + kBlock - 1) / kBlock;
-    bool bad = nb_seq > p.max_blocks_per_seq;
+    // Everything that depends only on (s, first block) is requested before
+    // the length is used: the query, the first two table windows (bounded by
+    // the row, not by the length) and the load-policy check.  In v1 these go
+    // out together with the length load, so the first tile waits on one
+    // round trip instead of two or three.
+    const int pb = V2 ? p.partition_size / kBlock : 0;
+    const int blk_begin = V2 ? part * pb : 0;
+    const int first = blk_begin + w;       // this wave's blocks: first + k*NW, k < n
+    const int32_t* row = p.block_tables + (size_t)s * p.max_blocks_per_seq;
+    const int mbps = p.max_blocks_per_seq;
+    const int n_req = first < mbps ? (mbps - first + NW - 1) / NW : 1;
+    int cur = table_window<NW>(row, first, n_req, 0, mbps);
+    int nxt = table_window<NW>(row, first, n_req, 64, mbps);
+#if PA_LOAD_POLICY == 1
+    const NeighbourIds nbr = neighbour_ids(p, s, blk_begin);
+#endif
+    typename Path::QRegs qr;
+    Path::load_q(qr, p, s, h0, nh);
+    // keep the scheduler from placing a use (and so a wait) between the loads
+    __builtin_amdgcn_sched_barrier(0);
+#if PA_LOAD_POLICY == 1
+    const bool cached = shared_unit(nbr);
+#endif
+
+    // No branch on L until the first tile request, so the compiler keeps the
+    // loads above where they are: an empty v1 sequence (L <= 0; v2 has no
+    // partition for it) walks no block and writes zeros.
+    const bool empty = !V2 && L <= 0;
+    const int nb_seq = empty ? 0 : (L + kBlock - 1) / kBlock;
+    bool bad = nb_seq > mbps;
     if constexpr (V2) bad = bad || (L - 1) / p.partition_size + 1 > p.max_num_partitions;
 
     // token / block range of this unit
-    int tok_end = L, blk_begin = 0, blk_end = nb_seq;
+    int tok_end = L, blk_end = nb_seq;
     if constexpr (V2) {
-        const int pb = p.partition_size / kBlock;
-        blk_begin = part * pb;
         blk_end = min(nb_seq, blk_begin + pb);
         tok_end = min(L, (part + 1) * p.partition_size);
     }
@@ -187,20 +269,15 @@ void pa_decode_kernel(DecodeParams p) {
 
     typename Path::State st;
     Path::init(st);
-    typename Path::QRegs qr;
-    Path::load_q(qr, p, s, h0, nh);
 
-    // this wave's blocks: blk_begin + w + k*NW, k < n
-    const int first = blk_begin + w;
     const int n = first < blk_end ? (blk_end - first + NW - 1) / NW : 0;
     constexpr int TB = D * kBlock * Path::kElem;           // bytes of one K or V tile
     const char* kbase = p.k_cache + (size_t)kvh * TB;
     const char* vbase = p.v_cache + (size_t)kvh * TB;
     const size_t blk_stride = (size_t)p.num_kv_heads * TB;
-    const int32_t* row = p.block_tables + (size_t)s * p.max_blocks_per_seq;
     const float sl2 = p.scale_log2;
 
-    if (n > 0) {
+    {
         // The wave walks its blocks in windows of 64 table entries: `cur` holds
         // window kw, `nxt` window kw + 64 (requested one window ahead), and
         // `pend` window kw + 128 (requested as window kw starts, so it has had
@@ -215,14 +292,13 @@ void pa_decode_kernel(DecodeParams p) {
         // The table index is clamped rather than the previous id kept, so the
         // compiler cannot prove two requests equal and replace one by a
         // register copy (which would drain the load queue).  An id outside
-        // the pool marks the unit bad and reads block 0.
-        int cur = table_window<NW>(row, first, n, 0);
-        int nxt = table_window<NW>(row, first, n, 64);
+        // the pool marks the unit bad and reads block 0.  A wave with no
+        // block (n == 0) makes one empty request and processes nothing.
         auto phys = [&](int kw, int j) {
-            const int d = min(j, n - 1) - kw;
+            const int d = max(min(j, n - 1), 0) - kw;
             const int v = d < 64 ? __builtin_amdgcn_readlane(cur, d) : __builtin_amdgcn_readlane(nxt, d - 64);
             const bool ok = (unsigned)v < (unsigned)p.num_blocks;
-            bad = bad || !ok;
+            bad = bad || (!ok && n > 0);   // with no block the entry is not the unit's
             return ok ? v : 0;
         };
         auto tile_k = [&](int id) { return kbase + (size_t)id * blk_stride; };
@@ -233,10 +309,10 @@ void pa_decode_kernel(DecodeParams p) {
             constexpr bool NTL = decltype(nt_tag)::value;
             typename Path::Tile ta, tb;
             int id = phys(0, 0);
-            Path::template load<NTL>(ta, tile_k(id), tile_v(id), TB);
+            Path::template load<NTL>(ta, tile_k(id), tile_v(id), live(0));
             int k = 0;
             for (int kw = 0;; kw += 64) {
-                const int pend = table_window<NW>(row, first, n, kw + 128);
+                const int pend = table_window<NW>(row, first, n, kw + 128, mbps);
                 const int kend = min(n, kw + 64) & ~1;   // pairs; an odd last block is the tail
                 for (; k < kend; k += 2) {
                     id = phys(kw, k + 1);
@@ -253,7 +329,7 @@ void pa_decode_kernel(DecodeParams p) {
             if (k < n) Path::process(st, ta, qr, valid(k), sl2);   // odd block count
         };
 #if PA_LOAD_POLICY == 1
-        if (shared_unit(p, s, blk_begin)) walk(std::false_type{});   // cached loads
+        if (cached) walk(std::false_type{});   // cached loads
         else walk(std::true_type{});
 #else
         walk(std::integral_constant<bool, PA_LOAD_POLICY == 2>{});
@@ -275,7 +351,7 @@ void pa_decode_kernel(DecodeParams p) {
         const f32x4* src = reinterpret_cast<const f32x4*>(s_o);
         const int nv = nh * D / 4;
         for (int e = lane_id(); e < nv; e += 64) {
-            const float inv = p.v_scale / s_l[(4 * e) / D];
+            const float inv = empty ? 0.f : p.v_scale / s_l[(4 * e) / D];
             f32x4 v = src[e] * inv;
             if (bad) v = f32x4{NAN, NAN, NAN, NAN};
             st_stream(reinterpret_cast<f32x4*>(out_h0) + e, v);
@@ -315,7 +391,8 @@ void pa_decode_kernel(DecodeParams p) {
                 num += s_acc[(v * nh + j) * D + d] * f;
                 den += s_l[v * HP + j] * f;
             }
-            st_stream(out_h0 + (size_t)j * out_head_stride + d, any_bad ? NAN : num / den * p.v_scale);
+            const float o = empty ? 0.f : num / den * p.v_scale;
+            st_stream(out_h0 + (size_t)j * out_head_stride + d, any_bad ? NAN : o);
             if (V2 && d == 0) {
                 s_fin[j] = M;
                 s_fin[16 + j] = den;
@@ -342,10 +419,33 @@ static size_t merge_lds_bytes(int NW, int nh_max, int D, int hp) {
 }
 
 template <class Path, int D, bool V2>
-static int launch_nw(int NW, const DecodeParams& p, int grid, int nh_max, hipStream_t st) {
+static int launch_nw(int NW, const DecodeParams& p0, int grid, int nh_max, hipStream_t st) {
     // keep the merge buffer within the default 64 KiB of dynamic LDS
     while (NW > 1 && merge_lds_bytes(NW, nh_max, D, Path::kHeads) > 65536) NW /= 2;
     const size_t lds = merge_lds_bytes(NW, nh_max, D, Path::kHeads);
+    DecodeParams p = p0;
+    const void* fn = nullptr;
+    switch (NW) {
+        case 1: fn = reinterpret_cast<const void*>(&pa_decode_kernel<Path, D, 1, V2>); break;
+        case 2: fn = reinterpret_cast<const void*>(&pa_decode_kernel<Path, D, 2, V2>); break;
+        case 4: fn = reinterpret_cast<const void*>(&pa_decode_kernel<Path, D, 4, V2>); break;
+        case 8: fn = reinterpret_cast<const void*>(&pa_decode_kernel<Path, D, 8, V2>); break;
+        default: return PA_ERR_INVALID_ARG;
+    }
+    if (V2) {
+        // Only when the whole grid is resident at once does the placement fix
+        // each CU's share: then the kernel takes the balanced unit order.
+        // With more units the dispatcher balances the CUs itself as slots
+        // free up, and the plain order keeps the units that share blocks
+        // (forks, samples of one prompt) running together.
+        int per_cu = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64 * NW, lds) != hipSuccess) {
+            (void)hipGetLastError();
+            per_cu = 0;
+        }
+        const long long resident = (long long)per_cu * p.num_cus;
+        p.resident = grid <= resident ? (int)resident : 0;
+    }
     switch (NW) {
         case 1: hipLaunchKernelGGL((pa_decode_kernel<Path, D, 1, V2>), dim3(grid), dim3(64), lds, st, p); break;
         case 2: hipLaunchKernelGGL((pa_decode_kernel<Path, D, 2, V2>), dim3(grid), dim3(128), lds, st, p); break;
@@ -373,6 +473,26 @@ static int launch_decode(const DecodeParams& p, int head_size, bool fp8, int NW,
                     : launch_nw<ValuPath<128>, 128, V2>(NW, p, grid, nh_max, st);
     return mfma ? launch_nw<MfmaPath<64>, 64, V2>(NW, p, grid, nh_max, st)
                 : launch_nw<ValuPath<64>, 64, V2>(NW, p, grid, nh_max, st);
+}
+
+// Compute units of the device that runs `stream` (cached per device; 0 if
+// it cannot be read).
+static int compute_units(void* stream) {
+    static std::atomic<int> cache[64];
+    hipDevice_t dev = 0;
+    if (hipStreamGetDevice(as_stream(stream), &dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    if (dev < 0 || dev >= 64) return 0;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 0) {
+        (void)hipGetLastError();
+        n = 0;
+    }
+    if (n > 0) cache[dev].store(n, std::memory_order_relaxed);
+    return n;
 }
 
 // Waves per workgroup.  Each wave keeps two K/V tiles in flight, so
@@ -446,11 +566,15 @@ extern "C" int pa_decode_v2(float* tmp_out, float* exp_sums, float* max_logits, 
     p.max_logits = max_logits;
     p.max_num_partitions = max_num_partitions;
     p.partition_size = partition_size;
+    // the grid covers whole snake rounds; workgroups past the real units exit
+    p.num_cus = compute_units(stream);
+    p.unit_period = p.num_cus > 0 && p.num_cus % kXcds == 0 ? p.num_cus : 1;
     const long long units = (long long)num_seqs * num_kv_heads * p.head_chunks * max_num_partitions;
-    if (units > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
+    const long long grid = (units + p.unit_period - 1) / p.unit_period * p.unit_period;
+    if (grid > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
     // a sequence has on average about half of max_num_partitions partitions
     const bool fp8 = kv_cache_dtype == PA_KV_FP8_E4M3;
     const int nw = PA_V2_WAVES ? PA_V2_WAVES
                                : pick_waves(units / 2, partition_size / 16, head_size, fp8 ? 1 : 2);
-    return launch_decode<true>(p, head_size, fp8, nw, (int)units, as_stream(stream));
+    return launch_decode<true>(p, head_size, fp8, nw, (int)grid, as_stream(stream));
 }

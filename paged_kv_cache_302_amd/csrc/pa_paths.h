@@ -81,6 +81,9 @@ struct DecodeParams {
     int max_blocks_per_seq;
     int num_blocks;
     int max_num_partitions;
+    int unit_period;      // v2: compute units the unit order snakes over (1 = plain order)
+    int num_cus;          // compute units of the device (0 = unknown)
+    int resident;         // v2: >0 when the device holds the whole grid at once
     int partition_size;   // tokens, multiple of 16 (v2)
     float scale;          // natural units (fp8: scale * k_scale)
     float scale_log2;     // scale * log2(e)
@@ -92,12 +95,15 @@ struct DecodeParams {
 // first + k*NW) have their physical ids cached 64 at a time in one VGPR
 // (lane j of window i holds entry 64i + j, clamped to the last entry) and are
 // read back with v_readlane.  Every lane always loads, so a window is a plain
-// unconditional load with nothing to merge afterwards.
+// unconditional load with nothing to merge afterwards.  `n` only bounds what
+// is loaded (lanes past it repeat an earlier entry) and may exceed the
+// wave's real block count; the index never leaves the row [0, row_len).
 // --------------------------------------------------------------------------
 template <int NW>
-__device__ __forceinline__ int table_window(const int32_t* row, int first, int n, int kbase) {
-    const int k = min(kbase + lane_id(), n - 1);
-    return row[first + k * NW];
+__device__ __forceinline__ int table_window(const int32_t* row, int first, int n, int kbase,
+                                            int row_len) {
+    const int k = max(min(kbase + lane_id(), n - 1), 0);
+    return row[min(first + k * NW, row_len - 1)];
 }
 
 // --------------------------------------------------------------------------
@@ -145,9 +151,14 @@ struct MfmaPath {
             qr.q[c] = ok ? *reinterpret_cast<const f16x8*>(row + 32 * c + 8 * g) : z;
         }
     }
+    // Rows past the unit's heads load the last real row and are zeroed
+    // afterwards, so the loads are not under a branch and go out at once.
     __device__ static void load_q(QRegs& qr, const DecodeParams& p, int s, int h0, int nh) {
         const int i = lane_id() & 15;
-        load_q_row(qr, p.q + ((size_t)s * p.num_heads + h0 + i) * D, i < nh);
+        load_q_row(qr, p.q + ((size_t)s * p.num_heads + h0 + min(i, nh - 1)) * D, true);
+        const f16x8 z = {};
+#pragma unroll
+        for (int c = 0; c < KC; ++c) qr.q[c] = i < nh ? qr.q[c] : z;
     }
 
     __device__ static void init(State& st) {
@@ -378,9 +389,14 @@ struct MfmaPath8 : MfmaPath<D> {
             qr.q[c] = ok ? *reinterpret_cast<const f16x8*>(row + d0) : z;
         }
     }
+    // Rows past the unit's heads load the last real row and are zeroed
+    // afterwards, so the loads are not under a branch and go out at once.
     __device__ static void load_q(QRegs& qr, const DecodeParams& p, int s, int h0, int nh) {
         const int i = lane_id() & 15;
-        load_q_row(qr, p.q + ((size_t)s * p.num_heads + h0 + i) * D, i < nh);
+        load_q_row(qr, p.q + ((size_t)s * p.num_heads + h0 + min(i, nh - 1)) * D, true);
+        const f16x8 z = {};
+#pragma unroll
+        for (int c = 0; c < KC; ++c) qr.q[c] = i < nh ? qr.q[c] : z;
     }
 
     template <bool NTL>
@@ -556,14 +572,38 @@ struct ValuPath8 {
 // each other).  Only the first block is compared: a shared prefix is a
 // leading run of blocks.
 // --------------------------------------------------------------------------
-__device__ __forceinline__ bool shared_unit(const DecodeParams& p, int s, int blk) {
+// The check is split in two so that its loads can be issued together with
+// the unit's other first loads and its answer taken only when needed.
+struct NeighbourIds {
+    int b0, bp, bn;   // the unit's first block id and the neighbours' entries there
+    int lp, ln;       // the neighbours' lengths
+    int blk;
+    bool has_p, has_n;
+};
+
+__device__ __forceinline__ NeighbourIds neighbour_ids(const DecodeParams& p, int s, int blk) {
     const int32_t* bt = p.block_tables;
     const size_t w = (size_t)p.max_blocks_per_seq;
-    const int b0 = bt[(size_t)s * w + blk];
-    bool shared = false;
-    if (s > 0 && blk * kBlock < p.seq_lens[s - 1]) shared = bt[(size_t)(s - 1) * w + blk] == b0;
-    if (s + 1 < p.num_seqs && blk * kBlock < p.seq_lens[s + 1])
-        shared = shared || bt[(size_t)(s + 1) * w + blk] == b0;
+    NeighbourIds r;
+    r.blk = min(blk, p.max_blocks_per_seq - 1);
+    r.has_p = s > 0;
+    r.has_n = s + 1 < p.num_seqs;
+    const int sp = r.has_p ? s - 1 : s;
+    const int sn = r.has_n ? s + 1 : s;
+    // five independent loads (one round trip); neighbours' entries past their
+    // lengths are read but not used
+    r.b0 = bt[(size_t)s * w + r.blk];
+    r.bp = bt[(size_t)sp * w + r.blk];
+    r.bn = bt[(size_t)sn * w + r.blk];
+    r.lp = p.seq_lens[sp];
+    r.ln = p.seq_lens[sn];
+    return r;
+}
+
+__device__ __forceinline__ bool shared_unit(const NeighbourIds& r) {
+    // bitwise, not short-circuit: no branch between the loads and their use
+    const bool shared = (r.has_p & (r.blk * kBlock < r.lp) & (r.bp == r.b0)) |
+                        (r.has_n & (r.blk * kBlock < r.ln) & (r.bn == r.b0));
     return __builtin_amdgcn_readfirstlane((int)shared) != 0;
 }
 
@@ -612,6 +652,9 @@ inline DecodeParams make_params(const void* q, const void* k_cache, const void* 
     p.group = num_heads / num_kv_heads;
     p.head_chunks = p.group >= 2 ? (p.group + 15) / 16 : 1;
     p.max_blocks_per_seq = max_blocks_per_seq;
+    p.unit_period = 1;
+    p.num_cus = 0;
+    p.resident = 0;
     p.num_blocks = num_blocks;
     p.scale = scale;
     p.scale_log2 = scale * kLog2e;

@@ -333,8 +333,8 @@ __global__ __launch_bounds__(64) void pa_prefill_kernel(DecodeParams p,
     if (n > 0) {
         // the same walk as the decode kernels (table windows of 64 entries,
         // paired tiles, a zero-size request past the last block)
-        int cur = table_window<1>(row, 0, n, 0);
-        int nxt = table_window<1>(row, 0, n, 64);
+        int cur = table_window<1>(row, 0, n, 0, p.max_blocks_per_seq);
+        int nxt = table_window<1>(row, 0, n, 64, p.max_blocks_per_seq);
         auto phys = [&](int kw, int j) {
             const int d = min(j, n - 1) - kw;
             const int v = d < 64 ? __builtin_amdgcn_readlane(cur, d) : __builtin_amdgcn_readlane(nxt, d - 64);
@@ -361,7 +361,7 @@ __global__ __launch_bounds__(64) void pa_prefill_kernel(DecodeParams p,
         G2::template load<false>(ta, tile_k(id), tile_v(id), TB);
         int k = 0;
         for (int kw = 0;; kw += 64) {
-            const int pend = table_window<1>(row, 0, n, kw + 128);
+            const int pend = table_window<1>(row, 0, n, kw + 128, p.max_blocks_per_seq);
             const int kend = min(n, kw + 64) & ~1;
             for (; k < kend; k += 2) {
                 id = phys(kw, k + 1);
@@ -475,9 +475,9 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
 
     if (n > 0) {
         int kw = 0;                                // cur: blocks [kw, kw + 64), nxt the next 64
-        int cur = table_window<1>(row, 0, n, 0);
-        int nxt = table_window<1>(row, 0, n, 64);
-        int pend = table_window<1>(row, 0, n, 128);
+        int cur = table_window<1>(row, 0, n, 0, p.max_blocks_per_seq);
+        int nxt = table_window<1>(row, 0, n, 64, p.max_blocks_per_seq);
+        int pend = table_window<1>(row, 0, n, 128, p.max_blocks_per_seq);
         const unsigned num_blocks = (unsigned)p.num_blocks;
         const int nst = (n + SB - 1) / SB;
         u32x4 stg[CPT];
@@ -534,7 +534,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
                 kw += 64;
                 cur = nxt;
                 nxt = pend;
-                pend = table_window<1>(row, 0, n, kw + 128);
+                pend = table_window<1>(row, 0, n, kw + 128, p.max_blocks_per_seq);
             }
             if (j + 1 < nst) {
                 PA_FETCH(j + 1)
