@@ -32,6 +32,15 @@ REDUCE_CASES = [
     ("parts40_d128", 3, 4, 4, 128, 900, 1300, 32),
     ("parts325_d64", 2, 8, 2, 64, 3000, 5200, 16),
 ]
+# v2 unit order: grids the device holds at once take the largest-first order;
+# 200 sequences span four 64-lane chunks of its lookup, 128-block partitions
+# leave the partly filled ones unsorted, and 1,200 sequences x 8 partitions
+# exceed what the device holds (plain order)
+ORDER_CASES = [
+    ("order_200seqs", 200, 8, 2, 64, 1, 700, 128),
+    ("order_ps2048", 3, 8, 2, 128, 1, 5000, 2048),
+    ("order_big_grid", 1200, 8, 2, 64, 1, 1000, 128),
+]
 
 
 def make_case(case, seed):
@@ -84,7 +93,8 @@ def test_v1_matches_oracle(case):
     assert_parity(run_v1(inp), ref_out(inp), case[0])
 
 
-@pytest.mark.parametrize("case", CASES + REDUCE_CASES, ids=[c[0] for c in CASES + REDUCE_CASES])
+@pytest.mark.parametrize("case", CASES + REDUCE_CASES + ORDER_CASES,
+                         ids=[c[0] for c in CASES + REDUCE_CASES + ORDER_CASES])
 def test_v2_partials_and_merge_match_oracle(case):
     inp = make_case(case, 3)
     ps = case[7]
