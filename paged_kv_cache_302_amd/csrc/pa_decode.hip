@@ -179,6 +179,33 @@ __device__ bool find_partition(const DecodeParams& p, int r, bool sort_tails, in
 }
 
 // --------------------------------------------------------------------------
+// Shared partitions (v2, MFMA path, G = 2, 4 or 8, one wave per unit).  A
+// score tile has 16 query rows and one KV group fills only G of them, so
+// sequences are taken in aligned sets of M = 16 / G.  The set's first
+// sequence (the leader) computes its partition for every member whose
+// block-table entries over the partition, and whose token range in it, equal
+// its own (forks and samples of one prompt read the same blocks): member m's
+// heads sit in tile rows mG .. mG + G - 1, and those members' own units
+// return at once.  A member that differs computes its partition alone, in
+// its own rows of the tile.  Every row's arithmetic is independent of the
+// other rows, so the results are bit for bit those of separate units.
+// --------------------------------------------------------------------------
+constexpr int kMaxMembers = 8;
+
+// Tile row i of a unit whose rows start at sequence `lead`: head h0 + i % gsz
+// of sequence lead + i / gsz, for i < M * gsz.  Every row loads a valid query
+// row (indices clamped) so that no load sits under a branch; rows outside
+// `live` are zeroed once the members are known.
+template <class Path>
+__device__ __forceinline__ void load_q_rows(typename Path::QRegs& qr, const DecodeParams& p,
+                                            int lead, int h0, int gsz, int M) {
+    const int i = lane_id() & 15;
+    const int m = min(i / gsz, M - 1), j = i - (i / gsz) * gsz;
+    const int sm = min(lead + m, p.num_seqs - 1);
+    Path::load_q_row(qr, p.q + ((size_t)sm * p.num_heads + h0 + min(j, gsz - 1)) * Path::kD, true);
+}
+
+// --------------------------------------------------------------------------
 // The kernel
 // --------------------------------------------------------------------------
 #ifndef PA_WAVES_PER_EU
@@ -227,6 +254,21 @@ void pa_decode_kernel(DecodeParams p) {
                            : (size_t)s * p.num_heads + h0;
     float* out_h0 = p.out + row0 * D;   // exp_sums / max_logits [S][P][H]: index row0 + j
 
+    // Shared partitions: M members per unit (1: the unit's own heads only).
+    // Only KV groups that fill the 16 rows evenly (G = 2, 4, 8): with others
+    // (G = 7: two members) the member check cost GQA-7B batches, which share
+    // nothing, 2% and could at best halve the shared reads.
+    int M = 1;
+    if constexpr (V2 && NW == 1 && Path::kHeads == 16) {
+        if (p.group <= kMaxMembers && 16 % p.group == 0 && p.head_chunks == 1 &&
+            p.partition_size <= 64 * kBlock)
+            M = 16 / p.group;
+    }
+    const int lead = s - s % M;          // first sequence of the aligned set
+    const int self = s - lead;
+    const int gsz = M > 1 ? p.group : nh;   // tile rows per member
+    const int nrows = M * gsz;
+
     // Everything that depends only on (s, first block) is requested before
     // the length is used: the query, the first two table windows (bounded by
     // the row, not by the length) and the load-policy check.  In v1 these go
@@ -244,12 +286,52 @@ void pa_decode_kernel(DecodeParams p) {
     const NeighbourIds nbr = neighbour_ids(p, s, blk_begin);
 #endif
     typename Path::QRegs qr;
-    Path::load_q(qr, p, s, h0, nh);
+    if constexpr (Path::kHeads == 16) load_q_rows<Path>(qr, p, lead, h0, gsz, M);
+    else Path::load_q(qr, p, s, h0, nh);
+    // the set's lengths and its members' table entries over the partition
+    int mlen[kMaxMembers], ment[kMaxMembers];
+    if (M > 1) {
+        const int bi = min(blk_begin + lane_id(), mbps - 1);
+#pragma unroll
+        for (int i = 0; i < kMaxMembers; ++i) {
+            const int f = min(lead + min(i, M - 1), p.num_seqs - 1);
+            mlen[i] = p.seq_lens[f];
+            ment[i] = p.block_tables[(size_t)f * mbps + bi];
+        }
+    }
     // keep the scheduler from placing a use (and so a wait) between the loads
     __builtin_amdgcn_sched_barrier(0);
 #if PA_LOAD_POLICY == 1
     const bool cached = shared_unit(nbr);
 #endif
+    unsigned members = 1u;   // bit m: the rows of sequence lead + m are computed here
+    if (M > 1) {
+        const int PS = p.partition_size;
+        auto fits = [&](int len) {   // the partition exists and the sequence is well formed
+            return len > part * PS && (len - 1) / PS + 1 <= p.max_num_partitions &&
+                   (len + kBlock - 1) / kBlock <= mbps;
+        };
+        const int tend = min(mlen[0], (part + 1) * PS);
+        const int nblk = (tend - part * PS + kBlock - 1) / kBlock;
+        unsigned match = 0;
+#pragma unroll
+        for (int i = 0; i < kMaxMembers; ++i) {
+            const bool same = __ballot(lane_id() < nblk && ment[i] != ment[0]) == 0;
+            const bool ok = i < M && lead + i < p.num_seqs && fits(mlen[0]) && fits(mlen[i]) &&
+                            min(mlen[i], (part + 1) * PS) == tend && same;
+            match |= ok ? 1u << i : 0u;
+        }
+        if (self != 0 && ((match >> self) & 1u)) return;   // the leader computes it
+        members = self == 0 ? (match | 1u) : 1u << self;
+    }
+    // rows of the tile this unit writes
+    auto live = [&](int i) { return i < nrows && ((members >> (i / gsz)) & 1u); };
+    if constexpr (Path::kHeads == 16) {
+        const int i = lane_id() & 15;
+        const bool keep = live(i);
+#pragma unroll
+        for (int c = 0; c < Path::KC; ++c) qr.q[c] = keep ? qr.q[c] : f16x8{};
+    }
 
     // No branch on L until the first tile request, so the compiler keeps the
     // loads above where they are: an empty v1 sequence (L <= 0; v2 has no
@@ -344,24 +426,37 @@ void pa_decode_kernel(DecodeParams p) {
         // writes 16 contiguous bytes.  Storing straight from the MFMA layout
         // would write every cache line in two halves from two instructions.
         const int HP = Path::kHeads;
-        float* s_o = lds;                 // [nh][D]
-        float* s_m = lds + nh * D;        // [HP]
+        float* s_o = lds;                 // [nrows][D]
+        float* s_m = lds + nrows * D;     // [HP]
         float* s_l = s_m + HP;            // [HP]
-        Path::stage(st, ltot, s_o, s_m, s_l, nh);
+        if constexpr (Path::kHeads == 16) Path::stage(st, ltot, s_o, s_m, s_l, nrows, live(lane_id() & 15));
+        else Path::stage(st, ltot, s_o, s_m, s_l, nrows);
+        // tile row i -> output row of head h0 + i % gsz of sequence lead + i / gsz
+        // (M == 1: row0 + i)
+        auto out_row = [&](int i) {
+            const size_t sq = (size_t)(lead + i / gsz);
+            const size_t r = V2 ? (sq * p.max_num_partitions + part) * p.num_heads
+                                : sq * p.num_heads;
+            return r + h0 + i % gsz;
+        };
         const f32x4* src = reinterpret_cast<const f32x4*>(s_o);
-        const int nv = nh * D / 4;
-        for (int e = lane_id(); e < nv; e += 64) {
-            const float inv = empty ? 0.f : p.v_scale / s_l[(4 * e) / D];
-            f32x4 v = src[e] * inv;
-            if (bad) v = f32x4{NAN, NAN, NAN, NAN};
-            st_stream(reinterpret_cast<f32x4*>(out_h0) + e, v);
+        for (unsigned mm = members; mm != 0u; mm &= mm - 1u) {   // the rows of each member
+            const int m = __ffs(mm) - 1;
+            const int e1 = (m + 1) * gsz * (D / 4);
+            for (int e = m * gsz * (D / 4) + lane_id(); e < e1; e += 64) {
+                const int i = (4 * e) / D;
+                const float inv = empty ? 0.f : p.v_scale / s_l[i];
+                f32x4 v = src[e] * inv;
+                if (bad) v = f32x4{NAN, NAN, NAN, NAN};
+                st_stream(reinterpret_cast<f32x4*>(p.out + out_row(i) * D) + (e - i * (D / 4)), v);
+            }
         }
         if constexpr (V2) {
-            // lane l < nh holds head l's max and total weight on both paths
+            // lane l < nrows holds tile row l's max and total weight on both paths
             const int l = lane_id();
-            if (l < nh) {
-                st_stream(p.max_logits + row0 + l, bad ? NAN : st.m * p.scale);
-                st_stream(p.exp_sums + row0 + l, bad ? NAN : ltot);
+            if (l < nrows && live(l)) {
+                st_stream(p.max_logits + out_row(l), bad ? NAN : st.m * p.scale);
+                st_stream(p.exp_sums + out_row(l), bad ? NAN : ltot);
             }
         }
         return;
@@ -422,6 +517,8 @@ template <class Path, int D, bool V2>
 static int launch_nw(int NW, const DecodeParams& p0, int grid, int nh_max, hipStream_t st) {
     // keep the merge buffer within the default 64 KiB of dynamic LDS
     while (NW > 1 && merge_lds_bytes(NW, nh_max, D, Path::kHeads) > 65536) NW /= 2;
+    // a one-wave v2 MFMA unit may hold several sequences' heads: 16 tile rows
+    if (V2 && NW == 1 && Path::kHeads == 16) nh_max = 16;
     const size_t lds = merge_lds_bytes(NW, nh_max, D, Path::kHeads);
     DecodeParams p = p0;
     const void* fn = nullptr;

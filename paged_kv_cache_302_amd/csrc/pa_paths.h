@@ -219,11 +219,12 @@ struct MfmaPath {
     // Per-head totals of the wave: l summed over the four token groups.
     __device__ static float wave_l(const State& st) { return col4_sum(st.l); }
 
-    // Stage the wave's state for the cross-wave merge: acc[h][d] unnormalised.
+    // Stage the wave's state for the cross-wave merge: acc[h][d] unnormalised
+    // (rows i < nh whose lanes pass `live`).
     __device__ static void stage(const State& st, float ltot, float* s_acc, float* s_m,
-                                 float* s_l, int nh) {
+                                 float* s_l, int nh, bool live = true) {
         const int l = lane_id(), i = l & 15, g = l >> 4;
-        if (i >= nh) return;
+        if (i >= nh || !live) return;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
             *reinterpret_cast<f32x4*>(s_acc + i * D + 16 * nt + 4 * g) = st.acc[nt];

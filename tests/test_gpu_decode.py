@@ -306,3 +306,55 @@ def test_worked_example_embedded():
                                 ex["scale"]).cpu().numpy()[0, 0]
     np.testing.assert_allclose(out[:4], ex["expected_out"], atol=1e-3)
     assert (out[4:] == 0).all()
+
+
+def _share_tables(bt, seq_lens, pattern):
+    """Copy table rows per `pattern`: (dst, src, first_block, last_block)."""
+    bt = bt.copy()
+    for dst, src, b0, b1 in pattern:
+        bt[dst, b0:b1] = bt[src, b0:b1]
+    return bt
+
+
+@pytest.mark.parametrize("G", [2, 4, 8])
+def test_partitions_shared_by_sequences_match_private_copies(G):
+    """v2 units of sequences that read the same blocks over a partition (taken
+    together in one tile) equal, bit for bit, the same sequences reading
+    private copies of those blocks, and the oracle; covered: whole sets that
+    share, a member that differs in one block, a member whose token range in
+    the last partition differs, sharing that crosses the sets' alignment."""
+    S, KVH, D, PS = 12, 2, 128, 64          # 4 blocks per partition
+    w = wl.small_workload("share", num_seqs=S, num_heads=G * KVH, num_kv_heads=KVH,
+                          head_size=D, seq_len_lo=300, seq_len_hi=300, partition_size=PS)
+    inp = wl.make_inputs(w, 21)
+    L = inp.seq_lens.copy()
+    L[9] = 290                               # same blocks as seq 8, shorter last partition
+    L[5] = 299
+    nb = -(-300 // 16)
+    pattern = [(d, 0, 0, nb) for d in (1, 2, 3)]          # seqs 0-3: one copy
+    pattern += [(d, 4, 0, nb) for d in (5, 6, 7)]         # seqs 4-7 ...
+    pattern += [(9, 8, 0, nb), (10, 7, 0, 8), (11, 7, 0, 8)]
+    bt = _share_tables(inp.block_tables, L, pattern)
+    bt[6, 2] = inp.block_tables[6, 2]        # ... but seq 6 differs in one block of partition 0
+    shared = wl.DecodeInputs(w, inp.seed, L, bt, inp.num_blocks, inp.q, inp.k_cache, inp.v_cache)
+    oracle.poison_unused(shared.k_cache, shared.v_cache, shared.block_tables, shared.seq_lens, 16)
+
+    # private copies: every table entry gets its own physical block
+    used = [(s, i) for s in range(S) for i in range(-(-int(L[s]) // 16))]
+    kc = np.full((len(used) + 3,) + inp.k_cache.shape[1:], np.float16(np.nan))
+    vc = np.full((len(used) + 3,) + inp.v_cache.shape[1:], np.float16(np.nan))
+    bt2 = np.full_like(bt, -1)
+    for n, (s, i) in enumerate(used):
+        kc[n + 3] = shared.k_cache[bt[s, i]]
+        vc[n + 3] = shared.v_cache[bt[s, i]]
+        bt2[s, i] = n + 3
+    private = wl.DecodeInputs(w, inp.seed, L, bt2, kc.shape[0], inp.q, kc, vc)
+
+    out_s, tmp_s, es_s, ml_s, P = run_v2(shared, PS)
+    out_p, tmp_p, es_p, ml_p, _ = run_v2(private, PS)
+    valid = ~np.isnan(es_p)
+    assert np.array_equal(tmp_s[valid], tmp_p[valid])
+    assert np.array_equal(es_s[valid], es_p[valid]) and np.array_equal(ml_s[valid], ml_p[valid])
+    assert np.isnan(es_s[~valid]).all(), "a partition past a sequence was written"
+    assert np.array_equal(out_s, out_p)
+    assert_parity(out_s, ref_out(shared), f"shared G={G}")
