@@ -193,14 +193,15 @@ __device__ bool find_partition(const DecodeParams& p, int r, bool sort_tails, in
 constexpr int kMaxMembers = 8;
 
 // Tile row i of a unit whose rows start at sequence `lead`: head h0 + i % gsz
-// of sequence lead + i / gsz, for i < M * gsz.  Every row loads a valid query
-// row (indices clamped) so that no load sits under a branch; rows outside
-// `live` are zeroed once the members are known.
+// of sequence lead + i / gsz, for i < M * gsz; with only >= 0 every row reads
+// member `only`'s row instead (the first load, before the members are known).
+// Every row loads a valid query row (indices clamped) so that no load sits
+// under a branch; rows outside `live` are zeroed once the members are known.
 template <class Path>
 __device__ __forceinline__ void load_q_rows(typename Path::QRegs& qr, const DecodeParams& p,
-                                            int lead, int h0, int gsz, int M) {
+                                            int lead, int h0, int gsz, int M, int only) {
     const int i = lane_id() & 15;
-    const int m = min(i / gsz, M - 1), j = i - (i / gsz) * gsz;
+    const int m = only >= 0 ? only : min(i / gsz, M - 1), j = i - (i / gsz) * gsz;
     const int sm = min(lead + m, p.num_seqs - 1);
     Path::load_q_row(qr, p.q + ((size_t)sm * p.num_heads + h0 + min(j, gsz - 1)) * Path::kD, true);
 }
@@ -286,17 +287,19 @@ void pa_decode_kernel(DecodeParams p) {
     const NeighbourIds nbr = neighbour_ids(p, s, blk_begin);
 #endif
     typename Path::QRegs qr;
-    if constexpr (Path::kHeads == 16) load_q_rows<Path>(qr, p, lead, h0, gsz, M);
+    if constexpr (Path::kHeads == 16) load_q_rows<Path>(qr, p, lead, h0, gsz, M, self);
     else Path::load_q(qr, p, s, h0, nh);
-    // the set's lengths and its members' table entries over the partition
-    int mlen[kMaxMembers], ment[kMaxMembers];
+    // the set's lengths and its members' first table entries of the partition
+    // (scalar loads); the other entries are read only if a member's first one
+    // equals the leader's
+    int mlen[kMaxMembers], mfirst[kMaxMembers];
     if (M > 1) {
-        const int bi = min(blk_begin + lane_id(), mbps - 1);
+        const int b0 = min(blk_begin, mbps - 1);
 #pragma unroll
         for (int i = 0; i < kMaxMembers; ++i) {
             const int f = min(lead + min(i, M - 1), p.num_seqs - 1);
             mlen[i] = p.seq_lens[f];
-            ment[i] = p.block_tables[(size_t)f * mbps + bi];
+            mfirst[i] = p.block_tables[(size_t)f * mbps + b0];
         }
     }
     // keep the scheduler from placing a use (and so a wait) between the loads
@@ -312,14 +315,25 @@ void pa_decode_kernel(DecodeParams p) {
                    (len + kBlock - 1) / kBlock <= mbps;
         };
         const int tend = min(mlen[0], (part + 1) * PS);
-        const int nblk = (tend - part * PS + kBlock - 1) / kBlock;
-        unsigned match = 0;
+        unsigned cand = 0;   // members whose first entry and token range match the leader's
 #pragma unroll
         for (int i = 0; i < kMaxMembers; ++i) {
-            const bool same = __ballot(lane_id() < nblk && ment[i] != ment[0]) == 0;
             const bool ok = i < M && lead + i < p.num_seqs && fits(mlen[0]) && fits(mlen[i]) &&
-                            min(mlen[i], (part + 1) * PS) == tend && same;
-            match |= ok ? 1u << i : 0u;
+                            min(mlen[i], (part + 1) * PS) == tend && mfirst[i] == mfirst[0];
+            cand |= ok ? 1u << i : 0u;
+        }
+        unsigned match = 0;
+        if (cand > 1u) {   // someone besides the leader: compare the whole partition
+            const int nblk = (tend - part * PS + kBlock - 1) / kBlock;
+            const int bi = min(blk_begin + lane_id(), mbps - 1);
+            const int e0 = p.block_tables[(size_t)lead * mbps + bi];
+#pragma unroll
+            for (int i = 0; i < kMaxMembers; ++i) {
+                const int f = min(lead + min(i, M - 1), p.num_seqs - 1);
+                const int e = p.block_tables[(size_t)f * mbps + bi];
+                const bool same = __ballot(lane_id() < nblk && e != e0) == 0;
+                match |= (((cand >> i) & 1u) && same) ? 1u << i : 0u;
+            }
         }
         if (self != 0 && ((match >> self) & 1u)) return;   // the leader computes it
         members = self == 0 ? (match | 1u) : 1u << self;
@@ -327,6 +341,7 @@ void pa_decode_kernel(DecodeParams p) {
     // rows of the tile this unit writes
     auto live = [&](int i) { return i < nrows && ((members >> (i / gsz)) & 1u); };
     if constexpr (Path::kHeads == 16) {
+        if (members != 1u << self) load_q_rows<Path>(qr, p, lead, h0, gsz, M, -1);
         const int i = lane_id() & 15;
         const bool keep = live(i);
 #pragma unroll
