@@ -162,3 +162,41 @@ def test_fp8_write_then_decode_pipeline():
     out = pa.paged_attention_v1(to_dev(q), kc, vc, to_dev(bt), to_dev(lens), 1 / np.sqrt(D),
                                 ks, vs).cpu().numpy()
     assert_parity(out, ref, "fp8 write + decode")
+
+
+def test_fp8_partitions_shared_by_sequences_match_private_copies():
+    """fp8 pools: v2 units of sequences that read the same blocks over a
+    partition (one tile for the aligned set of four, G = 4) equal, bit for bit,
+    the same sequences reading private copies of the codes, and the oracle over
+    the decoded values."""
+    S, KVH, G, D, PS = 8, 2, 4, 128, 128
+    inp, k8, v8, ks, vs = fp8_case("share8", S, G * KVH, KVH, D, 400, 400, seed=33)
+    nb = -(-400 // 16)
+    bt = inp.block_tables.copy()
+    for d in (1, 2, 3):
+        bt[d, :nb] = bt[0, :nb]                      # seqs 0-3 read one copy
+    for d in (5, 6, 7):
+        bt[d, :16] = bt[4, :16]                      # seqs 4-7 share their first two partitions
+    L = inp.seq_lens.copy()
+    used = [(s, i) for s in range(S) for i in range(nb)]
+    k8p = np.full((len(used),) + k8.shape[1:], 0x7F, np.uint8)
+    v8p = np.full((len(used),) + v8.shape[1:], 0x7F, np.uint8)
+    bt2 = np.full_like(bt, -1)
+    for n, (s, i) in enumerate(used):
+        k8p[n], v8p[n], bt2[s, i] = k8[bt[s, i]], v8[bt[s, i]], n
+
+    def run(kc8, vc8, table):
+        P = pa.pa_v2_max_partitions(400, PS)
+        tmp, es, ml = pa.v2_scratch(S, G * KVH, D, P, device())
+        pa.pa_decode_v2(tmp, es, ml, to_dev(inp.q), to_dev(kc8), to_dev(vc8), to_dev(table),
+                        to_dev(L), inp.scale, PS, ks, vs)
+        out = torch.empty((S, G * KVH, D), dtype=torch.float32, device=device())
+        pa.pa_reduce(out, tmp, es, ml, to_dev(L), PS)
+        return tmp.cpu().numpy(), es.cpu().numpy(), ml.cpu().numpy(), out.cpu().numpy()
+
+    shared, private = run(k8, v8, bt), run(k8p, v8p, bt2)
+    for a, b in zip(shared, private):
+        assert np.array_equal(a, b)
+    dk, dv = fp8.dequantize_pools(k8, v8, ks, vs)
+    ref = oracle.paged_decode(inp.q, dk, dv, bt, L, inp.scale, 16)
+    assert_parity(shared[3], ref, "fp8 shared")
