@@ -549,11 +549,21 @@ static int launch_nw(int NW, const DecodeParams& p0, int grid, int nh_max, hipSt
         // each CU's share: then the kernel takes the balanced unit order.
         // With more units the dispatcher balances the CUs itself as slots
         // free up, and the plain order keeps the units that share blocks
-        // (forks, samples of one prompt) running together.
+        // (forks, samples of one prompt) running together.  The occupancy
+        // of each (wave count, LDS size) is asked for once.
+        static std::atomic<long long> occ_cache[4];   // (lds << 8) | (workgroups per CU + 1)
+        const int slot = NW == 1 ? 0 : NW == 2 ? 1 : NW == 4 ? 2 : 3;
+        long long c = occ_cache[slot].load(std::memory_order_relaxed);
         int per_cu = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64 * NW, lds) != hipSuccess) {
-            (void)hipGetLastError();
-            per_cu = 0;
+        if (c != 0 && (size_t)(c >> 8) == lds) {
+            per_cu = (int)(c & 0xff) - 1;
+        } else {
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64 * NW, lds) != hipSuccess) {
+                (void)hipGetLastError();
+                per_cu = 0;
+            }
+            if (per_cu >= 0 && per_cu < 255)
+                occ_cache[slot].store(((long long)lds << 8) | (per_cu + 1), std::memory_order_relaxed);
         }
         const long long resident = (long long)per_cu * p.num_cus;
         p.resident = grid <= resident ? (int)resident : 0;
