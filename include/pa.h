@@ -17,8 +17,10 @@
  *     (allocated by the caller, e.g. through PyTorch).  The library never
  *     allocates, frees or synchronises; it validates its host-side arguments,
  *     enqueues kernels on `stream` (a hipStream_t; NULL = the null stream) and
- *     returns.  Calls keep no state between them and may be made from several
- *     host threads.
+ *     returns.  Calls keep no state between them that affects their results
+ *     (pa_decode_v2 caches each device's compute-unit count and its kernels'
+ *     occupancy, read-only properties, in thread-safe process-wide slots) and
+ *     may be made from several host threads.
  *   - Element types: q, key, value, k_cache and v_cache hold IEEE fp16; out,
  *     tmp_out, exp_sums and max_logits hold fp32; block_tables and seq_lens
  *     int32; slot_mapping and cu_seq_lens int64.  All tensors are dense
