@@ -97,9 +97,11 @@ struct SeqParts {
     int tail;   // blocks of the last partition when it is partly filled, else 0
 };
 
-__device__ __forceinline__ SeqParts seq_parts(const DecodeParams& p, int s, int PB, bool sorted) {
+// pre >= 0: the length of sequence s < 64, already loaded by the caller
+__device__ __forceinline__ SeqParts seq_parts(const DecodeParams& p, int s, int PB, bool sorted,
+                                              int pre = -1) {
     SeqParts r;
-    r.len = s < p.num_seqs ? p.seq_lens[s] : 0;
+    r.len = s < p.num_seqs ? (pre >= 0 && s < 64 ? pre : p.seq_lens[s]) : 0;
     r.np = n_parts(r.len, p.partition_size, p.max_num_partitions);
     const int nb = r.len > 0 ? (r.len - 1) / kBlock + 1 : 0;
     const int last = nb - (r.np - 1) * PB;   // blocks of partition np - 1 (if not capped)
@@ -109,14 +111,14 @@ __device__ __forceinline__ SeqParts seq_parts(const DecodeParams& p, int s, int 
 }
 
 __device__ bool find_partition(const DecodeParams& p, int r, bool sort_tails, int& s_out,
-                               int& p_out, int& L_out) {
+                               int& p_out, int& L_out, int pre0 = -1) {
     const int lane = lane_id();
     const int PB = p.partition_size / kBlock;
     const bool sorted = sort_tails && PB <= 64;
     // 1. full partitions (every partition when the tails are not sorted)
     int base = 0;
     for (int s0 = 0; s0 < p.num_seqs; s0 += 64) {
-        const SeqParts q = seq_parts(p, s0 + lane, PB, sorted);
+        const SeqParts q = seq_parts(p, s0 + lane, PB, sorted, s0 == 0 ? pre0 : -1);
         const int nfull = q.np - (q.tail > 0 ? 1 : 0);
         int incl = nfull;
 #pragma unroll
@@ -223,6 +225,7 @@ void pa_decode_kernel(DecodeParams p) {
     const int kvhc_count = p.num_kv_heads * p.head_chunks;
     int u = blockIdx.x;
     bool sorted = false;   // v2: largest-first order with the snake over the CUs
+    int pre0 = -1;         // v2, at most 64 sequences: lane s's length, loaded here
     if constexpr (V2) {
         sorted = p.resident > 0;
         if (sorted) {
@@ -231,6 +234,29 @@ void pa_decode_kernel(DecodeParams p) {
             const int per = p.unit_period, k = u / per, c = u - k * per;
             const bool back = (k & 1) && per >= kXcds;   // period 1: plain order
             u = k * per + (back ? per - kXcds - (c & ~(kXcds - 1)) + (c & (kXcds - 1)) : c);
+        } else if (p.num_seqs <= 64 && p.unit_period % (kXcds * kvhc_count) == 0) {
+            // A larger grid runs in (sequence, partition) order.  If no two
+            // neighbouring sequences share their first block, each run of
+            // 8 x (KV heads) workgroups gives XCD x every KV head of partition
+            // rank 8g + x: a partition's 16 KiB of rows and its statistics
+            // line then come from one XCD (its L2 merges the eight units'
+            // pieces of the line), while the eight XCDs still read
+            // neighbouring blocks at once.  Units that share blocks keep the
+            // plain order, where a KV head's units (and its shared blocks) stay
+            // on one XCD.  The lengths loaded for the check serve the
+            // partition lookup below.
+            const int ls = min(lane_id(), p.num_seqs - 1);
+            pre0 = p.seq_lens[ls];
+            const int f0 = p.block_tables[(size_t)ls * p.max_blocks_per_seq];
+            const int f1 = __shfl_down(f0, 1), l1 = __shfl_down(pre0, 1);
+            const bool shared =
+                __ballot(lane_id() + 1 < p.num_seqs && f0 == f1 && pre0 > 0 && l1 > 0) != 0;
+            if (lane_id() >= p.num_seqs) pre0 = 0;
+            if (!shared) {
+                const int gx = kXcds * kvhc_count;
+                const int g = u / gx, rem = u - g * gx;
+                u = (g * kXcds + rem % kXcds) * kvhc_count + rem / kXcds;
+            }
         }
     }
     const int kvhc = u % kvhc_count;
@@ -243,7 +269,7 @@ void pa_decode_kernel(DecodeParams p) {
 
     int s, part = 0, L;
     if constexpr (V2) {
-        if (!find_partition(p, r_unit, sorted, s, part, L)) return;
+        if (!find_partition(p, r_unit, sorted, s, part, L, pre0)) return;
     } else {
         s = r_unit;
         L = p.seq_lens[s];

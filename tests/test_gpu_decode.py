@@ -316,21 +316,25 @@ def _share_tables(bt, seq_lens, pattern):
     return bt
 
 
-@pytest.mark.parametrize("G", [2, 4, 8])
-def test_partitions_shared_by_sequences_match_private_copies(G):
+@pytest.mark.parametrize("G,LEN,PS", [(2, 300, 64), (4, 300, 64), (8, 300, 64), (4, 5000, 16)],
+                         ids=["g2", "g4", "g8", "g4_big_grid"])
+def test_partitions_shared_by_sequences_match_private_copies(G, LEN, PS):
     """v2 units of sequences that read the same blocks over a partition (taken
     together in one tile) equal, bit for bit, the same sequences reading
     private copies of those blocks, and the oracle; covered: whole sets that
     share, a member that differs in one block, a member whose token range in
-    the last partition differs, sharing that crosses the sets' alignment."""
-    S, KVH, D, PS = 12, 2, 128, 64          # 4 blocks per partition
+    the last partition differs, sharing that crosses the sets' alignment.
+    The last case's grid (12 x 2 x 313 one-block partitions) exceeds what the
+    device holds: shared tables keep the plain unit order, the private copies
+    take the XCD-major one."""
+    S, KVH, D = 12, 2, 128
     w = wl.small_workload("share", num_seqs=S, num_heads=G * KVH, num_kv_heads=KVH,
-                          head_size=D, seq_len_lo=300, seq_len_hi=300, partition_size=PS)
+                          head_size=D, seq_len_lo=LEN, seq_len_hi=LEN, partition_size=PS)
     inp = wl.make_inputs(w, 21)
     L = inp.seq_lens.copy()
-    L[9] = 290                               # same blocks as seq 8, shorter last partition
-    L[5] = 299
-    nb = -(-300 // 16)
+    L[9] = LEN - 10                          # same blocks as seq 8, shorter last partition
+    L[5] = LEN - 1
+    nb = -(-LEN // 16)
     pattern = [(d, 0, 0, nb) for d in (1, 2, 3)]          # seqs 0-3: one copy
     pattern += [(d, 4, 0, nb) for d in (5, 6, 7)]         # seqs 4-7 ...
     pattern += [(9, 8, 0, nb), (10, 7, 0, 8), (11, 7, 0, 8)]
