@@ -11,7 +11,6 @@ from .paged_attention import (  # noqa: F401
     gather_sequence_fast,
     key_vector,
     kv_head_of,
-    lse,
     lse_merge,
     num_partitions,
     online_block_attention,
@@ -20,10 +19,8 @@ from .paged_attention import (  # noqa: F401
     partition_partials,
     poison_unused,
     reshape_and_cache,
-    scores_fp64,
     used_fill,
     value_vector,
-    x_of,
 )
 from .block_manager import BlockManager, BlockManagerError, copy_blocks  # noqa: F401
 from . import fp8  # noqa: F401

@@ -38,8 +38,6 @@ Readings of points the pages leave open:
 """
 from __future__ import annotations
 
-import math
-
 import numpy as np
 
 F64 = np.float64
@@ -48,12 +46,6 @@ F64 = np.float64
 # ---------------------------------------------------------------------------
 # Layout decode (kernel page §3.1, §2 "block table is the page table of KV")
 # ---------------------------------------------------------------------------
-
-def x_of(dtype) -> int:
-    """Elements per 16-byte chunk of the K layout: x = 16 // element_size
-    (kernel page §3.1 and §4, split_kv_cache)."""
-    return 16 // np.dtype(dtype).itemsize
-
 
 def key_vector(k_cache: np.ndarray, block: int, kv_head: int, slot: int) -> np.ndarray:
     """K of the token in slot `slot` of physical block `block`.
@@ -386,13 +378,3 @@ def poison_unused(k_cache, v_cache, block_tables, seq_lens, block_size: int,
             kv[b, :, :, f:, :] = nan_bits
             vv[b, :, :, f:] = nan_bits
 
-
-def scores_fp64(q_row, K, scale):
-    """Scaled scores of one query row, for needle-style closed forms."""
-    return scale * (np.asarray(K, F64) @ np.asarray(q_row, F64))
-
-
-def lse(values) -> float:
-    v = np.asarray(values, dtype=F64)
-    M = v.max()
-    return float(M + math.log(np.exp(v - M).sum()))

@@ -33,15 +33,23 @@ class ServeResult:
 
 
 def serve_reserved(lengths: Sequence[int], total_cells: int, s_max: int) -> ServeResult:
-    """Every request reserves s_max cells; admit in order while that fits."""
-    served = used = reserved = 0
-    for s in lengths:
-        if reserved + s_max > total_cells:
+    """Whole-length reservation on the native block manager: the pool is cut
+    into total_cells // s_max regions of s_max cells and every request takes
+    one whole region however short it is (one block of s_max tokens); admit
+    in order until a region cannot be had."""
+    regions = total_cells // s_max
+    if regions <= 0:
+        return ServeResult(0, 0, 0)
+    bm = BlockManager(regions, s_max)
+    served = used = 0
+    for i, s in enumerate(lengths):
+        try:
+            bm.add_sequence(i, s_max)
+        except BlockManagerError:
             break
-        reserved += s_max
         used += int(s)
         served += 1
-    return ServeResult(served, used, reserved)
+    return ServeResult(served, used, (regions - bm.num_free_blocks()) * s_max)
 
 
 def serve_paged(lengths: Sequence[int], total_cells: int, block_size: int) -> ServeResult:

@@ -2,9 +2,13 @@
 (CPU; the paged side runs on the native block manager).
 
 Pins: the memory page's LLaMA-7B figure (2*32*4096*2048*16*2 bytes, printed
-as about 17.2 GB); its reservation example (300 of 2048 cells used); the
-closed forms of both utilisations; and the native simulator against the
-oracle's plain allocation loop on seeded request mixes."""
+as about 17.2 GB); its reservation example (300 of 2048 cells used); small
+admission cases and the page's own demo configuration worked out by hand; the
+closed forms of both utilisations; and the native simulator (reservation
+regions and paged blocks taken from the native block manager) against the
+oracle's closed-form admission on seeded request mixes."""
+import random
+
 import numpy as np
 import pytest
 
@@ -23,6 +27,44 @@ def test_reservation_example_of_the_page():
     assert r.served == 1 and r.token_cells == 300 and r.held_cells == 2048
     assert abs(r.utilization - om.reservation_utilization([300], 2048)) < 1e-15
     assert round(100 * r.utilization, 1) == 14.6
+
+
+def test_oracle_admission_on_hand_worked_cases():
+    # reservation: each request costs s_max = 8 cells whatever its length
+    assert om.serve_reserved([10, 3, 7], 25, 8) == (3, 20, 24)
+    assert om.serve_reserved([10, 3, 7], 23, 8) == (2, 13, 16)
+    assert om.serve_reserved([10, 3, 7], 7, 8) == (0, 0, 0)
+    # paged, B = 8, pool of 4 blocks: costs 1, 2, 2, 1 blocks; the running
+    # count 1, 3, 5 stops admission at the third request even though the
+    # fourth alone would fit (arrival order)
+    assert om.serve_paged([5, 9, 16, 1], 32, 8) == (2, 14, 24)
+    assert om.serve_paged([5, 9, 16, 1], 47, 8) == (3, 30, 40)   # 5 blocks fit
+    assert om.serve_paged([], 32, 8) == (0, 0, 0)
+    assert om.serve_paged([40], 32, 8) == (0, 0, 0)
+
+
+def test_memory_page_demo_configuration():
+    # The memory page's Python demo: random.seed(42), 40 request lengths
+    # randint(8, 28), a pool of 192 cells, reservation of max_len = 32 per
+    # request against blocks of 8.  Worked by hand from the drawn lengths
+    # 28 11 8 16 15 15 12 11 25 10 26 ...: reservation admits 192 // 32 = 6
+    # requests holding 28+11+8+16+15+15 = 93 tokens in 192 reserved cells;
+    # paging costs 4 2 1 2 2 2 2 2 4 2 blocks (running 23 of 24) for the first
+    # ten, and the eleventh (26 tokens, 4 blocks) does not fit: 10 requests,
+    # 151 tokens in 184 cells.
+    random.seed(42)
+    lengths = [random.randint(8, 28) for _ in range(40)]
+    assert lengths[:11] == [28, 11, 8, 16, 15, 15, 12, 11, 25, 10, 26]
+    assert om.serve_reserved(lengths, 192, 32) == (6, 93, 192)
+    assert om.serve_paged(lengths, 192, 8) == (10, 151, 184)
+    res = memsim.serve_reserved(lengths, 192, 32)
+    pag = memsim.serve_paged(lengths, 192, 8)
+    assert (res.served, res.token_cells, res.held_cells) == (6, 93, 192)
+    assert (pag.served, pag.token_cells, pag.held_cells) == (10, 151, 184)
+    # the page reports tokens over reserved cells for reservation (48.4%) and
+    # held blocks over the pool for paging (95.8%): about 50% -> over 90%
+    assert round(100 * res.token_cells / res.held_cells, 1) == 48.4
+    assert round(100 * pag.held_cells / 192, 1) == 95.8
 
 
 @pytest.mark.parametrize("seed", [0, 1, 2])
