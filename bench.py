@@ -87,8 +87,8 @@ def blas_threads() -> int:
 
 class Parity:
     """GPU output against the oracle on the sampled rows: max-abs, relative L2,
-    and whether every element is within 2e-3 + 1e-2 |ref| and the relative L2
-    within 1e-2."""
+    and whether the max-abs error is within 2e-3 and the relative L2 within
+    1e-2."""
 
     def __init__(self):
         self.max_abs, self.err2, self.ref2, self.within = 0.0, 0.0, 0.0, True
@@ -98,7 +98,7 @@ class Parity:
         self.max_abs = max(self.max_abs, float(np.abs(diff).max()))
         self.err2 += float((diff ** 2).sum())
         self.ref2 += float((ref ** 2).sum())
-        self.within = self.within and bool((np.abs(diff) <= 2e-3 + 1e-2 * np.abs(ref)).all())
+        self.within = self.within and bool(np.isfinite(gpu).all() and np.abs(diff).max() <= 2e-3)
 
     def result(self):
         rel = (self.err2 / self.ref2) ** 0.5 if self.ref2 > 0 else 0.0

@@ -5,11 +5,12 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-# fp16 Q/K/V with fp32 accumulation against the fp64 oracle:
-# elementwise |gpu - ref| <= ATOL + RTOL*|ref|, and a scale-aware check
-# ||gpu - ref||_2 / ||ref||_2 <= REL_L2 (outputs of long contexts are ~1e-3).
+# fp16 Q/K/V with fp32 accumulation against the fp64 oracle: a hard
+# max |gpu - ref| <= ATOL over every compared element, and the relative part
+# of the bar as a scale-aware check ||gpu - ref||_2 / ||ref||_2 <= REL_L2
+# (outputs of long contexts are ~1e-3, where an elementwise relative bound
+# would say little).
 ATOL = 2e-3
-RTOL = 1e-2
 REL_L2 = 1e-2
 
 
@@ -37,10 +38,10 @@ def assert_parity(gpu: np.ndarray, ref: np.ndarray, what: str = "", mask=None):
     assert gpu.shape == ref.shape
     assert np.isfinite(gpu).all(), f"{what}: non-finite GPU output"
     err = np.abs(gpu - ref)
-    bound = ATOL + RTOL * np.abs(ref)
-    worst = np.unravel_index(np.argmax(err - bound), err.shape) if err.size else None
-    assert (err <= bound).all(), (
-        f"{what}: max abs err {err.max():.3e} at {worst} (ref {ref[worst]:.4e}, gpu {gpu[worst]:.4e})")
+    worst = np.unravel_index(np.argmax(err), err.shape) if err.size else None
+    assert not err.size or err.max() <= ATOL, (
+        f"{what}: max abs err {err.max():.3e} > {ATOL} at {worst} "
+        f"(ref {ref[worst]:.4e}, gpu {gpu[worst]:.4e})")
     nref = np.linalg.norm(ref)
     if nref > 0:
         rel = np.linalg.norm(gpu - ref) / nref
