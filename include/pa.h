@@ -115,8 +115,10 @@ PA_API int pa_decode_v1(float* out, const void* q, const void* k_cache, const vo
                  float scale, int kv_cache_dtype, float k_scale, float v_scale,
                  void* stream);
 
-/* ceil(max_seq_len / partition_size): the partition count v2 scratch is sized
- * for; -1 if an argument is not positive. */
+/* ceil(max_seq_len / partition_size): the number of PARTITION_SIZE token
+ * ranges the longest sequence is cut into (kernel page §3.3, the v2 split),
+ * i.e. the partition count the v2 scratch is sized for; -1 if an argument is
+ * not positive. */
 PA_API int pa_v2_max_partitions(int max_seq_len, int partition_size);
 
 /*
@@ -184,7 +186,12 @@ PA_API int pa_reduce(float* out, const float* tmp_out, const float* exp_sums,
  *
  *   out             [total_q, num_heads, head_size] fp32, written
  *   q               [total_q, num_heads, head_size] fp16
- *   query_start_loc [num_seqs + 1] int32, non-decreasing, starting at 0
+ *   query_start_loc [num_seqs + 1] int32, non-decreasing, starting at 0;
+ *                   a sequence whose range [query_start_loc[s],
+ *                   query_start_loc[s+1]) runs backwards or leaves
+ *                   [0, total_q) is bad: the part of it inside [0, total_q)
+ *                   is set to NaN and nothing outside is read or written
+ *   total_q         rows of q and out (>= 0; 0 enqueues nothing)
  *   max_query_len   >= every n (sizes the grid; 0 enqueues nothing); rows of a
  *                   sequence beyond the first max_query_len (rounded up to
  *                   the tile) are set to NaN
@@ -193,7 +200,7 @@ PA_API int pa_reduce(float* out, const float* tmp_out, const float* exp_sums,
  */
 PA_API int pa_prefill(float* out, const void* q, const void* k_cache, const void* v_cache,
                const int32_t* block_tables, const int32_t* seq_lens,
-               const int32_t* query_start_loc, int num_seqs, int num_heads,
+               const int32_t* query_start_loc, int num_seqs, int total_q, int num_heads,
                int num_kv_heads, int head_size, int block_size, int max_blocks_per_seq,
                int num_blocks, int max_query_len, float scale, int kv_cache_dtype,
                float k_scale, float v_scale, void* stream);
@@ -229,7 +236,11 @@ PA_API int reshape_and_cache(const void* key, const void* value, void* k_cache, 
 /*
  * pa_gather_kv -- the read-side indirection alone: every sequence's K and V
  * copied bit-exactly, in logical token order, to contiguous arrays of the
- * pools' element type (fp16 values or fp8 codes).
+ * pools' element type (fp16 values or fp8 codes).  It is the cache write of
+ * kernel page §3.2 run in the other direction -- logical token t of a
+ * sequence is slot t % 16 of physical block block_tables[s][t / 16] (§3.4,
+ * the block-table walk; memory page 分页机制, the page map) -- with no
+ * attention arithmetic, so a test can check the walk bit for bit.
  *
  *   k_out, v_out [sum_s L_s, num_kv_heads, head_size] elements, written:
  *                token t of sequence s goes to row cu_seq_lens[s] + t

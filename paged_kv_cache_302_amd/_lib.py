@@ -30,7 +30,7 @@ _SIGNATURES = {
     "pa_v2_max_partitions": ([_c_int, _c_int], _c_int),
     "pa_decode_v2": ([_ptr] * 8 + [_c_int] * 9 + [_c_float, _c_int, _c_float, _c_float, _ptr], _c_int),
     "pa_reduce": ([_ptr] * 5 + [_c_int] * 5 + [_ptr], _c_int),
-    "pa_prefill": ([_ptr] * 7 + [_c_int] * 8 + [_c_float, _c_int, _c_float, _c_float, _ptr], _c_int),
+    "pa_prefill": ([_ptr] * 7 + [_c_int] * 9 + [_c_float, _c_int, _c_float, _c_float, _ptr], _c_int),
     "reshape_and_cache": ([_ptr] * 5 + [_c_int] * 5 + [_c_i64, _c_i64, _c_int, _c_float, _c_float,
                                                          _ptr], _c_int),
     "pa_gather_kv": ([_ptr] * 7 + [_c_int] * 7 + [_ptr], _c_int),
@@ -215,7 +215,7 @@ def pa_prefill(out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc
         raise ValueError("block_tables [S, ...] and query_start_loc [S + 1] must match seq_lens [S]")
     lib = load_library()
     rc = lib.pa_prefill(_p(out), _p(q), _p(k_cache), _p(v_cache), _p(block_tables), _p(seq_lens),
-                        _p(query_start_loc), S, H, KVH, D, B, block_tables.shape[1], NB,
+                        _p(query_start_loc), S, T, H, KVH, D, B, block_tables.shape[1], NB,
                         int(max_query_len), float(scale), kv_dtype_of(k_cache), float(k_scale),
                         float(v_scale), _stream(q, stream))
     _check(rc, "pa_prefill")

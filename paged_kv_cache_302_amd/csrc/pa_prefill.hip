@@ -289,10 +289,26 @@ __device__ __forceinline__ void nan_rows(float* out, int num_heads, int head0, i
     }
 }
 
+// Query rows [q0, q0 + nq) of sequence s, from query_start_loc.  A range
+// that leaves [0, total_q) or runs backwards marks the sequence bad and is
+// clipped to [0, total_q), so its NaN rows never leave q and out.
+struct QueryRange {
+    int q0, nq;
+    bool bad;
+};
+__device__ __forceinline__ QueryRange query_range(const int32_t* qsl, int s, int total_q) {
+    const int a = qsl[s], b = qsl[s + 1];
+    QueryRange r;
+    r.bad = a < 0 || b < a || b > total_q;
+    r.q0 = min(max(a, 0), total_q);
+    r.nq = min(max(b, r.q0), total_q) - r.q0;
+    return r;
+}
+
 template <class Path, int NG>
 __global__ __launch_bounds__(64) void pa_prefill_kernel(DecodeParams p,
                                                         const int32_t* __restrict__ qsl,
-                                                        int tpu, int q_tiles) {
+                                                        int total_q, int tpu, int q_tiles) {
     using G2 = MfmaGroups<Path, NG>;
     constexpr int D = G2::D;
     extern __shared__ float lds[];
@@ -304,14 +320,14 @@ __global__ __launch_bounds__(64) void pa_prefill_kernel(DecodeParams p,
     const int hc = kvhc - kvh * p.head_chunks;
     const int gleft = p.group - hc * 16;
     const int gc = gleft < 16 ? gleft : 16;            // heads of this chunk
-    const int q0 = qsl[s];
-    const int nq = qsl[s + 1] - q0;
+    const QueryRange qr_ = query_range(qsl, s, total_q);
+    const int q0 = qr_.q0, nq = qr_.nq;
     const int j0 = qt * tpu;
     if (j0 >= nq) return;
     const int ntok = min(tpu, nq - j0);
     const int L = p.seq_lens[s];
     const int nb_seq = (L + kBlock - 1) / kBlock;
-    bool bad = nq > L || nb_seq > p.max_blocks_per_seq;
+    bool bad = qr_.bad || nq > L || nb_seq > p.max_blocks_per_seq;
 
     const int head0 = kvh * p.group + hc * 16;
     const int pos_last = L - nq + j0 + ntok - 1;
@@ -425,7 +441,7 @@ template <class Path, int NG, int W>
 // (two resident waves per SIMD asked of the register allocator: at most 256 VGPRs)
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) void pa_prefill_wg_kernel(DecodeParams p,
                                                                const int32_t* __restrict__ qsl,
-                                                               int tpu, int q_tiles) {
+                                                               int total_q, int tpu, int q_tiles) {
     using G2 = MfmaGroups<Path, NG>;
     constexpr int D = G2::D;
     constexpr int NT = D / 16;
@@ -445,15 +461,15 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     const int hc = kvhc - kvh * p.head_chunks;
     const int gleft = p.group - hc * 16;
     const int gc = gleft < 16 ? gleft : 16;        // heads of this chunk
-    const int q0 = qsl[s];
-    const int nq = qsl[s + 1] - q0;
+    const QueryRange qr_ = query_range(qsl, s, total_q);
+    const int q0 = qr_.q0, nq = qr_.nq;
     const int jw = qt * W * tpu;                   // first query token of the workgroup
     if (jw >= nq) return;                          // the whole workgroup
     const int j0 = jw + wave * tpu;                // first query token of this wave
     const int ntok = max(0, min(tpu, nq - j0));
     const int L = p.seq_lens[s];
     const int nb_seq = (L + kBlock - 1) / kBlock;
-    bool bad = nq > L || nb_seq > p.max_blocks_per_seq;
+    bool bad = qr_.bad || nq > L || nb_seq > p.max_blocks_per_seq;
 
     const int head0 = kvh * p.group + hc * 16;
     int pos[NG];
@@ -588,17 +604,17 @@ using namespace pa;
 
 extern "C" int pa_prefill(float* out, const void* q, const void* k_cache, const void* v_cache,
                           const int32_t* block_tables, const int32_t* seq_lens,
-                          const int32_t* query_start_loc, int num_seqs, int num_heads,
-                          int num_kv_heads, int head_size, int block_size, int max_blocks_per_seq,
-                          int num_blocks, int max_query_len, float scale, int kv_cache_dtype,
-                          float k_scale, float v_scale, void* stream) {
+                          const int32_t* query_start_loc, int num_seqs, int total_q,
+                          int num_heads, int num_kv_heads, int head_size, int block_size,
+                          int max_blocks_per_seq, int num_blocks, int max_query_len, float scale,
+                          int kv_cache_dtype, float k_scale, float v_scale, void* stream) {
     int rc = check_decode_args(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_heads,
                                num_kv_heads, head_size, block_size, max_blocks_per_seq, num_blocks,
                                scale, kv_cache_dtype, k_scale, v_scale);
     if (rc != PA_OK) return rc;
-    if (!out || !query_start_loc || max_query_len < 0) return PA_ERR_INVALID_ARG;
+    if (!out || !query_start_loc || max_query_len < 0 || total_q < 0) return PA_ERR_INVALID_ARG;
     if (!aligned16(out) || !aligned4(query_start_loc)) return PA_ERR_MISALIGNED;
-    if (num_seqs == 0 || max_query_len == 0) return PA_OK;
+    if (num_seqs == 0 || max_query_len == 0 || total_q == 0) return PA_OK;
     DecodeParams p = make_params(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_heads,
                                  num_kv_heads, max_blocks_per_seq, num_blocks, scale,
                                  kv_cache_dtype, k_scale, v_scale);
@@ -624,17 +640,17 @@ extern "C" int pa_prefill(float* out, const void* q, const void* k_cache, const 
     if (head_size == 128) {
         if (fp8)
             hipLaunchKernelGGL((pa_prefill_wg_kernel<MfmaPath8<128>, NG, W8>), g, dim3(64 * W8), lds, st,
-                               p, query_start_loc, tpu, q_tiles);
+                               p, query_start_loc, total_q, tpu, q_tiles);
         else
             hipLaunchKernelGGL((pa_prefill_kernel<MfmaPath<128>, NG>), g, dim3(64), lds, st,
-                               p, query_start_loc, tpu, q_tiles);
+                               p, query_start_loc, total_q, tpu, q_tiles);
     } else {
         if (fp8)
             hipLaunchKernelGGL((pa_prefill_wg_kernel<MfmaPath8<64>, NG, W8>), g, dim3(64 * W8), lds, st,
-                               p, query_start_loc, tpu, q_tiles);
+                               p, query_start_loc, total_q, tpu, q_tiles);
         else
             hipLaunchKernelGGL((pa_prefill_kernel<MfmaPath<64>, NG>), g, dim3(64), lds, st,
-                               p, query_start_loc, tpu, q_tiles);
+                               p, query_start_loc, total_q, tpu, q_tiles);
     }
     return launch_status();
 }

@@ -139,3 +139,50 @@ def test_fp8_invalid_shapes_give_nan_rows():
     assert np.isnan(out[4 + 64:4 + 70]).all()
     assert_parity(out[4:4 + 64], ref[:64], "covered rows")
     assert_parity(out[4 + 70:], ref[70:], "other sequence")
+
+
+@pytest.mark.parametrize("fp8_pools", [False, True], ids=["fp16", "fp8"])
+def test_malformed_query_start_loc_stays_in_bounds(fp8_pools):
+    """query_start_loc ranges that run backwards or leave [0, total_q): the
+    sequence's rows inside [0, total_q) come back NaN, nothing past the last
+    row of out is written, and well-formed sequences are unaffected.  out is
+    a view of a larger buffer whose guard rows must keep their sentinel."""
+    H, KVH, D, T = 8, 2, 128, 10
+    inp, lens, _, q = make("qsl", H, KVH, D, [40, 30, 20, 30], [4, 4, 2, 2], seed=48)
+    q = np.random.default_rng(49).standard_normal((T, H, D)).astype(np.float16)
+    ks, vs = (0.03, 0.02) if fp8_pools else (1.0, 1.0)
+    if fp8_pools:
+        k8 = logical_to_k8(fp8.quantize(k16_to_logical(inp.k_cache), ks))
+        v8 = fp8.quantize(inp.v_cache, vs)
+        dk, dv = fp8.dequantize_pools(k8, v8, ks, vs)
+        kc, vc = to_dev(k8), to_dev(v8)
+    else:
+        dk, dv = inp.k_cache, inp.v_cache
+        kc, vc = to_dev(inp.k_cache), to_dev(inp.v_cache)
+    sentinel = 12345.0
+    # (query_start_loc, rows expected NaN, well-formed (sequence, first row, rows))
+    cases = [
+        # sequence 3 ends past total_q: rows 8, 9 NaN
+        ([0, 4, 4, 8, 30], [8, 9], [(0, 0, 4), (2, 4, 4)]),
+        # sequence 0 starts below 0: rows 0..3 NaN; sequence 2 runs backwards
+        # (no row); sequence 3 is empty; row 9 belongs to no sequence
+        ([-3, 4, 9, 6, 6], [0, 1, 2, 3], [(1, 4, 5)]),
+    ]
+    for qsl_list, nan_rows, good in cases:
+        qsl = np.array(qsl_list, np.int32)
+        buf = torch.full((T + 6, H, D), sentinel, dtype=torch.float32, device=device())
+        out = buf[:T]
+        pa.pa_prefill(out, to_dev(q), kc, vc, to_dev(inp.block_tables), to_dev(lens),
+                      to_dev(qsl), 30, inp.scale, ks, vs)
+        got = buf.cpu().numpy()
+        assert (got[T:] == sentinel).all(), f"{qsl_list}: a row past total_q was written"
+        assert np.isnan(got[nan_rows]).all(), f"{qsl_list}: rows {nan_rows} not NaN"
+        touched = set(nan_rows)
+        for s, r0, n in good:
+            sq = np.array([0, n], np.int32)
+            ref = oracle.paged_prefill(q[r0:r0 + n], dk, dv, inp.block_tables[s:s + 1],
+                                       lens[s:s + 1], sq, inp.scale, 16)
+            assert_parity(got[r0:r0 + n], ref, f"{qsl_list} sequence {s}")
+            touched |= set(range(r0, r0 + n))
+        for r in sorted(set(range(T)) - touched):
+            assert (got[r] == sentinel).all(), f"{qsl_list}: row {r} of no sequence was written"
