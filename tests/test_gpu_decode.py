@@ -34,12 +34,14 @@ REDUCE_CASES = [
 ]
 # v2 unit order: grids the device holds at once take the largest-first order;
 # 200 sequences span four 64-lane chunks of its lookup, 128-block partitions
-# leave the partly filled ones unsorted, and 1,200 sequences x 8 partitions
-# exceed what the device holds (plain order)
+# leave the partly filled ones unsorted, 1,200 sequences x 8 partitions
+# exceed what the device holds (plain order), and 64 sequences x 8 KV heads x
+# up to 16 partitions exceed it with no shared blocks (XCD-major order)
 ORDER_CASES = [
     ("order_200seqs", 200, 8, 2, 64, 1, 700, 128),
     ("order_ps2048", 3, 8, 2, 128, 1, 5000, 2048),
     ("order_big_grid", 1200, 8, 2, 64, 1, 1000, 128),
+    ("order_xcd_major", 64, 32, 8, 128, 1, 1024, 64),
 ]
 
 

@@ -200,3 +200,52 @@ def test_fp8_partitions_shared_by_sequences_match_private_copies():
     dk, dv = fp8.dequantize_pools(k8, v8, ks, vs)
     ref = oracle.paged_decode(inp.q, dk, dv, bt, L, inp.scale, 16)
     assert_parity(shared[3], ref, "fp8 shared")
+
+
+def fp8_decode_both(inp, k8, v8, ks, vs, ps):
+    q, bt, sl = to_dev(inp.q), to_dev(inp.block_tables), to_dev(inp.seq_lens)
+    kc, vc = to_dev(k8), to_dev(v8)
+    out1 = pa.paged_attention_v1(q, kc, vc, bt, sl, inp.scale, ks, vs).cpu().numpy()
+    out2 = pa.paged_attention_v2(q, kc, vc, bt, sl, inp.scale, ps, inp.workload.max_seq_len,
+                                 ks, vs).cpu().numpy()
+    return out1, out2
+
+
+# One sequence and one KV head: the launch uses 8 waves per unit, so these
+# lengths put 64, 65, 128 and 156 blocks on a wave (v1, and v2 with 16K-token
+# partitions), and the wave's table window of 64 entries is refilled during
+# the walk on both fp8 paths.
+FP8_WINDOW_LENS = [512 * 16, 512 * 16 + 1, 1024 * 16 + 7, 20000]
+
+
+@pytest.mark.parametrize("H,D", [(4, 64), (1, 128)], ids=["mfma", "valu"])
+@pytest.mark.parametrize("L", FP8_WINDOW_LENS)
+def test_fp8_long_unit_crosses_table_windows(H, D, L):
+    inp, k8, v8, ks, vs = fp8_case("windows8", 1, H, 1, D, L, L, seed=33)
+    dk, dv = fp8.dequantize_pools(k8, v8, ks, vs)
+    ref = oracle.paged_decode(inp.q, dk, dv, inp.block_tables, inp.seq_lens, inp.scale, 16)
+    out1, out2 = fp8_decode_both(inp, k8, v8, ks, vs, 16384)
+    assert_parity(out1, ref, f"fp8 v1 L={L}")
+    assert_parity(out2, ref, f"fp8 v2 L={L}")
+
+
+# v2 unit orders on fp8 pools: 64 sequences x 8 KV heads x up to 16
+# partitions is more than the device holds at once and shares no blocks (the
+# XCD-major order); 1,200 sequences exceed it with the plain order; 200
+# sequences fit (largest-first order over four lookup chunks).
+FP8_ORDER_CASES = [
+    ("xcd_major", 64, 32, 8, 128, 1, 1024, 64),
+    ("big_grid", 1200, 8, 2, 64, 1, 1000, 128),
+    ("resident_200", 200, 8, 2, 64, 1, 700, 128),
+]
+
+
+@pytest.mark.parametrize("case", FP8_ORDER_CASES, ids=[c[0] for c in FP8_ORDER_CASES])
+def test_fp8_v2_unit_orders(case):
+    label, S, H, KVH, D, lo, hi, ps = case
+    inp, k8, v8, ks, vs = fp8_case(label, S, H, KVH, D, lo, hi, seed=34)
+    dk, dv = fp8.dequantize_pools(k8, v8, ks, vs)
+    ref = oracle.paged_decode(inp.q, dk, dv, inp.block_tables, inp.seq_lens, inp.scale, 16)
+    out1, out2 = fp8_decode_both(inp, k8, v8, ks, vs, ps)
+    assert_parity(out2, ref, label + " fp8 v2")
+    assert_parity(out1, ref, label + " fp8 v1")

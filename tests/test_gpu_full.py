@@ -1,13 +1,16 @@
 """GPU parity at the full workload sizes, in the launch configuration bench.py
 times (the same calls on the same shapes): one decode step -- the cache write
 of each sequence's new token, then v1 or v2 + reduce -- checked on sampled
-(sequence, head) rows against the oracle, plus properties that hold at any
-size (shared prefix == private copies, a planted needle at 128K context)."""
+(sequence, head) rows against the oracle, on fp16 pools and on fp8 (E4M3)
+pools written by the library's own cache write, plus properties that hold at
+any size (shared prefix == private copies, a planted needle at 128K
+context)."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
+from oracle import fp8
 import paged_kv_cache_302_amd as pa
 import workloads as wl
 from tests._util import assert_parity, device, to_dev
@@ -34,14 +37,37 @@ class Step:
         self.tmp, self.es, self.ml = pa.v2_scratch(S, H, D, self.P, device())
         self.out = torch.empty((S, H, D), dtype=torch.float32, device=device())
 
+    def to_fp8(self, ks, vs):
+        """Replace the device pools by fp8 pools holding the E4M3 codes of every
+        live token, made by the library itself (as bench.py does): gather each
+        sequence's K/V in logical order, then write them through
+        reshape_and_cache into fp8 pools at the same slots."""
+        inp, w, dev = self.inp, self.w, device()
+        B, KVH, D = w.block_size, w.num_kv_heads, w.head_size
+        lens = inp.seq_lens.astype(np.int64)
+        cu = np.concatenate([[0], np.cumsum(lens)[:-1]])
+        slots = np.concatenate([inp.block_tables[s, np.arange(lens[s]) // B].astype(np.int64) * B
+                                + np.arange(lens[s]) % B for s in range(w.num_seqs)])
+        ko = torch.empty((int(lens.sum()), KVH, D), dtype=torch.float16, device=dev)
+        vo = torch.empty_like(ko)
+        pa.pa_gather_kv(ko, vo, self.kc, self.vc, self.bt, self.sl, to_dev(cu))
+        NB = inp.num_blocks
+        self.kc = torch.zeros((NB, KVH, D // 16, B, 16), dtype=torch.uint8, device=dev)
+        self.vc = torch.zeros((NB, KVH, D, B), dtype=torch.uint8, device=dev)
+        pa.reshape_and_cache(ko, vo, self.kc, self.vc, to_dev(slots), ks, vs)
+        torch.cuda.synchronize()
+        self.ks, self.vs = ks, vs
+
     def run(self, kernel):
-        pa.reshape_and_cache(self.key, self.val, self.kc, self.vc, self.slot_d)
+        ks, vs = getattr(self, "ks", 1.0), getattr(self, "vs", 1.0)
+        pa.reshape_and_cache(self.key, self.val, self.kc, self.vc, self.slot_d, ks, vs)
         if kernel == "v2":
             pa.pa_decode_v2(self.tmp, self.es, self.ml, self.q, self.kc, self.vc, self.bt, self.sl,
-                            self.inp.scale, self.w.partition_size)
+                            self.inp.scale, self.w.partition_size, ks, vs)
             pa.pa_reduce(self.out, self.tmp, self.es, self.ml, self.sl, self.w.partition_size)
         else:
-            pa.pa_decode_v1(self.out, self.q, self.kc, self.vc, self.bt, self.sl, self.inp.scale)
+            pa.pa_decode_v1(self.out, self.q, self.kc, self.vc, self.bt, self.sl, self.inp.scale,
+                            ks, vs)
         return self.out.cpu().numpy()
 
     def host_after_write(self):
@@ -81,6 +107,48 @@ def test_full_workload_step_sampled_parity(name, kernel):
     # the cache write itself, read back at the written slots
     kc = st.kc.cpu().numpy()
     assert kc.tobytes() == inp.k_cache.tobytes()
+
+
+def fp8_reference(inp, pairs, ks, vs):
+    """The oracle over its own E4M3 quantization of the fp16 values (per-pool
+    scales, element by element, so it commutes with the gather) for the
+    sampled (sequence, head) rows."""
+    w = inp.workload
+    S, H, D = inp.q.shape
+    G = H // w.num_kv_heads
+    ref = np.full((S, H, D), np.nan)
+    for s in sorted({p[0] for p in pairs}):
+        for kvh in sorted({p[1] // G for p in pairs if p[0] == s}):
+            K, V = oracle.gather_sequence_fast(inp.k_cache, inp.v_cache, inp.block_tables[s],
+                                               int(inp.seq_lens[s]), kvh, w.block_size)
+            K = fp8.dequantize(fp8.quantize(K, ks), ks)
+            V = fp8.dequantize(fp8.quantize(V, vs), vs)
+            hs = slice(kvh * G, (kvh + 1) * G)
+            ref[s, hs] = oracle.attention(inp.q[s, hs], K, V, inp.scale)
+    return ref
+
+
+@pytest.mark.parametrize("name,kernel", [
+    ("long_gqa", "v2"), ("gqa7b", "v1"), ("gqa7b", "v2"), ("mha7b", "v1"), ("shared_prefix", "v2"),
+])
+def test_full_workload_fp8_step_sampled_parity(name, kernel):
+    """The fp8 bench lines' shapes and launch configurations (k_scale = v_scale
+    = 2**-6, as bench.py --kv-dtype fp8): pools written by the library's cache
+    write from the workload's fp16 values, the step's token written into them,
+    then v1 or v2 + reduce; sampled rows against the oracle's own
+    quantization."""
+    w = wl.WORKLOADS[name]
+    inp = wl.make_inputs(w, {"gqa7b": 2, "mha7b": 3, "long_gqa": 4, "shared_prefix": 5}[name])
+    ks = vs = 2.0 ** -6
+    st = Step(inp)
+    st.to_fp8(ks, vs)
+    out = st.run(kernel)
+    assert np.isfinite(out).all()
+    st.host_after_write()
+    pairs = sample_heads(w, inp.seq_lens)
+    ref = fp8_reference(inp, pairs, ks, vs)
+    idx = tuple(np.array(pairs).T)
+    assert_parity(out[idx], ref[idx], f"{name} fp8 {kernel}")
 
 
 def test_shared_prefix_equals_private_copies_bit_exact():

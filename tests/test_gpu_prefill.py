@@ -186,3 +186,59 @@ def test_malformed_query_start_loc_stays_in_bounds(fp8_pools):
             touched |= set(range(r0, r0 + n))
         for r in sorted(set(range(T)) - touched):
             assert (got[r] == sentinel).all(), f"{qsl_list}: row {r} of no sequence was written"
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name,kv", [("prefill", "fp16"), ("chunked_prefill", "fp16"),
+                                     ("prefill", "fp8"), ("chunked_prefill", "fp8")])
+def test_bench_shape_prefill_sampled_rows(name, kv):
+    """The bench's prefill steps at full size (8 x 2,048-token prompts; 16 x
+    512-token chunks at the end of 4K-8K contexts): the cache write of the
+    query tokens, then pa_prefill in the bench's launch configuration, on fp16
+    pools or on fp8 pools written by the library's cache write (k_scale =
+    v_scale = 2**-6).  Sampled query rows of every sequence -- the first, the
+    last and a spread between -- against the oracle."""
+    w = wl.WORKLOADS[name]
+    seed = 4
+    inp = wl.make_inputs(w, seed)
+    qh, keyh, valh, slots, qsl = wl.make_chunk(w, inp, seed)
+    S, H, D, KVH, B, n = w.num_seqs, w.num_heads, w.head_size, w.num_kv_heads, w.block_size, w.query_len
+    G = H // KVH
+    dev = device()
+    kc, vc = to_dev(inp.k_cache), to_dev(inp.v_cache)
+    bt, sl = to_dev(inp.block_tables), to_dev(inp.seq_lens)
+    ks = vs = 2.0 ** -6 if kv == "fp8" else 1.0
+    if kv == "fp8":
+        # every live token's fp16 K/V through the library's gather and cache write
+        lens = inp.seq_lens.astype(np.int64)
+        cu = np.concatenate([[0], np.cumsum(lens)[:-1]])
+        allslots = np.concatenate([inp.block_tables[s, np.arange(lens[s]) // B].astype(np.int64) * B
+                                   + np.arange(lens[s]) % B for s in range(S)])
+        ko = torch.empty((int(lens.sum()), KVH, D), dtype=torch.float16, device=dev)
+        vo = torch.empty_like(ko)
+        pa.pa_gather_kv(ko, vo, kc, vc, bt, sl, to_dev(cu))
+        kc = torch.zeros((inp.num_blocks, KVH, D // 16, B, 16), dtype=torch.uint8, device=dev)
+        vc = torch.zeros((inp.num_blocks, KVH, D, B), dtype=torch.uint8, device=dev)
+        pa.reshape_and_cache(ko, vo, kc, vc, to_dev(allslots), ks, vs)
+        del ko, vo
+    out = torch.empty((S * n, H, D), dtype=torch.float32, device=dev)
+    pa.reshape_and_cache(to_dev(keyh), to_dev(valh), kc, vc, to_dev(slots), ks, vs)
+    pa.pa_prefill(out, to_dev(qh), kc, vc, bt, sl, to_dev(qsl), n, inp.scale, ks, vs)
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all()
+    oracle.reshape_and_cache(keyh, valh, inp.k_cache, inp.v_cache, slots, B, inplace=True)
+    rows = sorted({0, 1, 7, 8, 31, 32, n // 2, n - 33, n - 2, n - 1})
+    for s in range(S):
+        L = int(inp.seq_lens[s])
+        for kvh in ({0, KVH - 1, s % KVH}):
+            K, V = oracle.gather_sequence_fast(inp.k_cache, inp.v_cache, inp.block_tables[s], L,
+                                               kvh, B)
+            if kv == "fp8":
+                K = fp8.dequantize(fp8.quantize(K, ks), ks)
+                V = fp8.dequantize(fp8.quantize(V, vs), vs)
+            hs = slice(kvh * G, (kvh + 1) * G)
+            for j in rows:
+                p = L - n + j
+                r = int(qsl[s]) + j
+                ref = oracle.attention(qh[r, hs], K[:p + 1], V[:p + 1], inp.scale)   # keys 0..p
+                assert_parity(got[r, hs], ref, f"{name} {kv} seq {s} kvh {kvh} row {j}")
