@@ -74,7 +74,8 @@ typedef enum pa_status {
     PA_ERR_UNSUPPORTED = -2,  /* head_size not 64/128, block_size not 16        */
     PA_ERR_MISALIGNED = -3,   /* a pointer or stride breaks 16-byte alignment    */
     PA_ERR_LAUNCH = -4,       /* the HIP runtime refused a launch               */
-    PA_ERR_NO_SPACE = -5      /* block manager: too few free blocks / output too small */
+    PA_ERR_NO_SPACE = -5,     /* block manager: too few free blocks / output too small */
+    PA_ERR_SCRATCH_TOO_SMALL = -6  /* pa_decode_v2_noalloc: partials exceed its fixed scratch */
 } pa_status;
 
 /* Version of this ABI (bumped on any signature change). */
@@ -171,6 +172,32 @@ PA_API int pa_reduce(float* out, const float* tmp_out, const float* exp_sums,
               const float* max_logits, const int32_t* seq_lens,
               int num_seqs, int num_heads, int head_size,
               int max_num_partitions, int partition_size, void* stream);
+
+/*
+ * pa_decode_v2_noalloc -- pa_decode_v2 followed by pa_reduce, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the partials live in a
+ * fixed array of PA_NOALLOC_SCRATCH_BYTES inside the library's device code
+ * (one per GPU, held until the process ends) instead of caller scratch.
+ * The call allocates nothing; the caller passes the inputs and the output.
+ *
+ *   out  [num_seqs, num_heads, head_size] fp32, written (as pa_reduce)
+ *   other arguments as in pa_decode_v2.
+ * The partials take S*P*H*D*4 bytes plus 2*S*P*H*4 (P = max_num_partitions,
+ * each part rounded up to 256 bytes); more than PA_NOALLOC_SCRATCH_BYTES
+ * returns PA_ERR_SCRATCH_TOO_SMALL before anything is enqueued.  The first
+ * call on a GPU looks up the device address of that GPU's array.  Every call
+ * on a GPU uses the same array, so calls that overlap on one GPU (two
+ * streams, two host threads) race; calls in one stream are ordered.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (48ull * 1024ull * 1024ull)
+
+PA_API int pa_decode_v2_noalloc(float* out, const void* q, const void* k_cache,
+                 const void* v_cache, const int32_t* block_tables, const int32_t* seq_lens,
+                 int num_seqs, int num_heads, int num_kv_heads, int head_size,
+                 int block_size, int max_blocks_per_seq, int num_blocks,
+                 int max_num_partitions, int partition_size, float scale,
+                 int kv_cache_dtype, float k_scale, float v_scale, void* stream);
 
 /*
  * pa_prefill -- multi-token queries over the paged cache with a causal mask

@@ -30,6 +30,8 @@ _SIGNATURES = {
     "pa_v2_max_partitions": ([_c_int, _c_int], _c_int),
     "pa_decode_v2": ([_ptr] * 8 + [_c_int] * 9 + [_c_float, _c_int, _c_float, _c_float, _ptr], _c_int),
     "pa_reduce": ([_ptr] * 5 + [_c_int] * 5 + [_ptr], _c_int),
+    "pa_decode_v2_noalloc": ([_ptr] * 6 + [_c_int] * 9 + [_c_float, _c_int, _c_float, _c_float, _ptr],
+                             _c_int),
     "pa_prefill": ([_ptr] * 7 + [_c_int] * 9 + [_c_float, _c_int, _c_float, _c_float, _ptr], _c_int),
     "reshape_and_cache": ([_ptr] * 5 + [_c_int] * 5 + [_c_i64, _c_i64, _c_int, _c_float, _c_float,
                                                          _ptr], _c_int),
@@ -193,6 +195,24 @@ def pa_decode_v2(tmp_out, exp_sums, max_logits, q, k_cache, v_cache, block_table
                           P, int(partition_size), float(scale), kv_dtype_of(k_cache),
                           float(k_scale), float(v_scale), _stream(q, stream))
     _check(rc, "pa_decode_v2")
+
+
+def pa_decode_v2_noalloc(out, q, k_cache, v_cache, block_tables, seq_lens, scale: float,
+                         partition_size: int, max_num_partitions: int, k_scale: float = 1.0,
+                         v_scale: float = 1.0, stream=None):
+    """out[S,H,D] fp32 <- pa_decode_v2 + pa_reduce with the partials in the
+    library's fixed device scratch (no allocation; include/pa.h)."""
+    S, H, KVH, D, B, NB, MB = _decode_common(q, k_cache, v_cache, block_tables, seq_lens)
+    _want(out, "out", torch.float32, 3, q.device)
+    if tuple(out.shape) != (S, H, D):
+        raise ValueError("out must be [num_seqs, num_heads, head_size]")
+    lib = load_library()
+    rc = lib.pa_decode_v2_noalloc(_p(out), _p(q), _p(k_cache), _p(v_cache), _p(block_tables),
+                                  _p(seq_lens), S, H, KVH, D, B, MB, NB, int(max_num_partitions),
+                                  int(partition_size), float(scale), kv_dtype_of(k_cache),
+                                  float(k_scale), float(v_scale), _stream(q, stream))
+    _check(rc, "pa_decode_v2_noalloc")
+    return out
 
 
 def pa_prefill(out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc,

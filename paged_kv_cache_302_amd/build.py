@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpa.so")
 SOURCES = ["pa_api.hip", "pa_decode.hip", "pa_prefill.hip", "pa_reduce.hip", "pa_cache.hip",
-           "pa_blocks.cpp"]
+           "pa_noalloc.hip", "pa_blocks.cpp"]
 ARCH = "gfx950"
 
 

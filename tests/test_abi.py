@@ -61,7 +61,7 @@ def test_binding_signatures_match_header():
 
 def test_status_strings_and_version():
     lib = pa.load_library()
-    assert lib.pa_abi_version() == 6
+    assert lib.pa_abi_version() == 7
     assert lib.pa_status_str(0) == b"ok"
     for rc in (-1, -2, -3, -4, -5):
         assert len(lib.pa_status_str(rc)) > 5
