@@ -16,7 +16,9 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpa.so")
+# PA_LIBRARY names another build of the same library (e.g. one with host-side
+# sanitizers); by default the in-tree libpa.so
+LIB_PATH = os.environ.get("PA_LIBRARY") or os.path.join(_HERE, "libpa.so")
 
 _c_int = ctypes.c_int
 _c_float = ctypes.c_float
