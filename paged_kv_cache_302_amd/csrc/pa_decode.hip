@@ -97,11 +97,9 @@ struct SeqParts {
     int tail;   // blocks of the last partition when it is partly filled, else 0
 };
 
-// pre >= 0: the length of sequence s < 64, already loaded by the caller
-__device__ __forceinline__ SeqParts seq_parts(const DecodeParams& p, int s, int PB, bool sorted,
-                                              int pre = -1) {
+__device__ __forceinline__ SeqParts seq_parts(const DecodeParams& p, int len, int PB, bool sorted) {
     SeqParts r;
-    r.len = s < p.num_seqs ? (pre >= 0 && s < 64 ? pre : p.seq_lens[s]) : 0;
+    r.len = len;
     r.np = n_parts(r.len, p.partition_size, p.max_num_partitions);
     const int nb = r.len > 0 ? (r.len - 1) / kBlock + 1 : 0;
     const int last = nb - (r.np - 1) * PB;   // blocks of partition np - 1 (if not capped)
@@ -110,72 +108,115 @@ __device__ __forceinline__ SeqParts seq_parts(const DecodeParams& p, int s, int 
     return r;
 }
 
+// The lengths of kLenChunks x 64 consecutive sequences, requested together:
+// lane l of chunk c holds sequence g0 + 64c + l (0 past the last sequence).
+// Every lane loads (the index is clamped), so the requests go out in one
+// round trip and no load waits under a branch.
+#ifndef PA_LEN_CHUNKS
+#define PA_LEN_CHUNKS 4
+#endif
+constexpr int kLenChunks = PA_LEN_CHUNKS;
+constexpr int kLenGroup = 64 * kLenChunks;
+struct Lens {
+    int v[kLenChunks];
+};
+
+__device__ __forceinline__ Lens load_lens(const DecodeParams& p, int g0) {
+    Lens r;
+#pragma unroll
+    for (int c = 0; c < kLenChunks; ++c) {
+        const int sq = g0 + 64 * c + lane_id();
+        const int v = p.seq_lens[min(sq, p.num_seqs - 1)];
+        r.v[c] = sq < p.num_seqs ? v : 0;
+    }
+    return r;
+}
+
+// first: the lengths of the first kLenGroup sequences (load_lens(p, 0));
+// hist: 64 ints of LDS that only this wave uses
 __device__ bool find_partition(const DecodeParams& p, int r, bool sort_tails, int& s_out,
-                               int& p_out, int& L_out, int pre0 = -1) {
+                               int& p_out, int& L_out, const Lens& first, int* hist) {
     const int lane = lane_id();
     const int PB = p.partition_size / kBlock;
     const bool sorted = sort_tails && PB <= 64;
     // 1. full partitions (every partition when the tails are not sorted)
     int base = 0;
-    for (int s0 = 0; s0 < p.num_seqs; s0 += 64) {
-        const SeqParts q = seq_parts(p, s0 + lane, PB, sorted, s0 == 0 ? pre0 : -1);
-        const int nfull = q.np - (q.tail > 0 ? 1 : 0);
-        int incl = nfull;
+    for (int g0 = 0; g0 < p.num_seqs; g0 += kLenGroup) {
+        const Lens ls = g0 == 0 ? first : load_lens(p, g0);
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int t = __shfl_up(incl, off);
-            if (lane >= off) incl += t;
+        for (int c = 0; c < kLenChunks; ++c) {
+            const int s0 = g0 + 64 * c;
+            if (s0 >= p.num_seqs) break;
+            const SeqParts q = seq_parts(p, ls.v[c], PB, sorted);
+            const int nfull = q.np - (q.tail > 0 ? 1 : 0);
+            int incl = nfull;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int t = __shfl_up(incl, off);
+                if (lane >= off) incl += t;
+            }
+            const int total = __builtin_amdgcn_readlane(incl, 63);
+            if (r < base + total) {
+                const unsigned long long mask = __ballot(base + incl > r);
+                const int first_lane = __ffsll((long long)mask) - 1;
+                s_out = s0 + first_lane;
+                p_out = r - base - __builtin_amdgcn_readlane(incl - nfull, first_lane);
+                // the length came with the prefix sum: no second, dependent load
+                L_out = __builtin_amdgcn_readlane(q.len, first_lane);
+                return true;
+            }
+            base += total;
         }
-        const int total = __builtin_amdgcn_readlane(incl, 63);
-        if (r < base + total) {
-            const unsigned long long mask = __ballot(base + incl > r);
-            const int first = __ffsll((long long)mask) - 1;
-            s_out = s0 + first;
-            p_out = r - base - __builtin_amdgcn_readlane(incl - nfull, first);
-            // the length came with the prefix sum: no second, dependent load
-            L_out = __builtin_amdgcn_readlane(q.len, first);
-            return true;
-        }
-        base += total;
     }
     if (!sorted) return false;
-    // 2. tails: lane c counts the tails of c blocks (1 <= c < PB <= 64)
+    // 2. tails: a histogram of the tail sizes in LDS (one atomic add per
+    // sequence), read back as lane c = the number of tails of c blocks
     int j = r - base;
-    int hist = 0;
-    for (int s0 = 0; s0 < p.num_seqs; s0 += 64) {
-        const SeqParts q = seq_parts(p, s0 + lane, PB, true);
-        for (int c = 1; c < PB; ++c) {
-            const int cnt = __popcll(__ballot(q.tail == c));
-            if (lane == c) hist += cnt;
+    hist[lane] = 0;
+    for (int g0 = 0; g0 < p.num_seqs; g0 += kLenGroup) {
+        const Lens ls = g0 == 0 ? first : load_lens(p, g0);
+#pragma unroll
+        for (int c = 0; c < kLenChunks; ++c) {
+            if (g0 + 64 * c >= p.num_seqs) break;
+            const SeqParts q = seq_parts(p, ls.v[c], PB, true);
+            if (q.tail > 0)
+                __hip_atomic_fetch_add(hist + q.tail, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
         }
     }
+    const int cnt = hist[lane];
     // tails of more than c blocks come before class c: a suffix sum over lanes
-    int incl = hist;
+    int incl = cnt;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
         const int t = __shfl_down(incl, off);
         if (lane + off < 64) incl += t;
     }
-    const int above = incl - hist;
-    const unsigned long long hit = __ballot(lane >= 1 && lane < PB && j >= above && j < above + hist);
+    const int above = incl - cnt;
+    const unsigned long long hit = __ballot(lane >= 1 && lane < PB && j >= above && j < above + cnt);
     if (hit == 0) return false;
     const int cls = __ffsll((long long)hit) - 1;
     j -= __builtin_amdgcn_readlane(above, cls);
     // 3. the j-th sequence (in order) whose tail has cls blocks
-    for (int s0 = 0; s0 < p.num_seqs; s0 += 64) {
-        const SeqParts q = seq_parts(p, s0 + lane, PB, true);
-        const unsigned long long m = __ballot(q.tail == cls);
-        const int pc = __popcll(m);
-        if (j < pc) {
-            const int below = __popcll(m & ((1ull << lane) - 1ull));
-            const unsigned long long pick = __ballot(q.tail == cls && below == j);
-            const int first = __ffsll((long long)pick) - 1;
-            s_out = s0 + first;
-            p_out = __builtin_amdgcn_readlane(q.np, first) - 1;
-            L_out = __builtin_amdgcn_readlane(q.len, first);
-            return true;
+    for (int g0 = 0; g0 < p.num_seqs; g0 += kLenGroup) {
+        const Lens ls = g0 == 0 ? first : load_lens(p, g0);
+#pragma unroll
+        for (int c = 0; c < kLenChunks; ++c) {
+            const int s0 = g0 + 64 * c;
+            if (s0 >= p.num_seqs) break;
+            const SeqParts q = seq_parts(p, ls.v[c], PB, true);
+            const unsigned long long m = __ballot(q.tail == cls);
+            const int pc = __popcll(m);
+            if (j < pc) {
+                const int below = __popcll(m & ((1ull << lane) - 1ull));
+                const unsigned long long pick = __ballot(q.tail == cls && below == j);
+                const int first_lane = __ffsll((long long)pick) - 1;
+                s_out = s0 + first_lane;
+                p_out = __builtin_amdgcn_readlane(q.np, first_lane) - 1;
+                L_out = __builtin_amdgcn_readlane(q.len, first_lane);
+                return true;
+            }
+            j -= pc;
         }
-        j -= pc;
     }
     return false;
 }
@@ -195,15 +236,14 @@ __device__ bool find_partition(const DecodeParams& p, int r, bool sort_tails, in
 constexpr int kMaxMembers = 8;
 
 // Tile row i of a unit whose rows start at sequence `lead`: head h0 + i % gsz
-// of sequence lead + i / gsz, for i < M * gsz; with only >= 0 every row reads
-// member `only`'s row instead (the first load, before the members are known).
-// Every row loads a valid query row (indices clamped) so that no load sits
-// under a branch; rows outside `live` are zeroed once the members are known.
+// of sequence lead + i / gsz, for i < M * gsz.  Every row loads a valid query
+// row (indices clamped) so that no load sits under a branch; rows outside
+// `live` are zeroed once the members are known.
 template <class Path>
 __device__ __forceinline__ void load_q_rows(typename Path::QRegs& qr, const DecodeParams& p,
-                                            int lead, int h0, int gsz, int M, int only) {
+                                            int lead, int h0, int gsz, int M) {
     const int i = lane_id() & 15;
-    const int m = only >= 0 ? only : min(i / gsz, M - 1), j = i - (i / gsz) * gsz;
+    const int m = min(i / gsz, M - 1), j = i - (i / gsz) * gsz;
     const int sm = min(lead + m, p.num_seqs - 1);
     Path::load_q_row(qr, p.q + ((size_t)sm * p.num_heads + h0 + min(j, gsz - 1)) * Path::kD, true);
 }
@@ -221,13 +261,16 @@ __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER_EU)))
 #endif
 void pa_decode_kernel(DecodeParams p) {
     extern __shared__ float lds[];
+    __shared__ int s_hist[NW][64];   // v2 partition lookup, one row per wave
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index, uniform
     const int kvhc_count = p.num_kv_heads * p.head_chunks;
     int u = blockIdx.x;
     bool sorted = false;   // v2: largest-first order with the snake over the CUs
-    int pre0 = -1;         // v2, at most 64 sequences: lane s's length, loaded here
+    Lens lens0;            // v2: the first sequences' lengths, for the partition lookup
     if constexpr (V2) {
+        lens0 = load_lens(p, 0);
         sorted = p.resident > 0;
+
         if (sorted) {
             // a backward round reverses the CUs inside each XCD (workgroups
             // alternate over the 8 XCDs), so a unit keeps its XCD and L2
@@ -246,12 +289,11 @@ void pa_decode_kernel(DecodeParams p) {
             // on one XCD.  The lengths loaded for the check serve the
             // partition lookup below.
             const int ls = min(lane_id(), p.num_seqs - 1);
-            pre0 = p.seq_lens[ls];
+            const int l0 = lens0.v[0];
             const int f0 = p.block_tables[(size_t)ls * p.max_blocks_per_seq];
-            const int f1 = __shfl_down(f0, 1), l1 = __shfl_down(pre0, 1);
+            const int f1 = __shfl_down(f0, 1), l1 = __shfl_down(l0, 1);
             const bool shared =
-                __ballot(lane_id() + 1 < p.num_seqs && f0 == f1 && pre0 > 0 && l1 > 0) != 0;
-            if (lane_id() >= p.num_seqs) pre0 = 0;
+                __ballot(lane_id() + 1 < p.num_seqs && f0 == f1 && l0 > 0 && l1 > 0) != 0;
             if (!shared) {
                 const int gx = kXcds * kvhc_count;
                 const int g = u / gx, rem = u - g * gx;
@@ -269,7 +311,10 @@ void pa_decode_kernel(DecodeParams p) {
 
     int s, part = 0, L;
     if constexpr (V2) {
-        if (!find_partition(p, r_unit, sorted, s, part, L, pre0)) return;
+#ifdef PA_SORT_ALWAYS
+        sorted = true;
+#endif
+        if (!find_partition(p, r_unit, sorted, s, part, L, lens0, s_hist[w])) return;
     } else {
         s = r_unit;
         L = p.seq_lens[s];
@@ -313,19 +358,21 @@ void pa_decode_kernel(DecodeParams p) {
     const NeighbourIds nbr = neighbour_ids(p, s, blk_begin);
 #endif
     typename Path::QRegs qr;
-    if constexpr (Path::kHeads == 16) load_q_rows<Path>(qr, p, lead, h0, gsz, M, self);
+    // every member's query rows (rows of members not computed here are
+    // zeroed once the members are known)
+    if constexpr (Path::kHeads == 16) load_q_rows<Path>(qr, p, lead, h0, gsz, M);
     else Path::load_q(qr, p, s, h0, nh);
-    // the set's lengths and its members' first table entries of the partition
-    // (scalar loads); the other entries are read only if a member's first one
-    // equals the leader's
-    int mlen[kMaxMembers], mfirst[kMaxMembers];
+    // the set's lengths (scalar loads) and every member's table entries over
+    // the partition (lane j: entry blk_begin + j), requested together with
+    // the rest, so the comparison below waits on no further round trip
+    int mlen[kMaxMembers], mrow[kMaxMembers];
     if (M > 1) {
-        const int b0 = min(blk_begin, mbps - 1);
+        const int bi = min(blk_begin + lane_id(), mbps - 1);
 #pragma unroll
         for (int i = 0; i < kMaxMembers; ++i) {
             const int f = min(lead + min(i, M - 1), p.num_seqs - 1);
             mlen[i] = p.seq_lens[f];
-            mfirst[i] = p.block_tables[(size_t)f * mbps + b0];
+            mrow[i] = p.block_tables[(size_t)f * mbps + bi];
         }
     }
     // keep the scheduler from placing a use (and so a wait) between the loads
@@ -340,26 +387,17 @@ void pa_decode_kernel(DecodeParams p) {
             return len > part * PS && (len - 1) / PS + 1 <= p.max_num_partitions &&
                    (len + kBlock - 1) / kBlock <= mbps;
         };
+        // a member shares the leader's unit when its token range in the
+        // partition and every table entry over it equal the leader's
         const int tend = min(mlen[0], (part + 1) * PS);
-        unsigned cand = 0;   // members whose first entry and token range match the leader's
+        const int nblk = (tend - part * PS + kBlock - 1) / kBlock;   // <= 64 blocks
+        unsigned match = 0;
 #pragma unroll
         for (int i = 0; i < kMaxMembers; ++i) {
             const bool ok = i < M && lead + i < p.num_seqs && fits(mlen[0]) && fits(mlen[i]) &&
-                            min(mlen[i], (part + 1) * PS) == tend && mfirst[i] == mfirst[0];
-            cand |= ok ? 1u << i : 0u;
-        }
-        unsigned match = 0;
-        if (cand > 1u) {   // someone besides the leader: compare the whole partition
-            const int nblk = (tend - part * PS + kBlock - 1) / kBlock;
-            const int bi = min(blk_begin + lane_id(), mbps - 1);
-            const int e0 = p.block_tables[(size_t)lead * mbps + bi];
-#pragma unroll
-            for (int i = 0; i < kMaxMembers; ++i) {
-                const int f = min(lead + min(i, M - 1), p.num_seqs - 1);
-                const int e = p.block_tables[(size_t)f * mbps + bi];
-                const bool same = __ballot(lane_id() < nblk && e != e0) == 0;
-                match |= (((cand >> i) & 1u) && same) ? 1u << i : 0u;
-            }
+                            min(mlen[i], (part + 1) * PS) == tend;
+            const bool same = __ballot(lane_id() < nblk && mrow[i] != mrow[0]) == 0;
+            match |= (ok && same) ? 1u << i : 0u;
         }
         if (self != 0 && ((match >> self) & 1u)) return;   // the leader computes it
         members = self == 0 ? (match | 1u) : 1u << self;
@@ -367,7 +405,6 @@ void pa_decode_kernel(DecodeParams p) {
     // rows of the tile this unit writes
     auto live = [&](int i) { return i < nrows && ((members >> (i / gsz)) & 1u); };
     if constexpr (Path::kHeads == 16) {
-        if (members != 1u << self) load_q_rows<Path>(qr, p, lead, h0, gsz, M, -1);
         const int i = lane_id() & 15;
         const bool keep = live(i);
 #pragma unroll
@@ -430,26 +467,37 @@ void pa_decode_kernel(DecodeParams p) {
         auto live = [&](int j) { return j < n ? TB : 0; };
         auto walk = [&](auto nt_tag) {
             constexpr bool NTL = decltype(nt_tag)::value;
-            typename Path::Tile ta, tb;
-            int id = phys(0, 0);
-            Path::template load<NTL>(ta, tile_k(id), tile_v(id), live(0));
+            // a ring of DP tiles: block k lives in t[k % DP], and block
+            // k + DP - 1 is requested just before block k is processed
+            constexpr int DP = Path::kDepth;
+            static_assert(DP == 2 || DP == 4, "the ring must divide a 64-entry window");
+            typename Path::Tile t[DP];
+#pragma unroll
+            for (int j = 0; j < DP - 1; ++j) {
+                const int id = phys(0, j);
+                Path::template load<NTL>(t[j], tile_k(id), tile_v(id), live(j));
+            }
             int k = 0;
             for (int kw = 0;; kw += 64) {
                 const int pend = table_window<NW>(row, first, n, kw + 128, mbps);
-                const int kend = min(n, kw + 64) & ~1;   // pairs; an odd last block is the tail
-                for (; k < kend; k += 2) {
-                    id = phys(kw, k + 1);
-                    Path::template load<NTL>(tb, tile_k(id), tile_v(id), TB);
-                    Path::process(st, ta, qr, valid(k), sl2);
-                    id = phys(kw, k + 2);
-                    Path::template load<NTL>(ta, tile_k(id), tile_v(id), live(k + 2));
-                    Path::process(st, tb, qr, valid(k + 1), sl2);
+                const int kend = min(n, kw + 64) & ~(DP - 1);   // whole rings; the rest is the tail
+                for (; k < kend; k += DP) {
+#pragma unroll
+                    for (int j = 0; j < DP; ++j) {
+                        const int id = phys(kw, k + j + DP - 1);
+                        Path::template load<NTL>(t[(j + DP - 1) % DP], tile_k(id), tile_v(id),
+                                                 live(k + j + DP - 1));
+                        Path::process(st, t[j], qr, valid(k + j), sl2);
+                    }
                 }
                 if (kw + 64 >= n) break;
                 cur = nxt;
                 nxt = pend;
             }
-            if (k < n) Path::process(st, ta, qr, valid(k), sl2);   // odd block count
+            // the last n - k < DP blocks, already requested into t[0 ..]
+#pragma unroll
+            for (int j = 0; j < DP - 1; ++j)
+                if (k + j < n) Path::process(st, t[j], qr, valid(k + j), sl2);
         };
 #if PA_LOAD_POLICY == 1
         if (cached) walk(std::false_type{});   // cached loads

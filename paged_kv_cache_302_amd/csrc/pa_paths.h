@@ -19,6 +19,14 @@
 #define PA_LOAD_POLICY 1      // tile loads: 0 = cached, 1 = per unit (see load policy), 2 = nontemporal
 #endif
 
+// Tiles in flight per wave in the decode walk (2 or 4), for fp16 and fp8 pools.
+#ifndef PA_DEPTH_F16
+#define PA_DEPTH_F16 2
+#endif
+#ifndef PA_DEPTH_F8
+#define PA_DEPTH_F8 2
+#endif
+
 namespace pa {
 
 // Tile loads.  K/V that only this unit reads is streamed: nontemporal loads
@@ -116,6 +124,7 @@ struct MfmaPath {
     static constexpr int kHeads = 16;
     static constexpr int kElem = 2;     // bytes per cache element (fp16)
     static constexpr int kD = D;
+    static constexpr int kDepth = PA_DEPTH_F16;
 
     struct Tile {
         f16x8 k[KC];   // lane (g,i): K[t=i][d = 32c + 8g .. +7]
@@ -243,6 +252,7 @@ struct ValuPath {
     static constexpr int KC = D / 32;
     static constexpr int kHeads = 1;
     static constexpr int kElem = 2;
+    static constexpr int kDepth = PA_DEPTH_F16;
 
     struct Tile {
         f16x8 k[KC];   // lane l: K[t = l%16][d = 32c + 8(l/16) .. +7]
@@ -359,6 +369,7 @@ struct MfmaPath8 : MfmaPath<D> {
     static constexpr int KR = D / 64;   // 16-byte K chunks per lane
     static constexpr int NT = D / 16;
     static constexpr int kElem = 1;
+    static constexpr int kDepth = PA_DEPTH_F8;
 
     struct Tile {
         u32x4 k[KR];    // lane (g,i): K codes of token i, dims 16(g + 4r) .. +15
@@ -462,6 +473,7 @@ struct ValuPath8 {
     static constexpr int KR = D / 64;
     static constexpr int kHeads = 1;
     static constexpr int kElem = 1;
+    static constexpr int kDepth = PA_DEPTH_F8;
 
     struct Tile {
         u32x4 k[KR];   // lane l: K codes of token l%16, dims 16(l/16 + 4r) .. +15
