@@ -278,6 +278,44 @@ def timed_steps(args, step, n_events):
     return ms, evs, wall
 
 
+def scrubbed_pass(step, n_events, steps):
+    """`steps` more steps after the timed region, each behind a 1 GiB read
+    that leaves no K/V in the Infinity Cache or L2 (a read, so no dirty
+    lines are left for the step to write back): the cold-cache kernel times
+    the roofline is taken from.  Returns the per-step event lists."""
+    import torch
+    dev = torch.device("cuda:0")
+    scrub_buf = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    scrub_sum = torch.empty((), dtype=torch.float32, device=dev)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_events)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for k in range(steps):
+        torch.sum(scrub_buf, dim=0, out=scrub_sum)
+        step(evs[k])
+    torch.cuda.synchronize()
+    del scrub_buf
+    return evs
+
+
+def cold_and_warm(args, step, n_events, evs, i):
+    """Mean duration (s) of kernel i (events i, i + 1) over the scrubbed pass
+    (the timed steps themselves under --scrub) and over the warm timed
+    steps, and the scrubbed pass's events."""
+    cold = evs if args.scrub else scrubbed_pass(step, n_events, args.steps)
+    mean = lambda ev: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in ev])) / 1e3
+    return mean(cold), mean(evs), cold
+
+
+def roofline_entry(kname, nbytes, secs, traffic=None, cache="cold"):
+    achieved = nbytes / secs / 1e9
+    r = {"kernel": kname, "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+         "algorithmic_bytes_per_launch": nbytes, "avg_launch_us": round(secs * 1e6, 2)}
+    r["cache"] = ("cold: mean over launches each behind a 1 GiB read scrub, HIP events"
+                  if cache == "cold" else "warm: mean over the back-to-back timed steps, HIP events")
+    return r
+
+
 def main_fork(args):
     """First decode step after a parallel-sampling fork (see the module
     docstring)."""
@@ -339,18 +377,17 @@ def main_fork(args):
             ev[4].record(stream)
 
     ms_per_step, evs, wall = timed_steps(args, step, 5)
+    dec_s, dec_warm_s, cold = cold_and_warm(args, step, 5, evs, 2)
     if args.copy_calibration:
         copy_calibration(dev)
     med = lambda i: float(np.median([e[i].elapsed_time(e[i + 1]) for e in evs]))
     copy_s = med(0) / 1e3
-    dec_s = float(np.mean([e[2].elapsed_time(e[3]) for e in evs])) / 1e3
     block_bytes = KVH * D * B * 2                       # one block of one pool
     distinct = len(np.unique(tables[tables >= 0]))
     unique_bytes = distinct * 2 * block_bytes           # whole K and V tiles the decode reads
     kv_bytes = int(lens.astype(np.int64).sum()) * KVH * D * 4
     copy_bytes = len(copies) * 2 * block_bytes * 2      # read + write, both pools
     value = kv_bytes / (ms_per_step / 1e3) / 1e9
-    achieved = unique_bytes / dec_s / 1e9
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -382,17 +419,11 @@ def main_fork(args):
             "pa_decode_v2": round(med(2) * 1e3, 2),
             "pa_reduce": round(med(3) * 1e3, 2),
         },
-        "roofline": {
-            "kernel": "pa_decode_v2",
-            "bound": "hbm",
-            "achieved": round(achieved, 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": read_traffic("pa_decode_v2", "fork"),
-            "algorithmic_bytes_per_launch": unique_bytes,
-            "avg_launch_us": round(dec_s * 1e6, 2),
-        },
+        "kernels_us_cold": {"pa_decode_v2": round(float(np.median(
+            [e[2].elapsed_time(e[3]) for e in cold])) * 1e3, 2)},
+        "roofline": roofline_entry("pa_decode_v2", unique_bytes, dec_s,
+                                   read_traffic("pa_decode_v2", "fork")),
+        "roofline_warm": roofline_entry("pa_decode_v2", unique_bytes, dec_warm_s, cache="warm"),
         "copy_blocks": {
             "bytes_per_launch": copy_bytes,
             "achieved_gbs": round(copy_bytes / copy_s / 1e9, 2),
@@ -625,28 +656,9 @@ def main():
         if ev is not None:
             ev[3].record(stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    scrub_buf = torch.ones(1 << 28, dtype=torch.float32, device=dev) if args.scrub else None
-    scrub_sum = torch.empty((), dtype=torch.float32, device=dev)
-
     # timed region: exactly `steps` steps, synchronised on both sides
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for k in range(args.steps):
-        if scrub_buf is not None:
-            torch.sum(scrub_buf, dim=0, out=scrub_sum)
-        step(evs[k])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
-    wall_ms_per_step = elapsed * 1e3 / args.steps
-    if scrub_buf is not None:
-        ms_per_step = float(np.mean([e[0].elapsed_time(e[3]) for e in evs]))
-    else:
-        ms_per_step = wall_ms_per_step
+    ms_per_step, evs, wall_ms_per_step = timed_steps(args, step, 4)
+    dec_avg_s, dec_warm_s, cold = cold_and_warm(args, step, 4, evs, 1)
 
     if args.copy_calibration:
         copy_calibration(dev)
@@ -654,7 +666,7 @@ def main():
     cache_ms = [e[0].elapsed_time(e[1]) for e in evs]
     decode_ms = [e[1].elapsed_time(e[2]) for e in evs]
     reduce_ms = [e[2].elapsed_time(e[3]) for e in evs]
-    dec_avg_s = float(np.mean(decode_ms)) / 1e3
+    cold_ms = [[e[i].elapsed_time(e[i + 1]) for e in cold] for i in range(3)]
     copy_gbs = device_copy_gbs(dev)
 
     esz = 1 if fp8 else 2
@@ -663,6 +675,7 @@ def main():
     value = kv_bytes / (ms_per_step / 1e3) / 1e9
     achieved = unique_bytes / dec_avg_s / 1e9
     kname = "pa_decode_v2" if args.kernel == "v2" else "pa_decode_v1"
+    names = ["reshape_and_cache", kname] + (["pa_reduce"] if args.kernel == "v2" else [])
     traffic = read_traffic(kname, args.workload + ("_fp8" if fp8 else ""))
 
     res = {
@@ -705,20 +718,12 @@ def main():
             kname: pct(decode_ms),
             **({"pa_reduce": pct(reduce_ms)} if args.kernel == "v2" else {}),
         },
+        "kernels_us_cold": {n: round(float(np.median(cold_ms[i])) * 1e3, 2) for i, n in enumerate(names)},
         # second denominator: a measured device-to-device copy (read + write bytes)
         "device_copy_gbs": round(copy_gbs, 1),
         "pct_of_device_copy": round(100 * achieved / copy_gbs, 2),
-        "roofline": {
-            "kernel": kname,
-            "bound": "hbm",
-            "achieved": round(achieved, 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic,
-            "algorithmic_bytes_per_launch": unique_bytes,
-            "avg_launch_us": round(dec_avg_s * 1e6, 2),
-        },
+        "roofline": roofline_entry(kname, unique_bytes, dec_avg_s, traffic),
+        "roofline_warm": roofline_entry(kname, unique_bytes, dec_warm_s, cache="warm"),
         "timing": ("HIP events per step, 1 GiB read scrub between steps (wall %.4f ms/step incl. scrub)"
                    % wall_ms_per_step) if args.scrub else "wall clock over the timed steps",
         "input_gen_s": round(gen_s, 2),
