@@ -51,6 +51,7 @@
 // gets exactly 1 and a one-token sequence returns its V bit-exactly.
 #include <math.h>
 
+#include <algorithm>
 #include <atomic>
 #include <type_traits>
 
@@ -254,7 +255,9 @@ __device__ __forceinline__ void load_q_rows(typename Path::QRegs& qr, const Deco
 #ifndef PA_WAVES_PER_EU
 #define PA_WAVES_PER_EU 0
 #endif
-template <class Path, int D, int NW, bool V2>
+// RING: the tiles of a one-wave unit go through a two-slot LDS ring instead
+// of registers (fp16 MFMA path; see the walk below)
+template <class Path, int D, int NW, bool V2, bool RING = false>
 __global__ __launch_bounds__(64 * NW)
 #if PA_WAVES_PER_EU
 __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER_EU)))
@@ -499,11 +502,57 @@ void pa_decode_kernel(DecodeParams p) {
             for (int j = 0; j < DP - 1; ++j)
                 if (k + j < n) Path::process(st, t[j], qr, valid(k + j), sl2);
         };
+        // The LDS ring (units of grids the device holds at once, where it
+        // measured faster: fewer registers per wave; elsewhere the register
+        // ring is faster).  Block k + 1 is requested into the other slot just
+        // before block k is read out of its slot and processed.  The compiler
+        // does not track when a load into LDS has landed, so the waits are
+        // explicit: loads complete in issue order, so with block k + 1's
+        // kSlotLoads loads issued, block k's have landed once at most that
+        // many are outstanding; with no request after block k, all of them.
+        // Block k's slot is refilled (with block k + 2) only after block k
+        // has been read out and processed.
+        auto walk_ring = [&](auto nt_tag) {
+            if constexpr (RING) {
+                constexpr bool NTL = decltype(nt_tag)::value;
+                char* ring = reinterpret_cast<char*>(lds);
+                auto slot = [&](int k) { return ring + (k & 1) * Path::kSlot; };
+                if (n > 0) {
+                    const int id = phys(0, 0);
+                    Path::template load_lds<NTL>(slot(0), tile_k(id), tile_v(id));
+                }
+                for (int kw = 0;; kw += 64) {
+                    const int pend = table_window<NW>(row, first, n, kw + 128, mbps);
+                    const int kend = min(n, kw + 64);
+                    for (int k = kw; k < kend; ++k) {
+                        if (k + 1 < n) {
+                            const int id = phys(kw, k + 1);
+                            Path::template load_lds<NTL>(slot(k + 1), tile_k(id), tile_v(id));
+                            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(Path::kSlotLoads) : "memory");
+                        } else {
+                            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                        }
+                        typename Path::Tile t;
+                        Path::read_lds(t, slot(k));
+                        Path::process(st, t, qr, valid(k), sl2);
+                    }
+                    if (kw + 64 >= n) break;
+                    cur = nxt;
+                    nxt = pend;
+                }
+            }
+        };
 #if PA_LOAD_POLICY == 1
-        if (cached) walk(std::false_type{});   // cached loads
-        else walk(std::true_type{});
+        if constexpr (RING) {
+            if (cached) walk_ring(std::false_type{});
+            else walk_ring(std::true_type{});
+        } else {
+            if (cached) walk(std::false_type{});   // cached loads
+            else walk(std::true_type{});
+        }
 #else
-        walk(std::integral_constant<bool, PA_LOAD_POLICY == 2>{});
+        if constexpr (RING) walk_ring(std::integral_constant<bool, PA_LOAD_POLICY == 2>{});
+        else walk(std::integral_constant<bool, PA_LOAD_POLICY == 2>{});
 #endif
     }
 
@@ -625,21 +674,39 @@ static int launch_nw(int NW, const DecodeParams& p0, int grid, int nh_max, hipSt
         // free up, and the plain order keeps the units that share blocks
         // (forks, samples of one prompt) running together.  The occupancy
         // of each (wave count, LDS size) is asked for once.
-        static std::atomic<long long> occ_cache[4];   // (lds << 8) | (workgroups per CU + 1)
-        const int slot = NW == 1 ? 0 : NW == 2 ? 1 : NW == 4 ? 2 : 3;
-        long long c = occ_cache[slot].load(std::memory_order_relaxed);
-        int per_cu = 0;
-        if (c != 0 && (size_t)(c >> 8) == lds) {
-            per_cu = (int)(c & 0xff) - 1;
-        } else {
-            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64 * NW, lds) != hipSuccess) {
-                (void)hipGetLastError();
-                per_cu = 0;
+        static std::atomic<long long> occ_cache[5];   // (lds << 8) | (workgroups per CU + 1)
+        auto resident_slots = [&](const void* f, int threads, size_t lds_bytes, int slot) {
+            long long c = occ_cache[slot].load(std::memory_order_relaxed);
+            int per_cu = 0;
+            if (c != 0 && (size_t)(c >> 8) == lds_bytes) {
+                per_cu = (int)(c & 0xff) - 1;
+            } else {
+                if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, threads, lds_bytes) != hipSuccess) {
+                    (void)hipGetLastError();
+                    per_cu = 0;
+                }
+                if (per_cu >= 0 && per_cu < 255)
+                    occ_cache[slot].store(((long long)lds_bytes << 8) | (per_cu + 1), std::memory_order_relaxed);
             }
-            if (per_cu >= 0 && per_cu < 255)
-                occ_cache[slot].store(((long long)lds << 8) | (per_cu + 1), std::memory_order_relaxed);
+            return (long long)per_cu * p.num_cus;
+        };
+        // one-wave fp16 MFMA units of a grid the device holds at once walk
+        // their tiles through the LDS ring
+        if constexpr (V2 && Path::kHeads == 16 && Path::kElem == 2) {
+            if (NW == 1) {
+                const size_t lds_ring = std::max(lds, (size_t)2 * Path::kSlot);
+                const void* fr = reinterpret_cast<const void*>(&pa_decode_kernel<Path, D, 1, true, true>);
+                const long long res = resident_slots(fr, 64, lds_ring, 4);
+                if (grid <= res) {
+                    p.resident = (int)res;
+                    hipLaunchKernelGGL((pa_decode_kernel<Path, D, 1, true, true>), dim3(grid), dim3(64),
+                                       lds_ring, st, p);
+                    return launch_status();
+                }
+            }
         }
-        const long long resident = (long long)per_cu * p.num_cus;
+        const int slot = NW == 1 ? 0 : NW == 2 ? 1 : NW == 4 ? 2 : 3;
+        const long long resident = resident_slots(fn, 64 * NW, lds, slot);
         p.resident = grid <= resident ? (int)resident : 0;
     }
     switch (NW) {

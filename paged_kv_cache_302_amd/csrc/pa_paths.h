@@ -187,6 +187,36 @@ struct MfmaPath {
         for (int nt = 0; nt < NT; ++nt) t.v[nt] = ld_tile<NTL, f16x4>(rv, 8 * (4 * i + g + 64 * nt));
     }
 
+    // LDS-staged tiles: the K and V tiles of one block in an LDS slot
+    // (K at 0, V at D*16*2 bytes, each in its pool layout), written by loads
+    // that go from global memory to LDS without passing through registers;
+    // lane l's 16 bytes of each 1 KiB piece land at 16 l.
+    static constexpr int kTileBytes = D * kBlock * 2;
+    static constexpr int kSlot = 2 * kTileBytes;
+    static constexpr int kSlotLoads = kSlot / 1024;   // load instructions per slot
+    template <bool NTL>
+    __device__ __forceinline__ static void load_lds(char* slot, const char* kt, const char* vt) {
+        const int l = lane_id();
+#pragma unroll
+        for (int c = 0; c < kTileBytes / 1024; ++c) {
+            __builtin_amdgcn_global_load_lds(static_cast<const void*>(kt + 16 * l + 1024 * c),
+                                             (__attribute__((address_space(3))) void*)(slot + 1024 * c),
+                                             16, 0, NTL ? 2 : 0);
+            __builtin_amdgcn_global_load_lds(static_cast<const void*>(vt + 16 * l + 1024 * c),
+                                             (__attribute__((address_space(3))) void*)(slot + kTileBytes + 1024 * c),
+                                             16, 0, NTL ? 2 : 0);
+        }
+    }
+    // a slot's tiles into the MFMA operand registers (same layout as load())
+    __device__ __forceinline__ static void read_lds(Tile& t, const char* slot) {
+        const int l = lane_id(), i = l & 15, g = l >> 4;
+#pragma unroll
+        for (int c = 0; c < KC; ++c) t.k[c] = *reinterpret_cast<const f16x8*>(slot + 16 * (l + 64 * c));
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+            t.v[nt] = *reinterpret_cast<const f16x4*>(slot + kTileBytes + 8 * (4 * i + g + 64 * nt));
+    }
+
     // nvalid: tokens of the block inside the sequence (the rest is never
     // read), masked to -inf before the softmax.
     __device__ __forceinline__ static void process(State& st, Tile& t, const QRegs& qr,
