@@ -256,7 +256,7 @@ __device__ __forceinline__ void load_q_rows(typename Path::QRegs& qr, const Deco
 #define PA_WAVES_PER_EU 0
 #endif
 // RING: the tiles of a one-wave unit go through a two-slot LDS ring instead
-// of registers (fp16 MFMA path; see the walk below)
+// of registers (MFMA paths; see the walk below)
 template <class Path, int D, int NW, bool V2, bool RING = false>
 __global__ __launch_bounds__(64 * NW)
 #if PA_WAVES_PER_EU
@@ -690,9 +690,9 @@ static int launch_nw(int NW, const DecodeParams& p0, int grid, int nh_max, hipSt
             }
             return (long long)per_cu * p.num_cus;
         };
-        // one-wave fp16 MFMA units of a grid the device holds at once walk
-        // their tiles through the LDS ring
-        if constexpr (V2 && Path::kHeads == 16 && Path::kElem == 2) {
+        // one-wave MFMA units of a grid the device holds at once walk their
+        // tiles through the LDS ring
+        if constexpr (V2 && Path::kRing) {
             if (NW == 1) {
                 const size_t lds_ring = std::max(lds, (size_t)2 * Path::kSlot);
                 const void* fr = reinterpret_cast<const void*>(&pa_decode_kernel<Path, D, 1, true, true>);

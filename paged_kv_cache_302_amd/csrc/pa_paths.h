@@ -56,6 +56,25 @@ __device__ __forceinline__ T ld_tile(__amdgpu_buffer_rsrc_t r, int off) {
         return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, cpol));
 }
 
+// An LDS slot holding the K and V tiles of one block (TB bytes each, K at 0,
+// V at TB, each in its pool layout), written by loads that go from global
+// memory to LDS without passing through registers: lane l's 16 bytes of each
+// 1 KiB piece land at 16 l.  The compiler does not track when such loads have
+// landed; the caller waits on the load count.
+template <bool NTL, int TB>
+__device__ __forceinline__ void load_slot(char* slot, const char* kt, const char* vt) {
+    const int l = lane_id();
+#pragma unroll
+    for (int c = 0; c < TB / 1024; ++c) {
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(kt + 16 * l + 1024 * c),
+                                         (__attribute__((address_space(3))) void*)(slot + 1024 * c), 16, 0,
+                                         NTL ? 2 : 0);
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(vt + 16 * l + 1024 * c),
+                                         (__attribute__((address_space(3))) void*)(slot + TB + 1024 * c), 16,
+                                         0, NTL ? 2 : 0);
+    }
+}
+
 // Results are written once and not re-read by this kernel.  Plain stores
 // allocate in L2 and reach HBM mid-stream, where each write burst costs a
 // read/write turnaround: the partials of a 3.5 GB long-context call (27 MB)
@@ -187,27 +206,16 @@ struct MfmaPath {
         for (int nt = 0; nt < NT; ++nt) t.v[nt] = ld_tile<NTL, f16x4>(rv, 8 * (4 * i + g + 64 * nt));
     }
 
-    // LDS-staged tiles: the K and V tiles of one block in an LDS slot
-    // (K at 0, V at D*16*2 bytes, each in its pool layout), written by loads
-    // that go from global memory to LDS without passing through registers;
-    // lane l's 16 bytes of each 1 KiB piece land at 16 l.
+    // LDS-staged tiles (load_slot): a slot's tiles read into the MFMA
+    // operand registers, in the same layout as load()
+    static constexpr bool kRing = true;
     static constexpr int kTileBytes = D * kBlock * 2;
     static constexpr int kSlot = 2 * kTileBytes;
     static constexpr int kSlotLoads = kSlot / 1024;   // load instructions per slot
     template <bool NTL>
     __device__ __forceinline__ static void load_lds(char* slot, const char* kt, const char* vt) {
-        const int l = lane_id();
-#pragma unroll
-        for (int c = 0; c < kTileBytes / 1024; ++c) {
-            __builtin_amdgcn_global_load_lds(static_cast<const void*>(kt + 16 * l + 1024 * c),
-                                             (__attribute__((address_space(3))) void*)(slot + 1024 * c),
-                                             16, 0, NTL ? 2 : 0);
-            __builtin_amdgcn_global_load_lds(static_cast<const void*>(vt + 16 * l + 1024 * c),
-                                             (__attribute__((address_space(3))) void*)(slot + kTileBytes + 1024 * c),
-                                             16, 0, NTL ? 2 : 0);
-        }
+        load_slot<NTL, kTileBytes>(slot, kt, vt);
     }
-    // a slot's tiles into the MFMA operand registers (same layout as load())
     __device__ __forceinline__ static void read_lds(Tile& t, const char* slot) {
         const int l = lane_id(), i = l & 15, g = l >> 4;
 #pragma unroll
@@ -283,6 +291,7 @@ struct ValuPath {
     static constexpr int kHeads = 1;
     static constexpr int kElem = 2;
     static constexpr int kDepth = PA_DEPTH_F16;
+    static constexpr bool kRing = false;
 
     struct Tile {
         f16x8 k[KC];   // lane l: K[t = l%16][d = 32c + 8(l/16) .. +7]
@@ -451,6 +460,9 @@ struct MfmaPath8 : MfmaPath<D> {
         for (int nt = 0; nt < NT; ++nt) t.v[nt] = ld_tile<NTL, uint32_t>(rv, 16 * (16 * nt + i) + 4 * g);
     }
 
+    // no LDS ring for fp8 tiles: measured no faster than the register ring
+    static constexpr bool kRing = false;
+
     __device__ __forceinline__ static void process(typename Base::State& st, Tile& t,
                                                    const QRegs& qr, int nvalid, float sl2) {
         const int l = lane_id(), g = l >> 4;
@@ -504,6 +516,7 @@ struct ValuPath8 {
     static constexpr int kHeads = 1;
     static constexpr int kElem = 1;
     static constexpr int kDepth = PA_DEPTH_F8;
+    static constexpr bool kRing = false;
 
     struct Tile {
         u32x4 k[KR];   // lane l: K codes of token l%16, dims 16(l/16 + 4r) .. +15
