@@ -690,15 +690,15 @@ static int launch_nw(int NW, const DecodeParams& p0, int grid, int nh_max, hipSt
             }
             return (long long)per_cu * p.num_cus;
         };
-        // one-wave MFMA units of a grid the device holds at once walk their
-        // tiles through the LDS ring
+        // one-wave MFMA units walk their tiles through the LDS ring: fp16
+        // tiles when the device holds the whole grid at once, fp8 tiles always
         if constexpr (V2 && Path::kRing) {
             if (NW == 1) {
                 const size_t lds_ring = std::max(lds, (size_t)2 * Path::kSlot);
                 const void* fr = reinterpret_cast<const void*>(&pa_decode_kernel<Path, D, 1, true, true>);
                 const long long res = resident_slots(fr, 64, lds_ring, 4);
-                if (grid <= res) {
-                    p.resident = (int)res;
+                if (grid <= res || Path::kRingAll) {
+                    p.resident = grid <= res ? (int)res : 0;
                     hipLaunchKernelGGL((pa_decode_kernel<Path, D, 1, true, true>), dim3(grid), dim3(64),
                                        lds_ring, st, p);
                     return launch_status();

@@ -207,8 +207,11 @@ struct MfmaPath {
     }
 
     // LDS-staged tiles (load_slot): a slot's tiles read into the MFMA
-    // operand registers, in the same layout as load()
+    // operand registers, in the same layout as load(); with fp16 tiles the
+    // ring takes only grids the device holds at once (measured faster there,
+    // slower on larger grids of short units)
     static constexpr bool kRing = true;
+    static constexpr bool kRingAll = false;
     static constexpr int kTileBytes = D * kBlock * 2;
     static constexpr int kSlot = 2 * kTileBytes;
     static constexpr int kSlotLoads = kSlot / 1024;   // load instructions per slot
@@ -460,8 +463,26 @@ struct MfmaPath8 : MfmaPath<D> {
         for (int nt = 0; nt < NT; ++nt) t.v[nt] = ld_tile<NTL, uint32_t>(rv, 16 * (16 * nt + i) + 4 * g);
     }
 
-    // no LDS ring for fp8 tiles: measured no faster than the register ring
-    static constexpr bool kRing = false;
+    // LDS-staged tiles (load_slot), read as load() would; with fp8 tiles the
+    // ring takes every grid (its 16-byte V loads against 4-byte ones in
+    // registers)
+    static constexpr bool kRing = true;
+    static constexpr bool kRingAll = true;
+    static constexpr int kTileBytes = D * kBlock;
+    static constexpr int kSlot = 2 * kTileBytes;
+    static constexpr int kSlotLoads = kSlot / 1024;
+    template <bool NTL>
+    __device__ __forceinline__ static void load_lds(char* slot, const char* kt, const char* vt) {
+        load_slot<NTL, kTileBytes>(slot, kt, vt);
+    }
+    __device__ __forceinline__ static void read_lds(Tile& t, const char* slot) {
+        const int l = lane_id(), i = l & 15, g = l >> 4;
+#pragma unroll
+        for (int r = 0; r < KR; ++r) t.k[r] = *reinterpret_cast<const u32x4*>(slot + 16 * (l + 64 * r));
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+            t.v[nt] = *reinterpret_cast<const uint32_t*>(slot + kTileBytes + 16 * (16 * nt + i) + 4 * g);
+    }
 
     __device__ __forceinline__ static void process(typename Base::State& st, Tile& t,
                                                    const QRegs& qr, int nvalid, float sl2) {
