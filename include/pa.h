@@ -220,8 +220,9 @@ PA_API int pa_decode_v2_noalloc(float* out, const void* q, const void* k_cache,
  *                   is set to NaN and nothing outside is read or written
  *   total_q         rows of q and out (>= 0; 0 enqueues nothing)
  *   max_query_len   >= every n (sizes the grid; 0 enqueues nothing); rows of a
- *                   sequence beyond the first max_query_len (rounded up to
- *                   the tile) are set to NaN
+ *                   sequence beyond the first max_query_len, rounded up to
+ *                   the tile of 4 x 32/G query tokens (4 x 2 for G >= 16),
+ *                   are set to NaN
  *   other arguments as in pa_decode_v1.  n > L, a block id outside the pool
  *   or L beyond the table row gives NaN rows for that sequence.
  */

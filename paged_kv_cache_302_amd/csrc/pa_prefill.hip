@@ -131,8 +131,8 @@ struct MfmaGroups {
     // exp2(s * sl2 - m).  sl2 > 0, so the max of the scaled scores is the
     // scaled max.
     template <int NB>
-    __device__ __forceinline__ static void weights_group(State& st, int gr, const f32x4 (&s)[NB][NG],
-                                                         float sl2, f16x4 (&p)[NB]) {
+    __device__ __forceinline__ static void raise_max(State& st, int gr, const f32x4 (&s)[NB][NG],
+                                                     float sl2) {
         float v = fmaxf(fmaxf(s[0][gr][0], s[0][gr][1]), fmaxf(s[0][gr][2], s[0][gr][3]));
 #pragma unroll
         for (int b = 1; b < NB; ++b)
@@ -146,6 +146,10 @@ struct MfmaGroups {
             for (int nt = 0; nt < NT; ++nt) st.acc[gr][nt] *= corr;
             st.m[gr] = mn;
         }
+    }
+    template <int NB>
+    __device__ __forceinline__ static void weights(State& st, int gr, const f32x4 (&s)[NB][NG],
+                                                   float sl2, f16x4 (&p)[NB]) {
         float sum = 0.f;
         const float nm = -st.m[gr];
 #pragma unroll
@@ -157,6 +161,12 @@ struct MfmaGroups {
             p[b] = f16x4{(f16)pr[0], (f16)pr[1], (f16)pr[2], (f16)pr[3]};
         }
         st.l[gr] += sum;
+    }
+    template <int NB>
+    __device__ __forceinline__ static void weights_group(State& st, int gr, const f32x4 (&s)[NB][NG],
+                                                         float sl2, f16x4 (&p)[NB]) {
+        raise_max<NB>(st, gr, s, sl2);
+        weights<NB>(st, gr, s, sl2, p);
     }
 
     // One block alone (the last block of a unit with an odd block count).
@@ -598,6 +608,280 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
         nan_rows<D>(p.out, p.num_heads, head0, gc, q0, q_tiles * W * tpu, nq);
 }
 
+// --------------------------------------------------------------------------
+// fp16 pools: the ring form.  Four waves on consecutive query tiles of one
+// (sequence, KV head, head chunk) walk the block pairs of their union range
+// through an NS-slot LDS ring.  A slot holds one pair's K0 K1 V0 V1 tiles and
+// is filled by gfx950's global-to-LDS loads: wave w loads tile w (1 KiB per
+// instruction), so no register holds data in flight, and the loads of pair
+// k + NS - 1 go out while pair k is computed.  The compiler does not track
+// when such loads land, so the waits are explicit: loads complete in issue
+// order, so at the top of iteration k a wave waits until only the pairs
+// after k + 1 are outstanding, then a barrier makes every wave's share of
+// pair k + 1 visible and frees the slot of pair k - 1 for refilling.
+//
+// Within a wave, pairs that need no mask are software-pipelined: iteration k
+// raises the running max from pair k's scores (kept from iteration k - 1),
+// then issues the score MFMAs of pair k + 1 and computes pair k's weights
+// and PV MFMAs in the same stretch of code, so the matrix cores have the next
+// pair's scores to work on while the VALU runs this pair's exp2.  Pairs that
+// reach the causal diagonal or the sequence end take the masked steps of the
+// one-wave kernel on tiles read from LDS.  The arithmetic of every pair is the
+// one-wave kernel's, in the same order, so the results are bit-identical.
+//
+// K tiles keep their pool layout in LDS (lane l reads 16 bytes at 16 (l + 64c):
+// conflict-free).  The pair's two V tiles are interleaved per 16 head dims
+// on the way in: KiB nt holds head dims 16 nt .. 16 nt + 15 of block 0, then
+// of block 1, each half with the 16-byte piece of head dim d, tokens
+// 8h .. 8h + 7 at position (d % 16) + 16 h.  Lane (i, g)'s PV operand (head
+// dim 16 nt + i, tokens 4g .. 4g + 3 of both blocks) is then two 8-byte reads
+// 512 bytes apart, and one wave's read of one block covers 512 consecutive
+// bytes.  Each load instruction still reads two contiguous 512-byte runs of
+// the pool.
+// --------------------------------------------------------------------------
+#ifndef PA_PREFILL_RING
+#define PA_PREFILL_RING 1         // fp16 pools: 1 = ring form, 0 = one-wave kernel
+#endif
+#ifndef PA_PREFILL_RING_SLOTS
+#define PA_PREFILL_RING_SLOTS 3   // pairs in the ring (3 x 16 KiB at D = 128)
+#endif
+
+// lane (i, g)'s 8 bytes of block 0's V for head dims 16 nt + i, tokens
+// 4g .. 4g + 3; block 1's follow 512 bytes later
+template <int D>
+__device__ __forceinline__ int ring_v_offset(int nt) {
+    const int l = lane_id(), i = l & 15, g = l >> 4;
+    return 1024 * nt + 16 * (i + 16 * (g >> 1)) + 8 * (g & 1);
+}
+
+template <int D, int NG, int NS>
+// (two resident waves per SIMD asked of the register allocator: at most 256 VGPRs)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void pa_prefill_ring_kernel(
+    DecodeParams p, const int32_t* __restrict__ qsl, int total_q, int tpu, int q_tiles) {
+    using Path = MfmaPath<D>;
+    using G2 = MfmaGroups<Path, NG>;
+    using Tile = typename Path::Tile;
+    constexpr int W = 4;                           // waves; wave w loads tile w of each pair
+    constexpr int KC = D / 32, NT = D / 16;
+    constexpr int TB = D * kBlock * 2;             // bytes of one K (or V) tile
+    constexpr int STAGE = 4 * TB;                  // K0 K1 V0 V1
+    constexpr int CPW = TB / 1024;                 // load instructions per wave per pair
+    static_assert(NS >= 3, "the ring needs a slot being read, one landing and one refilled");
+    extern __shared__ __align__(16) char smem[];   // ring[NS][STAGE]; after the walk, per-wave staging
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int l = lane_id();
+    const int kvhc_count = p.num_kv_heads * p.head_chunks;
+    const int kvhc = blockIdx.x % kvhc_count;
+    const int sq = blockIdx.x / kvhc_count;
+    const int s = sq / q_tiles, qt = sq - s * q_tiles;
+    const int kvh = kvhc / p.head_chunks;
+    const int hc = kvhc - kvh * p.head_chunks;
+    const int gleft = p.group - hc * 16;
+    const int gc = gleft < 16 ? gleft : 16;        // heads of this chunk
+    const QueryRange qr_ = query_range(qsl, s, total_q);
+    const int q0 = qr_.q0, nq = qr_.nq;
+    const int jw = qt * W * tpu;                   // first query token of the workgroup
+    if (jw >= nq) return;                          // the whole workgroup
+    const int j0 = jw + wave * tpu;                // first query token of this wave
+    const int ntok = max(0, min(tpu, nq - j0));
+    const int L = p.seq_lens[s];
+    const int nb_seq = (L + kBlock - 1) / kBlock;
+    bool bad = qr_.bad || nq > L || nb_seq > p.max_blocks_per_seq;
+
+    const int head0 = kvh * p.group + hc * 16;
+    int pos[NG];
+    bool col_ok[NG];
+    typename G2::QRegs qr;
+    load_columns<G2>(qr, pos, col_ok, p.q, p.num_heads, head0, gc, q0, j0, ntok, L, nq, bad);
+    typename G2::State st;
+    G2::init(st);
+
+    const int ntok_wg = min(W * tpu, nq - jw);
+    const int n = bad ? 0 : (L - nq + jw + ntok_wg - 1) / kBlock + 1;        // blocks of the workgroup
+    const int np = (n + 1) / 2;                                              // pairs of the workgroup
+    const int n_w = ntok == 0 ? 0 : (L - nq + j0 + ntok - 1) / kBlock + 1;   // blocks of this wave
+    const int np_w = (n_w + 1) / 2;
+    const int pos_first = L - nq + j0;             // the wave's earliest column
+    // pairs of this wave that lie wholly before its earliest column: no mask
+    const int nf = ntok == 0 ? 0 : min(np_w, (pos_first + 1) / (2 * kBlock));
+    const float sl2 = p.scale_log2;
+
+    if (np > 0) {
+        const unsigned num_blocks = (unsigned)p.num_blocks;
+        // block ids come through scalar loads (the table is read-only here),
+        // so the vector load count holds only the ring's loads
+        typedef const int32_t __attribute__((address_space(4)))* ctable_t;
+        const ctable_t row = (ctable_t)(p.block_tables + (size_t)s * p.max_blocks_per_seq);
+        // The two block ids of pair j are loaded one pair ahead of their use
+        // and checked when used, so the scalar loads' latency is hidden; like
+        // the one-wave kernel, a wave's rows turn NaN when a block it attends
+        // over has an invalid id (the load then reads block 0).
+        struct Ids {
+            int b0, b1;
+        };
+        auto load_ids = [&](int j) { return Ids{row[min(2 * j, n - 1)], row[min(2 * j + 1, n - 1)]}; };
+        // waves 0 and 1 load K0 and K1 (pool layout); waves 2 and 3 load the
+        // pair's V tiles interleaved per 16 head dims: load instruction c
+        // of wave 2 + h covers head dims 16 nt .. 16 nt + 15, nt = CPW h + c,
+        // lanes 0..31 from block 0 and lanes 32..63 from block 1
+        const bool is_v = wave >= 2;
+        const char* tbase = (is_v ? p.v_cache : p.k_cache) + (size_t)kvh * TB;
+        const size_t blk_stride = (size_t)p.num_kv_heads * TB;
+        const bool hi_half = l >= 32;
+        int goff[CPW];                             // this lane's source byte in its tile, per KiB piece
+#pragma unroll
+        for (int c = 0; c < CPW; ++c) {
+            if (is_v) {
+                const int nt = CPW * (wave - 2) + c, q = l & 31;
+                goff[c] = 32 * (16 * nt + (q & 15)) + 16 * (q >> 4);
+            } else {
+                goff[c] = 16 * (64 * c + l);
+            }
+        }
+        auto slot = [&](int j) { return smem + (j % NS) * STAGE; };
+        auto issue = [&](int j, const Ids& ids) {
+            const bool ok0 = (unsigned)ids.b0 < num_blocks, ok1 = (unsigned)ids.b1 < num_blocks;
+            bad = bad || (2 * j < n_w && !ok0) || (2 * j + 1 < n_w && !ok1);
+            const int id0 = ok0 ? ids.b0 : 0, id1 = ok1 ? ids.b1 : 0;
+            const int id = is_v ? (hi_half ? id1 : id0) : ((wave & 1) ? id1 : id0);
+            const char* src = tbase + (size_t)id * blk_stride;
+            char* dst = slot(j) + wave * TB;
+#pragma unroll
+            for (int c = 0; c < CPW; ++c)
+                __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + goff[c]),
+                                                 (__attribute__((address_space(3))) void*)(dst + 1024 * c),
+                                                 16, 0, 0);
+        };
+        // prologue: pairs 0 .. NS - 2 requested, pair 0 waited for
+        Ids nid = load_ids(0);
+#pragma unroll
+        for (int j = 0; j < NS - 1; ++j) {
+            if (j < np) {
+                issue(j, nid);
+                nid = load_ids(j + 1);
+            }
+        }
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+        const int voff0 = 2 * TB;
+        auto k_operands = [&](f16x8 (&a)[KC], const char* sl, int b) {
+#pragma unroll
+            for (int c = 0; c < KC; ++c) a[c] = *reinterpret_cast<const f16x8*>(sl + b * TB + 16 * (l + 64 * c));
+        };
+        auto scores_pair = [&](f32x4 (&sc)[2][NG], const char* sl) {
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                f16x8 a[KC];
+                k_operands(a, sl, b);
+#pragma unroll
+                for (int gr = 0; gr < NG; ++gr) {
+                    sc[b][gr] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int c = 0; c < KC; ++c)
+                        sc[b][gr] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[c], qr.q[gr].q[c], sc[b][gr], 0, 0, 0);
+                }
+            }
+        };
+        auto lds_tile = [&](Tile& t, const char* sl, int b) {
+#pragma unroll
+            for (int c = 0; c < KC; ++c) t.k[c] = *reinterpret_cast<const f16x8*>(sl + b * TB + 16 * (l + 64 * c));
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                t.v[nt] = *reinterpret_cast<const f16x4*>(sl + voff0 + 512 * b + ring_v_offset<D>(nt));
+        };
+
+        // top of iteration k: pair k + 1 landed (every wave's share), the slot
+        // of pair k - 1 refilled with pair k + NS - 1
+        auto advance = [&](int k) {
+            if (k + 1 >= np) return;
+            if (k + NS - 2 < np)
+                asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(CPW * (NS - 3)) : "memory");
+            else
+                asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            if (k + NS - 1 < np) {
+                issue(k + NS - 1, nid);
+                nid = load_ids(k + NS);
+            }
+        };
+
+        // 1. unmasked pairs, pipelined: the scores of pair k + 1 are computed
+        // while pair k's weights and PV run
+        int k = 0;
+        if (nf > 0) {
+            f32x4 scur[2][NG];
+            scores_pair(scur, slot(0));
+            for (; k < nf; ++k) {
+                advance(k);
+                const char* sl = slot(k);
+#pragma unroll
+                for (int gr = 0; gr < NG; ++gr) G2::template raise_max<2>(st, gr, scur, sl2);
+                // the next pair's scores (unused after the last unmasked pair,
+                // whose successor slot may hold anything: always computed, so
+                // the MFMAs and this pair's VALU work share one stretch of code)
+                f32x4 snext[2][NG];
+                scores_pair(snext, slot(k + 1));
+                f16x8 av[NT];
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    const f16x4 v0 = *reinterpret_cast<const f16x4*>(sl + voff0 + ring_v_offset<D>(nt));
+                    const f16x4 v1 = *reinterpret_cast<const f16x4*>(sl + voff0 + 512 + ring_v_offset<D>(nt));
+                    av[nt] = f16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+                }
+#pragma unroll
+                for (int gr = 0; gr < NG; ++gr) {
+                    f16x4 pw[2];
+                    G2::template weights<2>(st, gr, scur, sl2, pw);
+                    const f16x8 w = {pw[0][0], pw[0][1], pw[0][2], pw[0][3], pw[1][0], pw[1][1], pw[1][2], pw[1][3]};
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt)
+                        st.acc[gr][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[nt], w, st.acc[gr][nt], 0, 0, 0);
+                }
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+#pragma unroll
+                    for (int gr = 0; gr < NG; ++gr) scur[b][gr] = snext[b][gr];
+            }
+        }
+        // 2. pairs that reach the diagonal or the sequence end (masked steps
+        // of the one-wave kernel), then the rest of the workgroup's walk
+        for (; k < np; ++k) {
+            advance(k);
+            if (k >= np_w) continue;
+            const char* sl = slot(k);
+            int lim[NG];
+            const int kb = 2 * k;
+#pragma unroll
+            for (int gr = 0; gr < NG; ++gr)
+                lim[gr] = col_ok[gr] ? min(kBlock - 1, pos[gr] - kb * kBlock) : kBlock - 1;
+            Tile ta;
+            lds_tile(ta, sl, 0);
+            const int va = min(kBlock, L - kb * kBlock);
+            const bool ca = kb * kBlock + kBlock - 1 > pos_first;
+            if (kb + 1 < n_w) {
+                typename G2::Half h;
+                G2::first(h, ta, qr, sl2, va, ca, lim);
+                Tile tb;
+                lds_tile(tb, sl, 1);
+#pragma unroll
+                for (int gr = 0; gr < NG; ++gr)
+                    lim[gr] = col_ok[gr] ? min(kBlock - 1, pos[gr] - (kb + 1) * kBlock) : kBlock - 1;
+                G2::second(st, h, tb, qr, sl2, min(kBlock, L - (kb + 1) * kBlock),
+                           (kb + 1) * kBlock + kBlock - 1 > pos_first, lim);
+            } else {
+                G2::single(st, ta, qr, sl2, va, ca, lim);
+            }
+        }
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+
+    // per wave: its rows through its own LDS area (the ring is free after the
+    // last barrier)
+    store_rows<G2>(st, reinterpret_cast<float*>(smem) + wave * (16 * D + 16), p.out, p.num_heads,
+                   head0, gc, q0, j0, ntok, p.v_scale, bad);
+    if (qt == q_tiles - 1 && wave == 0 && nq > q_tiles * W * tpu)
+        nan_rows<D>(p.out, p.num_heads, head0, gc, q0, q_tiles * W * tpu, nq);
+}
+
 }  // namespace pa
 
 using namespace pa;
@@ -624,20 +908,31 @@ extern "C" int pa_prefill(float* out, const void* q, const void* k_cache, const 
     constexpr int NG = kPrefillGroups;
     const bool fp8 = kv_cache_dtype == PA_KV_FP8_E4M3;
     // fp8 pools: four waves share 4-block K/V stages through LDS (1.2-1.3x
-    // over one wave); fp16 pools: one wave per unit with its tiles in
-    // registers (the shared form needs 256 VGPRs there and runs slower)
+    // over one wave); fp16 pools: four waves share block pairs through an
+    // LDS ring filled by global-to-LDS loads
     constexpr int W8 = 4;
-    const int W = fp8 ? W8 : 1;
+    constexpr int NS = PA_PREFILL_RING_SLOTS;
+    const bool ring16 = !fp8 && PA_PREFILL_RING;
+    const int W = fp8 || ring16 ? W8 : 1;
     const int tpu = G >= 16 ? NG : (16 * NG) / G;       // query tokens per wave
     const int q_tiles = (max_query_len + W * tpu - 1) / (W * tpu);
     const long long grid = (long long)num_seqs * q_tiles * num_kv_heads * p.head_chunks;
     if (grid > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
     const size_t ring = 2 * 2 * kStageBlocks * (size_t)head_size * kBlock * kv_elem_bytes(kv_cache_dtype);
     const size_t stage = W * (16 * (size_t)head_size + 16) * sizeof(float);
-    const size_t lds = W == 1 ? stage : (ring > stage ? ring : stage);
+    const size_t ring_f16 = NS * 4 * (size_t)head_size * kBlock * 2;
+    const size_t lds = ring16 ? (ring_f16 > stage ? ring_f16 : stage)
+                              : W == 1 ? stage : (ring > stage ? ring : stage);
     hipStream_t st = as_stream(stream);
     const dim3 g((unsigned)grid);
-    if (head_size == 128) {
+    if (ring16) {
+        if (head_size == 128)
+            hipLaunchKernelGGL((pa_prefill_ring_kernel<128, NG, NS>), g, dim3(64 * W8), lds, st, p,
+                               query_start_loc, total_q, tpu, q_tiles);
+        else
+            hipLaunchKernelGGL((pa_prefill_ring_kernel<64, NG, NS>), g, dim3(64 * W8), lds, st, p,
+                               query_start_loc, total_q, tpu, q_tiles);
+    } else if (head_size == 128) {
         if (fp8)
             hipLaunchKernelGGL((pa_prefill_wg_kernel<MfmaPath8<128>, NG, W8>), g, dim3(64 * W8), lds, st,
                                p, query_start_loc, total_q, tpu, q_tiles);

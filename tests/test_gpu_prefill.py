@@ -116,9 +116,9 @@ def test_max_query_len_too_small_gives_nan_rows():
     ref = oracle.paged_prefill(q, inp.k_cache, inp.v_cache, inp.block_tables, lens, qsl, inp.scale, 16)
     out = run(q, to_dev(inp.k_cache), to_dev(inp.v_cache), inp.block_tables, lens, qsl,
               inp.scale, 20)
-    # G = 4: 8 query tokens per tile, so max_query_len 20 covers 24 rows
-    assert np.isnan(out[24:60]).all()
-    assert_parity(out[:24], ref[:24], "covered rows")
+    # G = 4: a tile is 4 waves x 8 query tokens, so max_query_len 20 covers 32 rows
+    assert np.isnan(out[32:60]).all()
+    assert_parity(out[:32], ref[:32], "covered rows")
     assert_parity(out[60:], ref[60:], "other sequence")
 
 
