@@ -29,6 +29,9 @@
 // same blocks.
 #include "pa_paths.h"
 
+#ifndef PA_PREFILL_TILE_MAJOR
+#define PA_PREFILL_TILE_MAJOR 0   // grid order: 0 = sequence-major, 1 = query-tile-major
+#endif
 #ifndef PA_PREFILL_GROUPS
 #define PA_PREFILL_GROUPS 2   // 16-column groups per wave (query rows per K/V tile read / 16)
 #endif
@@ -133,10 +136,13 @@ struct MfmaGroups {
     template <int NB>
     __device__ __forceinline__ static void raise_max(State& st, int gr, const f32x4 (&s)[NB][NG],
                                                      float sl2) {
-        float v = fmaxf(fmaxf(s[0][gr][0], s[0][gr][1]), fmaxf(s[0][gr][2], s[0][gr][3]));
+        // IEEE maximum (v_maximum3_f32, no quieting of its inputs first): the
+        // scores are finite or -inf (masked), so it is plain max here
+        auto mx = [](float a, float b) { return __builtin_elementwise_maximum(a, b); };
+        float v = mx(mx(s[0][gr][0], s[0][gr][1]), mx(s[0][gr][2], s[0][gr][3]));
 #pragma unroll
         for (int b = 1; b < NB; ++b)
-            v = fmaxf(v, fmaxf(fmaxf(s[b][gr][0], s[b][gr][1]), fmaxf(s[b][gr][2], s[b][gr][3])));
+            v = mx(v, mx(mx(s[b][gr][0], s[b][gr][1]), mx(s[b][gr][2], s[b][gr][3])));
         const float bm = v * sl2;
         if (__builtin_amdgcn_ballot_w64(bm > st.m[gr] + kLazy) != 0) {
             const float mn = fmaxf(st.m[gr], col4_max(bm));
@@ -466,7 +472,13 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     const int kvhc_count = p.num_kv_heads * p.head_chunks;
     const int kvhc = blockIdx.x % kvhc_count;
     const int sq = blockIdx.x / kvhc_count;
-    const int s = sq / q_tiles, qt = sq - s * q_tiles;
+#if PA_PREFILL_TILE_MAJOR
+    const int rt = sq / p.num_seqs, s = sq - rt * p.num_seqs, qt = q_tiles - 1 - rt;
+#else
+    // a sequence's query tiles together (they read the same K/V), its last
+    // tiles (the longest walks under the causal mask) first
+    const int s = sq / q_tiles, qt = q_tiles - 1 - (sq - s * q_tiles);
+#endif
     const int kvh = kvhc / p.head_chunks;
     const int hc = kvhc - kvh * p.head_chunks;
     const int gleft = p.group - hc * 16;
@@ -673,7 +685,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     const int kvhc_count = p.num_kv_heads * p.head_chunks;
     const int kvhc = blockIdx.x % kvhc_count;
     const int sq = blockIdx.x / kvhc_count;
-    const int s = sq / q_tiles, qt = sq - s * q_tiles;
+#if PA_PREFILL_TILE_MAJOR
+    const int rt = sq / p.num_seqs, s = sq - rt * p.num_seqs, qt = q_tiles - 1 - rt;
+#else
+    // a sequence's query tiles together (they read the same K/V), its last
+    // tiles (the longest walks under the causal mask) first
+    const int s = sq / q_tiles, qt = q_tiles - 1 - (sq - s * q_tiles);
+#endif
     const int kvh = kvhc / p.head_chunks;
     const int hc = kvhc - kvh * p.head_chunks;
     const int gleft = p.group - hc * 16;
@@ -768,19 +786,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 #pragma unroll
             for (int c = 0; c < KC; ++c) a[c] = *reinterpret_cast<const f16x8*>(sl + b * TB + 16 * (l + 64 * c));
         };
-        auto scores_pair = [&](f32x4 (&sc)[2][NG], const char* sl) {
+        auto scores_from = [&](f32x4 (&sc)[2][NG], const f16x8 (&a)[2][KC]) {
 #pragma unroll
             for (int b = 0; b < 2; ++b) {
-                f16x8 a[KC];
-                k_operands(a, sl, b);
 #pragma unroll
                 for (int gr = 0; gr < NG; ++gr) {
                     sc[b][gr] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int c = 0; c < KC; ++c)
-                        sc[b][gr] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[c], qr.q[gr].q[c], sc[b][gr], 0, 0, 0);
+                        sc[b][gr] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[b][c], qr.q[gr].q[c], sc[b][gr], 0, 0, 0);
                 }
             }
+        };
+        auto scores_pair = [&](f32x4 (&sc)[2][NG], const char* sl) {
+            f16x8 a[2][KC];
+            k_operands(a[0], sl, 0);
+            k_operands(a[1], sl, 1);
+            scores_from(sc, a);
         };
         auto lds_tile = [&](Tile& t, const char* sl, int b) {
 #pragma unroll
@@ -805,41 +827,51 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         };
 
         // 1. unmasked pairs, pipelined: the scores of pair k + 1 are computed
-        // while pair k's weights and PV run
+        // while pair k's weights and PV run.  Pair k's scores come in sc, pair
+        // k + 1's go to sn; the loop is unrolled by two so the two score sets
+        // swap roles instead of being copied.  The next pair's scores are
+        // always computed (after the last unmasked pair its slot may hold
+        // anything and they are dropped), so the score MFMAs and this pair's
+        // VALU work share one stretch of code.
+        auto fast_pair = [&](int kk, f32x4 (&sc)[2][NG], f32x4 (&sn)[2][NG]) {
+            advance(kk);
+            const char* sl = slot(kk);
+            // the next pair's K operands are requested before the max check,
+            // whose branch would otherwise keep them behind it
+            f16x8 ka[2][KC];
+            k_operands(ka[0], slot(kk + 1), 0);
+            k_operands(ka[1], slot(kk + 1), 1);
+#pragma unroll
+            for (int gr = 0; gr < NG; ++gr) G2::template raise_max<2>(st, gr, sc, sl2);
+            scores_from(sn, ka);
+            f16x8 av[NT];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const f16x4 v0 = *reinterpret_cast<const f16x4*>(sl + voff0 + ring_v_offset<D>(nt));
+                const f16x4 v1 = *reinterpret_cast<const f16x4*>(sl + voff0 + 512 + ring_v_offset<D>(nt));
+                av[nt] = f16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+            }
+#pragma unroll
+            for (int gr = 0; gr < NG; ++gr) {
+                f16x4 pw[2];
+                G2::template weights<2>(st, gr, sc, sl2, pw);
+                const f16x8 w = {pw[0][0], pw[0][1], pw[0][2], pw[0][3], pw[1][0], pw[1][1], pw[1][2], pw[1][3]};
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+                    st.acc[gr][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[nt], w, st.acc[gr][nt], 0, 0, 0);
+            }
+        };
         int k = 0;
         if (nf > 0) {
-            f32x4 scur[2][NG];
-            scores_pair(scur, slot(0));
-            for (; k < nf; ++k) {
-                advance(k);
-                const char* sl = slot(k);
-#pragma unroll
-                for (int gr = 0; gr < NG; ++gr) G2::template raise_max<2>(st, gr, scur, sl2);
-                // the next pair's scores (unused after the last unmasked pair,
-                // whose successor slot may hold anything: always computed, so
-                // the MFMAs and this pair's VALU work share one stretch of code)
-                f32x4 snext[2][NG];
-                scores_pair(snext, slot(k + 1));
-                f16x8 av[NT];
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    const f16x4 v0 = *reinterpret_cast<const f16x4*>(sl + voff0 + ring_v_offset<D>(nt));
-                    const f16x4 v1 = *reinterpret_cast<const f16x4*>(sl + voff0 + 512 + ring_v_offset<D>(nt));
-                    av[nt] = f16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-                }
-#pragma unroll
-                for (int gr = 0; gr < NG; ++gr) {
-                    f16x4 pw[2];
-                    G2::template weights<2>(st, gr, scur, sl2, pw);
-                    const f16x8 w = {pw[0][0], pw[0][1], pw[0][2], pw[0][3], pw[1][0], pw[1][1], pw[1][2], pw[1][3]};
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt)
-                        st.acc[gr][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[nt], w, st.acc[gr][nt], 0, 0, 0);
-                }
-#pragma unroll
-                for (int b = 0; b < 2; ++b)
-#pragma unroll
-                    for (int gr = 0; gr < NG; ++gr) scur[b][gr] = snext[b][gr];
+            f32x4 sa[2][NG], sb[2][NG];
+            scores_pair(sa, slot(0));
+            for (; k + 1 < nf; k += 2) {
+                fast_pair(k, sa, sb);
+                fast_pair(k + 1, sb, sa);
+            }
+            if (k < nf) {
+                fast_pair(k, sa, sb);
+                ++k;
             }
         }
         // 2. pairs that reach the diagonal or the sequence end (masked steps
