@@ -10,23 +10,20 @@
 // token's, are already in the pools (written by reshape_and_cache).  n_s = 1
 // is a decode step; n_s = L_s is a plain prefill.
 //
-// Two forms.  fp16 pools: one wavefront per (sequence, query tile, KV head,
-// head chunk), its tiles loaded straight into registers.  fp8 pools: a
-// workgroup of four such wavefronts on consecutive query tiles sharing K/V
-// through LDS (pa_prefill_wg_kernel below).
+// One workgroup of four wavefronts per (sequence, four consecutive query
+// tiles, KV head, head chunk); the waves share the K/V block pairs through an
+// LDS ring (pa_prefill_ring_kernel below), fp16 and fp8 pools alike.
 //
 // Work unit of a wavefront:
 // The columns of the MFMA score tiles S^T = K Q^T are (token, head) pairs of
 // one KV group -- 16 NG / G consecutive query tokens times the G heads, or
 // NG tokens of 16 heads when G >= 16 -- in NG groups of 16, so every K/V
 // tile read serves 16 NG query rows and the MFMA runs full (MHA included:
-// 16 NG tokens of one head).  The unit walks blocks 0 .. p_last/16 in order with the decode
-// kernels' table windows and paired tiles; each column's causal limit is a
-// lane-local mask (the softmax state of a column lives in its own lanes),
-// and block 0 -- visible to every column -- comes first, so no column's
-// running max is still -inf when a later, fully masked block arrives.  Tiles
-// are read with cached loads: the query tiles of one sequence re-read the
-// same blocks.
+// 16 NG tokens of one head).  The unit walks block pairs 0 .. p_last/32 in
+// order; each column's causal limit is a lane-local mask (the softmax state
+// of a column lives in its own lanes), and block 0 -- visible to every
+// column -- comes first, so no column's running max is still -inf when a
+// later, fully masked block arrives.
 #include "pa_paths.h"
 
 #ifndef PA_PREFILL_TILE_MAJOR
@@ -39,7 +36,6 @@
 namespace pa {
 
 constexpr int kPrefillGroups = PA_PREFILL_GROUPS;
-constexpr int kStageBlocks = 4;   // blocks per LDS stage of the workgroup form
 
 // --------------------------------------------------------------------------
 // NG groups of 16 columns per wave: every K/V tile read (and, for fp8 pools,
@@ -321,363 +317,112 @@ __device__ __forceinline__ QueryRange query_range(const int32_t* qsl, int s, int
     return r;
 }
 
-template <class Path, int NG>
-__global__ __launch_bounds__(64) void pa_prefill_kernel(DecodeParams p,
-                                                        const int32_t* __restrict__ qsl,
-                                                        int total_q, int tpu, int q_tiles) {
-    using G2 = MfmaGroups<Path, NG>;
-    constexpr int D = G2::D;
-    extern __shared__ float lds[];
-    const int kvhc_count = p.num_kv_heads * p.head_chunks;
-    const int kvhc = blockIdx.x % kvhc_count;
-    const int sq = blockIdx.x / kvhc_count;
-    const int s = sq / q_tiles, qt = sq - s * q_tiles;
-    const int kvh = kvhc / p.head_chunks;
-    const int hc = kvhc - kvh * p.head_chunks;
-    const int gleft = p.group - hc * 16;
-    const int gc = gleft < 16 ? gleft : 16;            // heads of this chunk
-    const QueryRange qr_ = query_range(qsl, s, total_q);
-    const int q0 = qr_.q0, nq = qr_.nq;
-    const int j0 = qt * tpu;
-    if (j0 >= nq) return;
-    const int ntok = min(tpu, nq - j0);
-    const int L = p.seq_lens[s];
-    const int nb_seq = (L + kBlock - 1) / kBlock;
-    bool bad = qr_.bad || nq > L || nb_seq > p.max_blocks_per_seq;
-
-    const int head0 = kvh * p.group + hc * 16;
-    const int pos_last = L - nq + j0 + ntok - 1;
-    int pos[NG];
-    bool col_ok[NG];
-    typename G2::QRegs qr;
-    load_columns<G2>(qr, pos, col_ok, p.q, p.num_heads, head0, gc, q0, j0, ntok, L, nq, bad);
-    typename G2::State st;
-    G2::init(st);
-
-    const int n = bad ? 0 : pos_last / kBlock + 1;      // blocks 0 .. pos_last / 16
-    constexpr int TB = D * kBlock * G2::kElem;
-    const char* kbase = p.k_cache + (size_t)kvh * TB;
-    const char* vbase = p.v_cache + (size_t)kvh * TB;
-    const size_t blk_stride = (size_t)p.num_kv_heads * TB;
-    const int32_t* row = p.block_tables + (size_t)s * p.max_blocks_per_seq;
-    const float sl2 = p.scale_log2;
-
-    if (n > 0) {
-        // the same walk as the decode kernels (table windows of 64 entries,
-        // paired tiles, a zero-size request past the last block)
-        int cur = table_window<1>(row, 0, n, 0, p.max_blocks_per_seq);
-        int nxt = table_window<1>(row, 0, n, 64, p.max_blocks_per_seq);
-        auto phys = [&](int kw, int j) {
-            const int d = min(j, n - 1) - kw;
-            const int v = d < 64 ? __builtin_amdgcn_readlane(cur, d) : __builtin_amdgcn_readlane(nxt, d - 64);
-            const bool ok = (unsigned)v < (unsigned)p.num_blocks;
-            bad = bad || !ok;
-            return ok ? v : 0;
-        };
-        auto tile_k = [&](int id) { return kbase + (size_t)id * blk_stride; };
-        auto tile_v = [&](int id) { return vbase + (size_t)id * blk_stride; };
-        auto valid = [&](int k) { return min(kBlock, L - k * kBlock); };
-        // the earliest column's position: blocks reaching past it need the causal mask
-        const int pos_first = L - nq + j0;
-        auto lims = [&](int k, int (&lim)[NG]) {
-#pragma unroll
-            for (int gr = 0; gr < NG; ++gr)
-                lim[gr] = col_ok[gr] ? min(kBlock - 1, pos[gr] - k * kBlock) : kBlock - 1;
-        };
-        auto causal = [&](int k) { return k * kBlock + kBlock - 1 > pos_first; };
-        auto live = [&](int j) { return j < n ? TB : 0; };
-        typename G2::Tile ta, tb;
-        typename G2::Half h;
-        int lim[NG];
-        int id = phys(0, 0);
-        G2::template load<false>(ta, tile_k(id), tile_v(id), TB);
-        int k = 0;
-        for (int kw = 0;; kw += 64) {
-            const int pend = table_window<1>(row, 0, n, kw + 128, p.max_blocks_per_seq);
-            const int kend = min(n, kw + 64) & ~1;
-            for (; k < kend; k += 2) {
-                id = phys(kw, k + 1);
-                G2::template load<false>(tb, tile_k(id), tile_v(id), TB);
-                lims(k, lim);
-                G2::first(h, ta, qr, sl2, valid(k), causal(k), lim);
-                id = phys(kw, k + 2);
-                G2::template load<false>(ta, tile_k(id), tile_v(id), live(k + 2));
-                lims(k + 1, lim);
-                G2::second(st, h, tb, qr, sl2, valid(k + 1), causal(k + 1), lim);
-            }
-            if (kw + 64 >= n) break;
-            cur = nxt;
-            nxt = pend;
-        }
-        if (k < n) {
-            lims(k, lim);
-            G2::single(st, ta, qr, sl2, valid(k), causal(k), lim);
-        }
-    }
-
-    store_rows<G2>(st, lds, p.out, p.num_heads, head0, gc, q0, j0, ntok, p.v_scale, bad);
-    // more queries than max_query_len allowed for: the sequence's last tile
-    // sets the rows no tile covers to NaN
-    if (qt == q_tiles - 1 && nq > q_tiles * tpu)
-        nan_rows<D>(p.out, p.num_heads, head0, gc, q0, q_tiles * tpu, nq);
-}
-
-
-
 // --------------------------------------------------------------------------
-// Workgroup form: W waves on consecutive query tiles of one (sequence, KV
-// head, head chunk) share K/V through a two-slot LDS ring of 4-block stages.
-// While the waves compute stage j from LDS, every thread holds its share of
-// stage j + 1 (16-byte loads issued a whole stage ahead) and writes it to the
-// other slot; one barrier per stage.  K tiles keep their pool layout in LDS
-// (lane l reads 16 bytes at 16 (l + 64c): conflict-free); V tiles are stored
-// with the piece of lane (i, g) -- head dim 16nt + i, tokens 4g .. 4g + 3 --
-// at index 16g + i + 64nt, so a wave's V operand read is consecutive too.
-// --------------------------------------------------------------------------
-// A tile from an LDS stage: K in pool layout, V with lane (i, g)'s piece at
-// index 16g + i + 64nt.
-template <class Path>
-__device__ __forceinline__ void lds_tile(typename Path::Tile& t, const char* kt, const char* vt) {
-    constexpr int D = Path::kD;
-    const int l = lane_id();
-    if constexpr (Path::kElem == 2) {
-#pragma unroll
-        for (int c = 0; c < D / 32; ++c) t.k[c] = *reinterpret_cast<const f16x8*>(kt + 16 * (l + 64 * c));
-#pragma unroll
-        for (int nt = 0; nt < D / 16; ++nt) t.v[nt] = *reinterpret_cast<const f16x4*>(vt + 8 * (l + 64 * nt));
-    } else {
-#pragma unroll
-        for (int r = 0; r < D / 64; ++r) t.k[r] = *reinterpret_cast<const u32x4*>(kt + 16 * (l + 64 * r));
-#pragma unroll
-        for (int nt = 0; nt < D / 16; ++nt) t.v[nt] = *reinterpret_cast<const uint32_t*>(vt + 4 * (l + 64 * nt));
-    }
-}
-
-template <class Path, int NG, int W>
-// (two resident waves per SIMD asked of the register allocator: at most 256 VGPRs)
-__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) void pa_prefill_wg_kernel(DecodeParams p,
-                                                               const int32_t* __restrict__ qsl,
-                                                               int total_q, int tpu, int q_tiles) {
-    using G2 = MfmaGroups<Path, NG>;
-    constexpr int D = G2::D;
-    constexpr int NT = D / 16;
-    constexpr int EB = G2::kElem;                  // bytes per element
-    constexpr int TB = D * kBlock * EB;            // bytes of one K (or V) tile
-    constexpr int SB = kStageBlocks;
-    constexpr int STAGE = 2 * SB * TB;             // K and V of SB blocks
-    constexpr int CPT = STAGE / (16 * 64 * W);     // 16-byte pieces per thread per stage
-    static_assert(CPT >= 1 && STAGE % (16 * 64 * W) == 0, "stage copy does not tile the workgroup");
-    extern __shared__ __align__(16) char smem[];   // ring[2][STAGE]; after the walk, per-wave staging
-    const int wave = threadIdx.x >> 6;
-    const int kvhc_count = p.num_kv_heads * p.head_chunks;
-    const int kvhc = blockIdx.x % kvhc_count;
-    const int sq = blockIdx.x / kvhc_count;
-#if PA_PREFILL_TILE_MAJOR
-    const int rt = sq / p.num_seqs, s = sq - rt * p.num_seqs, qt = q_tiles - 1 - rt;
-#else
-    // a sequence's query tiles together (they read the same K/V), its last
-    // tiles (the longest walks under the causal mask) first
-    const int s = sq / q_tiles, qt = q_tiles - 1 - (sq - s * q_tiles);
-#endif
-    const int kvh = kvhc / p.head_chunks;
-    const int hc = kvhc - kvh * p.head_chunks;
-    const int gleft = p.group - hc * 16;
-    const int gc = gleft < 16 ? gleft : 16;        // heads of this chunk
-    const QueryRange qr_ = query_range(qsl, s, total_q);
-    const int q0 = qr_.q0, nq = qr_.nq;
-    const int jw = qt * W * tpu;                   // first query token of the workgroup
-    if (jw >= nq) return;                          // the whole workgroup
-    const int j0 = jw + wave * tpu;                // first query token of this wave
-    const int ntok = max(0, min(tpu, nq - j0));
-    const int L = p.seq_lens[s];
-    const int nb_seq = (L + kBlock - 1) / kBlock;
-    bool bad = qr_.bad || nq > L || nb_seq > p.max_blocks_per_seq;
-
-    const int head0 = kvh * p.group + hc * 16;
-    int pos[NG];
-    bool col_ok[NG];
-    typename G2::QRegs qr;
-    load_columns<G2>(qr, pos, col_ok, p.q, p.num_heads, head0, gc, q0, j0, ntok, L, nq, bad);
-    typename G2::State st;
-    G2::init(st);
-
-    const int ntok_wg = min(W * tpu, nq - jw);
-    const int n = bad ? 0 : (L - nq + jw + ntok_wg - 1) / kBlock + 1;        // blocks of the workgroup
-    const int n_w = ntok == 0 ? 0 : (L - nq + j0 + ntok - 1) / kBlock + 1;   // blocks of this wave
-    const char* kbase = p.k_cache + (size_t)kvh * TB;
-    const char* vbase = p.v_cache + (size_t)kvh * TB;
-    const size_t blk_stride = (size_t)p.num_kv_heads * TB;
-    const int32_t* row = p.block_tables + (size_t)s * p.max_blocks_per_seq;
-    const float sl2 = p.scale_log2;
-    const int pos_first = L - nq + j0;
-
-    if (n > 0) {
-        int kw = 0;                                // cur: blocks [kw, kw + 64), nxt the next 64
-        int cur = table_window<1>(row, 0, n, 0, p.max_blocks_per_seq);
-        int nxt = table_window<1>(row, 0, n, 64, p.max_blocks_per_seq);
-        int pend = table_window<1>(row, 0, n, 128, p.max_blocks_per_seq);
-        const unsigned num_blocks = (unsigned)p.num_blocks;
-        const int nst = (n + SB - 1) / SB;
-        u32x4 stg[CPT];
-        typename G2::Half h;
-        typename G2::Tile ta, tb;
-        int lim[NG];
-        // stage j of the K/V walk from global memory into stg (16-byte pieces:
-        // piece e is tile e / (TB / 16) -- block q / 2, K if q is even -- at
-        // byte (e % (TB / 16)) * 16); blocks past the walk read nothing
-#define PA_FETCH(J)                                                                                \
-        _Pragma("unroll") for (int u = 0; u < CPT; ++u) {                                          \
-            const int e = (int)threadIdx.x + 64 * W * u;                                           \
-            const int q = e / (TB / 16);                                                           \
-            const int o = (e - q * (TB / 16)) * 16;                                                \
-            const int k = SB * (J) + (q >> 1);                                                     \
-            const int d = min(k, n - 1) - kw;                                                      \
-            const int v = d < 64 ? __builtin_amdgcn_readlane(cur, d)                               \
-                                 : __builtin_amdgcn_readlane(nxt, d - 64);                         \
-            const bool ok = (unsigned)v < num_blocks;                                              \
-            bad = bad || !ok;                                                                      \
-            const char* src = ((q & 1) ? vbase : kbase) + (size_t)(ok ? v : 0) * blk_stride + o;  \
-            stg[u] = k < n ? *reinterpret_cast<const u32x4*>(src) : u32x4{0u, 0u, 0u, 0u};        \
-        }
-        // stg into LDS slot SLOT (V pieces rearranged for the operand reads)
-#define PA_COMMIT(SLOT)                                                                            \
-        _Pragma("unroll") for (int u = 0; u < CPT; ++u) {                                          \
-            const int e = (int)threadIdx.x + 64 * W * u;                                           \
-            const int q = e / (TB / 16);                                                           \
-            const int o = (e - q * (TB / 16)) * 16;                                                \
-            char* tile = smem + (SLOT) * STAGE + q * TB;                                           \
-            if (!(q & 1)) {                                                                        \
-                *reinterpret_cast<u32x4*>(tile + o) = stg[u];                                      \
-            } else if constexpr (EB == 2) {                                                        \
-                /* head dim d, tokens 8h .. 8h + 7: pieces g = 2h, 2h + 1 */                       \
-                const int dd = o >> 5, hh = (o >> 4) & 1;                                          \
-                const int base = (dd & 15) + 64 * (dd >> 4);                                       \
-                *reinterpret_cast<u32x2*>(tile + 8 * (32 * hh + base)) = u32x2{stg[u][0], stg[u][1]};      \
-                *reinterpret_cast<u32x2*>(tile + 8 * (32 * hh + 16 + base)) = u32x2{stg[u][2], stg[u][3]}; \
-            } else {                                                                               \
-                /* head dim d, all 16 tokens: pieces g = 0 .. 3 */                                 \
-                const int dd = o >> 4;                                                             \
-                const int base = (dd & 15) + 64 * (dd >> 4);                                       \
-                *reinterpret_cast<uint32_t*>(tile + 4 * (base)) = stg[u][0];                       \
-                *reinterpret_cast<uint32_t*>(tile + 4 * (16 + base)) = stg[u][1];                  \
-                *reinterpret_cast<uint32_t*>(tile + 4 * (32 + base)) = stg[u][2];                  \
-                *reinterpret_cast<uint32_t*>(tile + 4 * (48 + base)) = stg[u][3];                  \
-            }                                                                                      \
-        }
-        PA_FETCH(0)
-        PA_COMMIT(0)
-        __syncthreads();
-        for (int j = 0; j < nst; ++j) {
-            if (SB * (j + 1) + SB - 1 >= kw + 128) {   // the next stage leaves the table window
-                kw += 64;
-                cur = nxt;
-                nxt = pend;
-                pend = table_window<1>(row, 0, n, kw + 128, p.max_blocks_per_seq);
-            }
-            if (j + 1 < nst) {
-                PA_FETCH(j + 1)
-            }
-            const char* ring = smem + (j & 1) * STAGE;
-#pragma unroll 1
-            for (int pr = 0; pr < SB / 2; ++pr) {
-                const int k = SB * j + 2 * pr;
-                if (k < n_w) {
-                    lds_tile<Path>(ta, ring + (4 * pr) * TB, ring + (4 * pr + 1) * TB);
-#pragma unroll
-                    for (int gr = 0; gr < NG; ++gr)
-                        lim[gr] = col_ok[gr] ? min(kBlock - 1, pos[gr] - k * kBlock) : kBlock - 1;
-                    const int va = min(kBlock, L - k * kBlock);
-                    const bool ca = k * kBlock + kBlock - 1 > pos_first;
-                    if (k + 1 < n_w) {
-                        G2::first(h, ta, qr, sl2, va, ca, lim);
-                        lds_tile<Path>(tb, ring + (4 * pr + 2) * TB, ring + (4 * pr + 3) * TB);
-#pragma unroll
-                        for (int gr = 0; gr < NG; ++gr)
-                            lim[gr] = col_ok[gr] ? min(kBlock - 1, pos[gr] - (k + 1) * kBlock) : kBlock - 1;
-                        G2::second(st, h, tb, qr, sl2, min(kBlock, L - (k + 1) * kBlock),
-                                   (k + 1) * kBlock + kBlock - 1 > pos_first, lim);
-                    } else {
-                        G2::single(st, ta, qr, sl2, va, ca, lim);
-                    }
-                }
-            }
-            if (j + 1 < nst) {
-                PA_COMMIT((j + 1) & 1)
-            }
-            __syncthreads();
-        }
-#undef PA_FETCH
-#undef PA_COMMIT
-    }
-
-    // per wave: its rows through its own LDS area (the ring is free after the
-    // last barrier)
-    store_rows<G2>(st, reinterpret_cast<float*>(smem) + wave * (16 * D + 16), p.out, p.num_heads,
-                   head0, gc, q0, j0, ntok, p.v_scale, bad);
-    // more queries than max_query_len allowed for: the sequence's last
-    // workgroup sets the rows no tile covers to NaN
-    if (qt == q_tiles - 1 && wave == 0 && nq > q_tiles * W * tpu)
-        nan_rows<D>(p.out, p.num_heads, head0, gc, q0, q_tiles * W * tpu, nq);
-}
-
-// --------------------------------------------------------------------------
-// fp16 pools: the ring form.  Four waves on consecutive query tiles of one
+// The ring form.  Four waves on consecutive query tiles of one
 // (sequence, KV head, head chunk) walk the block pairs of their union range
-// through an NS-slot LDS ring.  A slot holds one pair's K0 K1 V0 V1 tiles and
-// is filled by gfx950's global-to-LDS loads: wave w loads tile w (1 KiB per
-// instruction), so no register holds data in flight, and the loads of pair
-// k + NS - 1 go out while pair k is computed.  The compiler does not track
-// when such loads land, so the waits are explicit: loads complete in issue
-// order, so at the top of iteration k a wave waits until only the pairs
-// after k + 1 are outstanding, then a barrier makes every wave's share of
-// pair k + 1 visible and frees the slot of pair k - 1 for refilling.
+// through an NS-slot LDS ring.  A slot holds one pair's K0, K1 and V tiles
+// and is filled by gfx950's global-to-LDS loads (wave w loads the slot's
+// w-th tile's worth, 1 KiB per instruction), so no register holds data in
+// flight, and the loads of pair k + NS - 1 go out while pair k is computed.
+// The compiler does not track when such loads land, so the waits are
+// explicit: loads complete in issue order, so at the top of iteration k a
+// wave waits until only the pairs after k + 1 are outstanding, then a
+// barrier makes every wave's share of pair k + 1 visible and frees the slot
+// of pair k - 1 for refilling.
 //
 // Within a wave, pairs that need no mask are software-pipelined: iteration k
 // raises the running max from pair k's scores (kept from iteration k - 1),
 // then issues the score MFMAs of pair k + 1 and computes pair k's weights
 // and PV MFMAs in the same stretch of code, so the matrix cores have the next
 // pair's scores to work on while the VALU runs this pair's exp2.  Pairs that
-// reach the causal diagonal or the sequence end take the masked steps of the
-// one-wave kernel on tiles read from LDS.  The arithmetic of every pair is the
-// one-wave kernel's, in the same order, so the results are bit-identical.
-//
-// K tiles keep their pool layout in LDS (lane l reads 16 bytes at 16 (l + 64c):
-// conflict-free).  The pair's two V tiles are interleaved per 16 head dims
-// on the way in: KiB nt holds head dims 16 nt .. 16 nt + 15 of block 0, then
-// of block 1, each half with the 16-byte piece of head dim d, tokens
-// 8h .. 8h + 7 at position (d % 16) + 16 h.  Lane (i, g)'s PV operand (head
-// dim 16 nt + i, tokens 4g .. 4g + 3 of both blocks) is then two 8-byte reads
-// 512 bytes apart, and one wave's read of one block covers 512 consecutive
-// bytes.  Each load instruction still reads two contiguous 512-byte runs of
-// the pool.
+// reach the causal diagonal or the sequence end take MfmaGroups' masked
+// first / second / single steps on tiles read from LDS.  Either way a pair's
+// arithmetic is the same, in the same order.
 // --------------------------------------------------------------------------
-#ifndef PA_PREFILL_RING
-#define PA_PREFILL_RING 1         // fp16 pools: 1 = ring form, 0 = one-wave kernel
-#endif
 #ifndef PA_PREFILL_RING_SLOTS
 #define PA_PREFILL_RING_SLOTS 3   // pairs in the ring (3 x 16 KiB at D = 128)
 #endif
 
-// lane (i, g)'s 8 bytes of block 0's V for head dims 16 nt + i, tokens
-// 4g .. 4g + 3; block 1's follow 512 bytes later
-template <int D>
-__device__ __forceinline__ int ring_v_offset(int nt) {
-    const int l = lane_id(), i = l & 15, g = l >> 4;
-    return 1024 * nt + 16 * (i + 16 * (g >> 1)) + 8 * (g & 1);
-}
+// Where a pair's tiles sit in a ring slot ([K0 | K1 | V of both blocks],
+// TB bytes per tile) and how the MFMA operands are read back.  K tiles keep
+// their pool layout (16 bytes at 16 (l + 64 r) per lane, conflict-free).
+// The two V tiles are interleaved:
+//  - fp16: KiB nt holds head dims 16 nt .. 16 nt + 15 of block 0, then of
+//    block 1, each half with the 16-byte piece of head dim d, tokens
+//    8h .. 8h + 7 at position (d % 16) + 16 h; lane (i, g)'s operand (head
+//    dim 16 nt + i, tokens 4g .. 4g + 3 of both blocks) is two 8-byte reads
+//    512 bytes apart, each wave-wide read covering 512 consecutive bytes;
+//  - fp8: the 16-byte rows (head dim d, 16 tokens) of the two blocks
+//    alternate, block b's row d at 32 d + 16 b; lane (i, g)'s operand is two
+//    4-byte reads 16 bytes apart, the wave's reads covering 512 consecutive
+//    bytes.
+// Each 1 KiB load instruction still reads whole 16-byte pieces of the pool.
+template <class Path>
+struct RingLayout {
+    static constexpr int D = Path::kD;
+    static constexpr int TB = D * kBlock * Path::kElem;   // bytes of one K (or V) tile
+    static constexpr int CPW = TB / 1024;                 // load instructions per tile
+    using Tile = typename Path::Tile;
 
-template <int D, int NG, int NS>
+    // V-loading lane l of load instruction c (0 .. 2 CPW - 1 over the
+    // pair's V): the block (0 or 1) and the byte of that block's V tile
+    __device__ __forceinline__ static int v_block(int l) {
+        return Path::kElem == 2 ? l >> 5 : l & 1;
+    }
+    __device__ __forceinline__ static int v_src(int c, int l) {
+        if constexpr (Path::kElem == 2) {
+            const int q = l & 31;
+            return 32 * (16 * c + (q & 15)) + 16 * (q >> 4);
+        } else {
+            return 16 * (32 * c + (l >> 1));
+        }
+    }
+    // block b's K tile (raw) and V pieces into a tile as Path::load gives them
+    __device__ __forceinline__ static void read_k(Tile& t, const char* sl, int b) {
+        const int l = lane_id();
+#pragma unroll
+        for (int r = 0; r < CPW; ++r)
+            t.k[r] = *reinterpret_cast<const std::remove_reference_t<decltype(t.k[0])>*>(sl + b * TB + 16 * (l + 64 * r));
+    }
+    __device__ __forceinline__ static int v_at(int nt, int b) {
+        const int l = lane_id(), i = l & 15, g = l >> 4;
+        if constexpr (Path::kElem == 2)
+            return 2 * TB + 1024 * nt + 512 * b + 16 * (i + 16 * (g >> 1)) + 8 * (g & 1);
+        else
+            return 2 * TB + 32 * (16 * nt + i) + 16 * b + 4 * g;
+    }
+    __device__ __forceinline__ static void read_v(Tile& t, const char* sl, int b) {
+#pragma unroll
+        for (int nt = 0; nt < D / 16; ++nt)
+            t.v[nt] = *reinterpret_cast<const std::remove_reference_t<decltype(t.v[0])>*>(sl + v_at(nt, b));
+    }
+    // the PV operand of the pair for head dims 16 nt .. 16 nt + 15
+    __device__ __forceinline__ static f16x8 v_pair(const char* sl, int nt) {
+        f16x4 v0, v1;
+        if constexpr (Path::kElem == 2) {
+            v0 = *reinterpret_cast<const f16x4*>(sl + v_at(nt, 0));
+            v1 = *reinterpret_cast<const f16x4*>(sl + v_at(nt, 1));
+        } else {
+            v0 = e4m3x4_to_f16x4(*reinterpret_cast<const uint32_t*>(sl + v_at(nt, 0)));
+            v1 = e4m3x4_to_f16x4(*reinterpret_cast<const uint32_t*>(sl + v_at(nt, 1)));
+        }
+        return f16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+    }
+};
+
+template <class Path, int NG, int NS>
 // (two resident waves per SIMD asked of the register allocator: at most 256 VGPRs)
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void pa_prefill_ring_kernel(
     DecodeParams p, const int32_t* __restrict__ qsl, int total_q, int tpu, int q_tiles) {
-    using Path = MfmaPath<D>;
     using G2 = MfmaGroups<Path, NG>;
     using Tile = typename Path::Tile;
+    using RL = RingLayout<Path>;
+    constexpr int D = Path::kD;
     constexpr int W = 4;                           // waves; wave w loads tile w of each pair
     constexpr int KC = D / 32, NT = D / 16;
-    constexpr int TB = D * kBlock * 2;             // bytes of one K (or V) tile
+    constexpr int TB = RL::TB;                     // bytes of one K (or V) tile
     constexpr int STAGE = 4 * TB;                  // K0 K1 V0 V1
-    constexpr int CPW = TB / 1024;                 // load instructions per wave per pair
+    constexpr int CPW = RL::CPW;                   // load instructions per wave per pair
     static_assert(NS >= 3, "the ring needs a slot being read, one landing and one refilled");
     extern __shared__ __align__(16) char smem[];   // ring[NS][STAGE]; after the walk, per-wave staging
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -731,37 +476,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         typedef const int32_t __attribute__((address_space(4)))* ctable_t;
         const ctable_t row = (ctable_t)(p.block_tables + (size_t)s * p.max_blocks_per_seq);
         // The two block ids of pair j are loaded one pair ahead of their use
-        // and checked when used, so the scalar loads' latency is hidden; like
-        // the one-wave kernel, a wave's rows turn NaN when a block it attends
-        // over has an invalid id (the load then reads block 0).
+        // and checked when used, so the scalar loads' latency is hidden.  A
+        // wave's rows turn NaN when a block it attends over has an invalid id
+        // (the load then reads block 0); other waves' rows are unaffected.
         struct Ids {
             int b0, b1;
         };
         auto load_ids = [&](int j) { return Ids{row[min(2 * j, n - 1)], row[min(2 * j + 1, n - 1)]}; };
         // waves 0 and 1 load K0 and K1 (pool layout); waves 2 and 3 load the
-        // pair's V tiles interleaved per 16 head dims: load instruction c
-        // of wave 2 + h covers head dims 16 nt .. 16 nt + 15, nt = CPW h + c,
-        // lanes 0..31 from block 0 and lanes 32..63 from block 1
+        // pair's two V tiles, interleaved (RingLayout)
         const bool is_v = wave >= 2;
         const char* tbase = (is_v ? p.v_cache : p.k_cache) + (size_t)kvh * TB;
         const size_t blk_stride = (size_t)p.num_kv_heads * TB;
-        const bool hi_half = l >= 32;
+        const bool v_second = RL::v_block(l) == 1;
         int goff[CPW];                             // this lane's source byte in its tile, per KiB piece
 #pragma unroll
-        for (int c = 0; c < CPW; ++c) {
-            if (is_v) {
-                const int nt = CPW * (wave - 2) + c, q = l & 31;
-                goff[c] = 32 * (16 * nt + (q & 15)) + 16 * (q >> 4);
-            } else {
-                goff[c] = 16 * (64 * c + l);
-            }
-        }
+        for (int c = 0; c < CPW; ++c)
+            goff[c] = is_v ? RL::v_src(CPW * (wave - 2) + c, l) : 16 * (64 * c + l);
         auto slot = [&](int j) { return smem + (j % NS) * STAGE; };
         auto issue = [&](int j, const Ids& ids) {
             const bool ok0 = (unsigned)ids.b0 < num_blocks, ok1 = (unsigned)ids.b1 < num_blocks;
             bad = bad || (2 * j < n_w && !ok0) || (2 * j + 1 < n_w && !ok1);
             const int id0 = ok0 ? ids.b0 : 0, id1 = ok1 ? ids.b1 : 0;
-            const int id = is_v ? (hi_half ? id1 : id0) : ((wave & 1) ? id1 : id0);
+            const int id = is_v ? (v_second ? id1 : id0) : ((wave & 1) ? id1 : id0);
             const char* src = tbase + (size_t)id * blk_stride;
             char* dst = slot(j) + wave * TB;
 #pragma unroll
@@ -781,10 +518,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         }
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-        const int voff0 = 2 * TB;
+        // block b's K operands (fp8 tiles converted to fp16)
         auto k_operands = [&](f16x8 (&a)[KC], const char* sl, int b) {
+            Tile t;
+            RL::read_k(t, sl, b);
 #pragma unroll
-            for (int c = 0; c < KC; ++c) a[c] = *reinterpret_cast<const f16x8*>(sl + b * TB + 16 * (l + 64 * c));
+            for (int c = 0; c < KC; ++c) a[c] = Path::a_k(t, c);
         };
         auto scores_from = [&](f32x4 (&sc)[2][NG], const f16x8 (&a)[2][KC]) {
 #pragma unroll
@@ -805,11 +544,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
             scores_from(sc, a);
         };
         auto lds_tile = [&](Tile& t, const char* sl, int b) {
-#pragma unroll
-            for (int c = 0; c < KC; ++c) t.k[c] = *reinterpret_cast<const f16x8*>(sl + b * TB + 16 * (l + 64 * c));
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-                t.v[nt] = *reinterpret_cast<const f16x4*>(sl + voff0 + 512 * b + ring_v_offset<D>(nt));
+            RL::read_k(t, sl, b);
+            RL::read_v(t, sl, b);
         };
 
         // top of iteration k: pair k + 1 landed (every wave's share), the slot
@@ -838,19 +574,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
             const char* sl = slot(kk);
             // the next pair's K operands are requested before the max check,
             // whose branch would otherwise keep them behind it
-            f16x8 ka[2][KC];
-            k_operands(ka[0], slot(kk + 1), 0);
-            k_operands(ka[1], slot(kk + 1), 1);
+            Tile kt[2];
+            RL::read_k(kt[0], slot(kk + 1), 0);
+            RL::read_k(kt[1], slot(kk + 1), 1);
 #pragma unroll
             for (int gr = 0; gr < NG; ++gr) G2::template raise_max<2>(st, gr, sc, sl2);
+            f16x8 ka[2][KC];
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int c = 0; c < KC; ++c) ka[b][c] = Path::a_k(kt[b], c);
             scores_from(sn, ka);
             f16x8 av[NT];
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                const f16x4 v0 = *reinterpret_cast<const f16x4*>(sl + voff0 + ring_v_offset<D>(nt));
-                const f16x4 v1 = *reinterpret_cast<const f16x4*>(sl + voff0 + 512 + ring_v_offset<D>(nt));
-                av[nt] = f16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-            }
+            for (int nt = 0; nt < NT; ++nt) av[nt] = RL::v_pair(sl, nt);
 #pragma unroll
             for (int gr = 0; gr < NG; ++gr) {
                 f16x4 pw[2];
@@ -874,8 +611,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
                 ++k;
             }
         }
-        // 2. pairs that reach the diagonal or the sequence end (masked steps
-        // of the one-wave kernel), then the rest of the workgroup's walk
+        // 2. pairs that reach the diagonal or the sequence end (MfmaGroups'
+        // masked steps), then the rest of the workgroup's walk
         for (; k < np; ++k) {
             advance(k);
             if (k >= np_w) continue;
@@ -939,45 +676,27 @@ extern "C" int pa_prefill(float* out, const void* q, const void* k_cache, const 
     p.head_chunks = G > 16 ? (G + 15) / 16 : 1;
     constexpr int NG = kPrefillGroups;
     const bool fp8 = kv_cache_dtype == PA_KV_FP8_E4M3;
-    // fp8 pools: four waves share 4-block K/V stages through LDS (1.2-1.3x
-    // over one wave); fp16 pools: four waves share block pairs through an
-    // LDS ring filled by global-to-LDS loads
-    constexpr int W8 = 4;
+    // four waves per workgroup, each on 16 NG / G query tokens (NG for G >= 16)
+    constexpr int W = 4;
     constexpr int NS = PA_PREFILL_RING_SLOTS;
-    const bool ring16 = !fp8 && PA_PREFILL_RING;
-    const int W = fp8 || ring16 ? W8 : 1;
     const int tpu = G >= 16 ? NG : (16 * NG) / G;       // query tokens per wave
     const int q_tiles = (max_query_len + W * tpu - 1) / (W * tpu);
     const long long grid = (long long)num_seqs * q_tiles * num_kv_heads * p.head_chunks;
     if (grid > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
-    const size_t ring = 2 * 2 * kStageBlocks * (size_t)head_size * kBlock * kv_elem_bytes(kv_cache_dtype);
-    const size_t stage = W * (16 * (size_t)head_size + 16) * sizeof(float);
-    const size_t ring_f16 = NS * 4 * (size_t)head_size * kBlock * 2;
-    const size_t lds = ring16 ? (ring_f16 > stage ? ring_f16 : stage)
-                              : W == 1 ? stage : (ring > stage ? ring : stage);
+    const size_t ring = NS * 4 * (size_t)head_size * kBlock * kv_elem_bytes(kv_cache_dtype);
+    const size_t stage = W * (16 * (size_t)head_size + 16) * sizeof(float);   // output staging
+    const size_t lds = ring > stage ? ring : stage;
     hipStream_t st = as_stream(stream);
     const dim3 g((unsigned)grid);
-    if (ring16) {
-        if (head_size == 128)
-            hipLaunchKernelGGL((pa_prefill_ring_kernel<128, NG, NS>), g, dim3(64 * W8), lds, st, p,
-                               query_start_loc, total_q, tpu, q_tiles);
-        else
-            hipLaunchKernelGGL((pa_prefill_ring_kernel<64, NG, NS>), g, dim3(64 * W8), lds, st, p,
-                               query_start_loc, total_q, tpu, q_tiles);
-    } else if (head_size == 128) {
-        if (fp8)
-            hipLaunchKernelGGL((pa_prefill_wg_kernel<MfmaPath8<128>, NG, W8>), g, dim3(64 * W8), lds, st,
-                               p, query_start_loc, total_q, tpu, q_tiles);
-        else
-            hipLaunchKernelGGL((pa_prefill_kernel<MfmaPath<128>, NG>), g, dim3(64), lds, st,
-                               p, query_start_loc, total_q, tpu, q_tiles);
+#define PA_PREFILL_LAUNCH(KERNEL) \
+    hipLaunchKernelGGL((KERNEL), g, dim3(64 * W), lds, st, p, query_start_loc, total_q, tpu, q_tiles)
+    if (head_size == 128) {
+        if (fp8) PA_PREFILL_LAUNCH((pa_prefill_ring_kernel<MfmaPath8<128>, NG, NS>));
+        else PA_PREFILL_LAUNCH((pa_prefill_ring_kernel<MfmaPath<128>, NG, NS>));
     } else {
-        if (fp8)
-            hipLaunchKernelGGL((pa_prefill_wg_kernel<MfmaPath8<64>, NG, W8>), g, dim3(64 * W8), lds, st,
-                               p, query_start_loc, total_q, tpu, q_tiles);
-        else
-            hipLaunchKernelGGL((pa_prefill_kernel<MfmaPath<64>, NG>), g, dim3(64), lds, st,
-                               p, query_start_loc, total_q, tpu, q_tiles);
+        if (fp8) PA_PREFILL_LAUNCH((pa_prefill_ring_kernel<MfmaPath8<64>, NG, NS>));
+        else PA_PREFILL_LAUNCH((pa_prefill_ring_kernel<MfmaPath<64>, NG, NS>));
     }
+#undef PA_PREFILL_LAUNCH
     return launch_status();
 }
