@@ -223,8 +223,10 @@ PA_API int pa_decode_v2_noalloc(float* out, const void* q, const void* k_cache,
  *                   sequence beyond the first max_query_len, rounded up to
  *                   the tile of 4 x 32/G query tokens (4 x 2 for G >= 16),
  *                   are set to NaN
- *   other arguments as in pa_decode_v1.  n > L, a block id outside the pool
- *   or L beyond the table row gives NaN rows for that sequence.
+ *   other arguments as in pa_decode_v1.  n > L or L beyond the table row
+ *   gives NaN rows for that sequence; a block id outside the pool gives NaN
+ *   rows for the queries that attend over that block (with the other
+ *   queries of their wave's tile of 32/G tokens, 2 for G >= 16).
  */
 PA_API int pa_prefill(float* out, const void* q, const void* k_cache, const void* v_cache,
                const int32_t* block_tables, const int32_t* seq_lens,

@@ -142,6 +142,30 @@ def test_fp8_invalid_shapes_give_nan_rows():
 
 
 @pytest.mark.parametrize("fp8_pools", [False, True], ids=["fp16", "fp8"])
+def test_invalid_block_id_gives_nan_rows_from_its_first_token(fp8_pools):
+    """A block id outside the pool at logical block 5 of a full prefill: every
+    query at or past its first token (80) comes back NaN, the queries before
+    it (whole query tiles of 8 tokens at G = 4) are unaffected, and so is the
+    other sequence."""
+    inp, lens, qsl, q = make("badid", 8, 2, 128, [200, 120], [200, 120], seed=48)
+    ks, vs = (0.03, 0.02) if fp8_pools else (1.0, 1.0)
+    if fp8_pools:
+        kc = logical_to_k8(fp8.quantize(k16_to_logical(inp.k_cache), ks))
+        vc = fp8.quantize(inp.v_cache, vs)
+        dk, dv = fp8.dequantize_pools(kc, vc, ks, vs)
+    else:
+        kc, vc, dk, dv = inp.k_cache, inp.v_cache, inp.k_cache, inp.v_cache
+    ref = oracle.paged_prefill(q, dk, dv, inp.block_tables, lens, qsl, inp.scale, 16)
+    bt = inp.block_tables.copy()
+    bt[0, 5] = inp.num_blocks + 3
+    out = run(q, to_dev(kc), to_dev(vc), bt, lens, qsl, inp.scale, 200, ks, vs)
+    assert np.isnan(out[80:200]).all()
+    assert np.isfinite(out[:80]).all() and np.isfinite(out[200:]).all()
+    assert_parity(out[:80], ref[:80], "rows before the bad block")
+    assert_parity(out[200:], ref[200:], "other sequence")
+
+
+@pytest.mark.parametrize("fp8_pools", [False, True], ids=["fp16", "fp8"])
 def test_malformed_query_start_loc_stays_in_bounds(fp8_pools):
     """query_start_loc ranges that run backwards or leave [0, total_q): the
     sequence's rows inside [0, total_q) come back NaN, nothing past the last
