@@ -57,8 +57,8 @@ def test_prefill_matches_oracle(case):
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_prefill_fp8_matches_oracle(case):
-    """fp8 pools take the workgroup form (four waves sharing K/V stages through
-    LDS): every query-tile shape, the table-window crossing, extra tiles."""
+    """fp8 pools: every query-tile shape, the table-window crossing, extra
+    workgroups."""
     inp, lens, qsl, q = make(*case, seed=42)
     ks, vs = 0.03, 0.02
     k8 = logical_to_k8(fp8.quantize(k16_to_logical(inp.k_cache), ks))
@@ -68,6 +68,36 @@ def test_prefill_fp8_matches_oracle(case):
     out = run(q, to_dev(k8), to_dev(v8), inp.block_tables, lens, qsl, inp.scale,
               int(max(case[5])) + 40, ks, vs)                  # extra workgroups exit at once
     assert_parity(out, ref, case[0] + " fp8")
+
+
+# Seeded random shapes: KV group sizes 2, 8 and 32 (head chunks), both head
+# sizes and pool types, lengths and query counts drawn per sequence (full
+# prefills, chunks, single queries), block counts that are odd and even, so
+# that pairs end half empty and workgroups end mid-pair.
+SWEEP = [(g, d, fp8_pools, seed) for seed, (g, d, fp8_pools) in enumerate(
+    [(2, 128, False), (8, 64, False), (32, 128, False), (2, 64, True), (8, 128, True), (32, 64, True)])]
+
+
+@pytest.mark.parametrize("g,d,fp8_pools,seed", SWEEP,
+                         ids=[f"g{g}_d{d}_{'fp8' if f else 'fp16'}" for g, d, f, _ in SWEEP])
+def test_prefill_random_shapes(g, d, fp8_pools, seed):
+    rng = np.random.default_rng(100 + seed)
+    kvh = 2 if g <= 8 else 1
+    S = 5
+    lens = [int(x) for x in rng.integers(1, 400, size=S)]
+    nq = [int(min(L, max(1, rng.integers(1, L + 1)) if i % 2 else L)) for i, L in enumerate(lens)]
+    inp, lens, qsl, q = make(f"sweep{seed}", g * kvh, kvh, d, lens, nq, seed=60 + seed)
+    if fp8_pools:
+        ks, vs = 0.05, 0.04
+        kc = logical_to_k8(fp8.quantize(k16_to_logical(inp.k_cache), ks))
+        vc = fp8.quantize(inp.v_cache, vs)
+        dk, dv = fp8.dequantize_pools(kc, vc, ks, vs)
+    else:
+        ks, vs = 1.0, 1.0
+        kc, vc, dk, dv = inp.k_cache, inp.v_cache, inp.k_cache, inp.v_cache
+    ref = oracle.paged_prefill(q, dk, dv, inp.block_tables, lens, qsl, inp.scale, 16)
+    out = run(q, to_dev(kc), to_dev(vc), inp.block_tables, lens, qsl, inp.scale, max(nq), ks, vs)
+    assert_parity(out, ref, f"g{g} d{d} {'fp8' if fp8_pools else 'fp16'} lens {lens} queries {nq}")
 
 
 def test_single_queries_agree_with_decode():
