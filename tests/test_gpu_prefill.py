@@ -38,8 +38,10 @@ def make(label, H, KVH, D, lens, nq, seed):
     return inp, lens, qsl, q
 
 
-def run(q, kc, vc, bt, lens, qsl, scale, max_q, ks=1.0, vs=1.0):
-    out = torch.empty(q.shape, dtype=torch.float32, device=device())
+def run(q, kc, vc, bt, lens, qsl, scale, max_q, ks=1.0, vs=1.0, fill=float("nan")):
+    # NaN-filled by default, so a row the kernel leaves unwritten cannot pass;
+    # tests that expect NaN rows fill with 0, so the NaN must come from the kernel
+    out = torch.full(q.shape, fill, dtype=torch.float32, device=device())
     pa.pa_prefill(out, to_dev(q), kc, vc, to_dev(bt), to_dev(lens), to_dev(qsl), max_q, scale,
                   ks, vs)
     return out.cpu().numpy()
@@ -100,6 +102,26 @@ def test_prefill_random_shapes(g, d, fp8_pools, seed):
     assert_parity(out, ref, f"g{g} d{d} {'fp8' if fp8_pools else 'fp16'} lens {lens} queries {nq}")
 
 
+@pytest.mark.parametrize("fp8_pools", [False, True], ids=["fp16", "fp8"])
+def test_sequences_without_queries_and_one_token(fp8_pools):
+    """Sequences with no query rows between others, a one-token sequence with
+    its one query, and a prefill whose length is a multiple of 32 (its last
+    pair exactly full): the rows present are right, none is left unwritten."""
+    inp, lens, qsl, q = make("gaps", 8, 2, 128, [64, 50, 1, 96, 33], [64, 0, 1, 0, 20], seed=49)
+    if fp8_pools:
+        ks, vs = 0.05, 0.04
+        kc = logical_to_k8(fp8.quantize(k16_to_logical(inp.k_cache), ks))
+        vc = fp8.quantize(inp.v_cache, vs)
+        dk, dv = fp8.dequantize_pools(kc, vc, ks, vs)
+    else:
+        ks, vs = 1.0, 1.0
+        kc, vc, dk, dv = inp.k_cache, inp.v_cache, inp.k_cache, inp.v_cache
+    ref = oracle.paged_prefill(q, dk, dv, inp.block_tables, lens, qsl, inp.scale, 16)
+    out = run(q, to_dev(kc), to_dev(vc), inp.block_tables, lens, qsl, inp.scale, 64, ks, vs)
+    assert np.isfinite(out).all()
+    assert_parity(out, ref, "gaps")
+
+
 def test_single_queries_agree_with_decode():
     inp, lens, qsl, q = make("one", 16, 4, 128, [300, 45, 1000], [1, 1, 1], seed=43)
     kc, vc = to_dev(inp.k_cache), to_dev(inp.v_cache)
@@ -115,7 +137,7 @@ def test_more_queries_than_tokens_gives_nan_rows():
     inp, lens, qsl, q = make("bad", 8, 2, 64, [10, 30], [4, 12], seed=44)
     lens = np.array([3, 30], np.int32)              # sequence 0: 4 queries, 3 tokens
     out = run(q, to_dev(inp.k_cache), to_dev(inp.v_cache), inp.block_tables, lens, qsl,
-              inp.scale, 12)
+              inp.scale, 12, fill=0.0)
     assert np.isnan(out[:4]).all()
     ref = oracle.paged_prefill(q[4:], inp.k_cache, inp.v_cache, inp.block_tables[1:], lens[1:],
                                qsl[1:] - qsl[1], inp.scale, 16)
@@ -145,7 +167,7 @@ def test_max_query_len_too_small_gives_nan_rows():
     inp, lens, qsl, q = make("short", 8, 2, 128, [90, 40], [60, 5], seed=46)
     ref = oracle.paged_prefill(q, inp.k_cache, inp.v_cache, inp.block_tables, lens, qsl, inp.scale, 16)
     out = run(q, to_dev(inp.k_cache), to_dev(inp.v_cache), inp.block_tables, lens, qsl,
-              inp.scale, 20)
+              inp.scale, 20, fill=0.0)
     # G = 4: a tile is 4 waves x 8 query tokens, so max_query_len 20 covers 32 rows
     assert np.isnan(out[32:60]).all()
     assert_parity(out[:32], ref[:32], "covered rows")
@@ -161,7 +183,7 @@ def test_fp8_invalid_shapes_give_nan_rows():
     k8 = logical_to_k8(fp8.quantize(k16_to_logical(inp.k_cache), ks))
     v8 = fp8.quantize(inp.v_cache, vs)
     dk, dv = fp8.dequantize_pools(k8, v8, ks, vs)
-    out = run(q, to_dev(k8), to_dev(v8), inp.block_tables, lens, qsl, inp.scale, 40, ks, vs)
+    out = run(q, to_dev(k8), to_dev(v8), inp.block_tables, lens, qsl, inp.scale, 40, ks, vs, fill=0.0)
     assert np.isnan(out[:4]).all()
     ref = oracle.paged_prefill(q[4:], dk, dv, inp.block_tables[1:], lens[1:], qsl[1:] - qsl[1],
                                inp.scale, 16)
@@ -188,7 +210,7 @@ def test_invalid_block_id_gives_nan_rows_from_its_first_token(fp8_pools):
     ref = oracle.paged_prefill(q, dk, dv, inp.block_tables, lens, qsl, inp.scale, 16)
     bt = inp.block_tables.copy()
     bt[0, 5] = inp.num_blocks + 3
-    out = run(q, to_dev(kc), to_dev(vc), bt, lens, qsl, inp.scale, 200, ks, vs)
+    out = run(q, to_dev(kc), to_dev(vc), bt, lens, qsl, inp.scale, 200, ks, vs, fill=0.0)
     assert np.isnan(out[80:200]).all()
     assert np.isfinite(out[:80]).all() and np.isfinite(out[200:]).all()
     assert_parity(out[:80], ref[:80], "rows before the bad block")
