@@ -56,8 +56,11 @@ def make_case(case, seed):
 
 def run_v1(inp):
     d = dev_inputs(inp)
-    return pa.paged_attention_v1(d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
-                                 d["seq_lens"], inp.scale).cpu().numpy()
+    # NaN-filled, so a row the kernel leaves unwritten cannot pass
+    out = torch.full(inp.q.shape, float("nan"), dtype=torch.float32, device=device())
+    pa.pa_decode_v1(out, d["q"], d["k_cache"], d["v_cache"], d["block_tables"], d["seq_lens"],
+                    inp.scale)
+    return out.cpu().numpy()
 
 
 def run_v2(inp, ps, max_seq_len=None):
@@ -70,7 +73,7 @@ def run_v2(inp, ps, max_seq_len=None):
         t.fill_(float("nan"))
     pa.pa_decode_v2(tmp, es, ml, d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
                     d["seq_lens"], inp.scale, ps)
-    out = torch.empty((S, H, D), dtype=torch.float32, device=device())
+    out = torch.full((S, H, D), float("nan"), dtype=torch.float32, device=device())
     pa.pa_reduce(out, tmp, es, ml, d["seq_lens"], ps)
     # partials come back [S,P,H,...]; return them [S,H,P,...] like the oracle
     return (out.cpu().numpy(), tmp.cpu().numpy().transpose(0, 2, 1, 3),
