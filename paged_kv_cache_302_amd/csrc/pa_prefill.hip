@@ -222,9 +222,10 @@ struct MfmaGroups {
         }
     }
 
-    // Rows of group gr to LDS: s_acc[i * D + d] unnormalised, s_l[i] the
-    // column's weight sum.
-    __device__ static void stage_group(const State& st, int gr, float* s_acc, float* s_l) {
+    // Rows of group gr to LDS: s_acc[i * D + d] unnormalised, s_inv[i] the
+    // column's factor v_scale / (weight sum), one division per column.
+    __device__ static void stage_group(const State& st, int gr, float* s_acc, float* s_inv,
+                                       float v_scale) {
         const int l = lane_id(), i = l & 15, g = l >> 4;
 #pragma unroll
         for (int x = 0; x < NG; ++x) {
@@ -233,7 +234,7 @@ struct MfmaGroups {
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
                 *reinterpret_cast<f32x4*>(s_acc + i * D + 16 * nt + 4 * g) = st.acc[x][nt];
-            if (g == 0) s_l[i] = ltot;
+            if (g == 0) s_inv[i] = v_scale / ltot;
         }
     }
 
@@ -261,29 +262,43 @@ __device__ __forceinline__ void load_columns(typename G2::QRegs& qr, int (&pos)[
     }
 }
 
-// The wave's result rows, group by group through its LDS area s_o (16 D + 16
-// floats), then whole 16-byte stores (the heads of one token are one
-// contiguous run of gc D floats); NaN rows for a bad sequence.
+// Floats of a wave's output staging area: 16 rows of D, the 16 columns'
+// factors, and the output row index of each of the wave's 16 NG columns.
+template <class G2>
+constexpr int stage_floats() {
+    return 16 * G2::D + 16 + 16 * G2::kNG;
+}
+
+// The wave's result rows, group by group through its LDS area s_o
+// (stage_floats), then whole 16-byte stores (the heads of one token are one
+// contiguous run of gc D floats); NaN rows for a bad sequence.  Each
+// column's output row (one integer division) and factor (one float
+// division) are computed once, not per stored element.
 template <class G2>
 __device__ __forceinline__ void store_rows(const typename G2::State& st, float* s_o, float* out,
                                            int num_heads, int head0, int gc, int q0, int j0,
                                            int ntok, float v_scale, bool bad) {
     constexpr int D = G2::D;
-    float* s_l = s_o + 16 * D;
+    constexpr int NCOL = 16 * G2::kNG;
+    float* s_inv = s_o + 16 * D;
+    int* s_row = reinterpret_cast<int*>(s_o + 16 * D + 16);
     const int cols = ntok * gc;
+    const int lane = lane_id();
+    if (lane < NCOL) {   // a row index fits 32 bits: out would not fit in memory otherwise
+        const int cj = lane / gc;
+        s_row[lane] = (q0 + j0 + cj) * num_heads + head0 + (lane - cj * gc);
+    }
     const f32x4* src = reinterpret_cast<const f32x4*>(s_o);
 #pragma unroll
     for (int gr = 0; gr < G2::kNG; ++gr) {
         if (16 * gr >= cols) break;
-        G2::stage_group(st, gr, s_o, s_l);
+        G2::stage_group(st, gr, s_o, s_inv, v_scale);
         const int cg = min(16, cols - 16 * gr);
-        for (int e = lane_id(); e < cg * (D / 4); e += 64) {
-            const int ci = (4 * e) / D;
-            const int c = 16 * gr + ci;
-            const int cj = c / gc;
-            f32x4 v = src[e] * (v_scale / s_l[ci]);
+        for (int e = lane; e < cg * (D / 4); e += 64) {
+            const int ci = e / (D / 4);
+            f32x4 v = src[e] * s_inv[ci];
             if (bad) v = f32x4{NAN, NAN, NAN, NAN};
-            float* orow = out + ((size_t)(q0 + j0 + cj) * num_heads + head0 + (c - cj * gc)) * D;
+            float* orow = out + (size_t)s_row[16 * gr + ci] * D;
             st_stream(reinterpret_cast<f32x4*>(orow) + (e - ci * (D / 4)), v);
         }
     }
@@ -645,7 +660,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 
     // per wave: its rows through its own LDS area (the ring is free after the
     // last barrier)
-    store_rows<G2>(st, reinterpret_cast<float*>(smem) + wave * (16 * D + 16), p.out, p.num_heads,
+    store_rows<G2>(st, reinterpret_cast<float*>(smem) + wave * stage_floats<G2>(), p.out, p.num_heads,
                    head0, gc, q0, j0, ntok, p.v_scale, bad);
     if (qt == q_tiles - 1 && wave == 0 && nq > q_tiles * W * tpu)
         nan_rows<D>(p.out, p.num_heads, head0, gc, q0, q_tiles * W * tpu, nq);
@@ -684,7 +699,7 @@ extern "C" int pa_prefill(float* out, const void* q, const void* k_cache, const 
     const long long grid = (long long)num_seqs * q_tiles * num_kv_heads * p.head_chunks;
     if (grid > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
     const size_t ring = NS * 4 * (size_t)head_size * kBlock * kv_elem_bytes(kv_cache_dtype);
-    const size_t stage = W * (16 * (size_t)head_size + 16) * sizeof(float);   // output staging
+    const size_t stage = W * (16 * (size_t)head_size + 16 + 16 * NG) * sizeof(float);   // output staging
     const size_t lds = ring > stage ? ring : stage;
     hipStream_t st = as_stream(stream);
     const dim3 g((unsigned)grid);
