@@ -66,6 +66,12 @@
 #ifndef PA_V1_WAVES
 #define PA_V1_WAVES 0         // waves per v1 workgroup (0 = heuristic)
 #endif
+#ifndef PA_SET_WAVES
+#define PA_SET_WAVES 2        // waves per set-kernel workgroup: 1, 2 or 4 teams of PA_SET_SPLIT (0 = no set kernel)
+#endif
+#ifndef PA_SET_SPLIT
+#define PA_SET_SPLIT 2        // set kernel: waves per class (the split of a class's blocks)
+#endif
 
 namespace pa {
 
@@ -643,6 +649,212 @@ void pa_decode_kernel(DecodeParams p) {
 }
 
 // --------------------------------------------------------------------------
+// Set kernel (v2, MFMA path, G = 2, 4 or 8, more than 64 sequences, PS <= 1024).
+// One workgroup per (aligned set of M = 16/G sequences, partition, KV head):
+// a score tile has 16 query rows and one KV group fills G of them, so the
+// set's M groups fill the tile.  The set's members fall into classes: the
+// leader together with every member whose token range in the partition and
+// table entries over it equal the leader's (samples and forks of one prompt
+// read the same blocks), and every other member alone.  Each class is
+// computed once, by a team of SF waves: wave s of the team takes the class's
+// blocks s, s + SF, ..., every member of the class in its own G tile rows, and
+// the last wave of the team to finish merges the SF states (in wave order)
+// through LDS and writes the class's rows.  The NW / SF teams of a workgroup
+// take the classes in turn; a team with no class returns at once.  Every
+// member's rows are thus the same SF-way split walk over the same K/V values
+// whether or not the member shares its blocks: the results are bit for bit
+// equal to those of private copies.  A class's blocks come straight from the
+// table entries loaded for the class check (lane j: entry j of the
+// partition), so the walk needs no table window.
+//
+// Against one unit per sequence, a shared partition is walked by SF waves at
+// once instead of by one, the members it serves cost no workgroup, and
+// (sequence, partition) follows from the workgroup index with no search over
+// the lengths; a workgroup whose partition exists for no member (a partition
+// past every member's length) returns after the length loads.
+// --------------------------------------------------------------------------
+template <class Path, int D, int NW, int SF>
+__global__ __launch_bounds__(64 * NW) void pa_decode_set_kernel(DecodeParams p) {
+    static_assert(NW % SF == 0, "teams of SF waves");
+    constexpr int kTeams = NW / SF;
+    extern __shared__ float lds[];
+    float* s_acc = lds;                                  // [SF][16][D]
+    float* s_m = lds + SF * 16 * D;                      // [SF][16]
+    float* s_l = s_m + SF * 16;                          // [SF][16]
+    int* s_bad = reinterpret_cast<int*>(s_l + SF * 16);  // [SF][kMaxMembers]
+    int* s_done = s_bad + SF * kMaxMembers;              // [kMaxMembers]: waves done, per class
+    if (threadIdx.x < kMaxMembers) s_done[threadIdx.x] = 0;
+    __syncthreads();   // before any wave can return
+
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int team = w / SF, sub = w - team * SF;
+    const int lane = lane_id();
+    const int KVH = p.num_kv_heads, P = p.max_num_partitions, PS = p.partition_size;
+    const int G = p.group, M = 16 / G;
+    const int u = blockIdx.x;
+    const int kvh = u % KVH;
+    const int r = u / KVH;
+    const int set = r / P, part = r - set * P;
+    const int lead = set * M;
+    const int h0 = kvh * G;
+    const int mbps = p.max_blocks_per_seq;
+    const int pb = PS / kBlock, blk_begin = part * pb;
+
+    // One round trip: the members' lengths (scalar loads), their table entries
+    // over the partition (lane j: entry blk_begin + j, clamped to the row) and
+    // the 16 query rows (tile row i: head h0 + i % G of sequence lead + i / G).
+    int mlen[kMaxMembers], mrow[kMaxMembers];
+    {
+        const int bi = min(blk_begin + lane, mbps - 1);
+#pragma unroll
+        for (int i = 0; i < kMaxMembers; ++i) {
+            const int f = min(lead + min(i, M - 1), p.num_seqs - 1);
+            mlen[i] = p.seq_lens[f];
+            mrow[i] = p.block_tables[(size_t)f * mbps + bi];
+        }
+    }
+    typename Path::QRegs qr;
+    load_q_rows<Path>(qr, p, lead, h0, G, M);
+    __builtin_amdgcn_sched_barrier(0);
+
+    auto fits = [&](int len) {   // the partition exists and the sequence is well formed
+        return len > part * PS && (len - 1) / PS + 1 <= P && (len + kBlock - 1) / kBlock <= mbps;
+    };
+    unsigned exists = 0, match = 0;
+    {
+        const int tend = min(mlen[0], (part + 1) * PS);
+        const int nblk = (tend - part * PS + kBlock - 1) / kBlock;   // <= 64 blocks
+#pragma unroll
+        for (int i = 0; i < kMaxMembers; ++i) {
+            const bool in = i < M && lead + i < p.num_seqs;
+            exists |= (in && mlen[i] > part * PS) ? 1u << i : 0u;
+            const bool ok = in && fits(mlen[0]) && fits(mlen[i]) &&
+                            min(mlen[i], (part + 1) * PS) == tend;
+            const bool same = __ballot(lane < nblk && mrow[i] != mrow[0]) == 0;
+            match |= (ok && same) ? 1u << i : 0u;
+        }
+    }
+
+    constexpr int TB = D * kBlock * Path::kElem;   // bytes of one K or V tile
+    const char* kbase = p.k_cache + (size_t)kvh * TB;
+    const char* vbase = p.v_cache + (size_t)kvh * TB;
+    const size_t blk_stride = (size_t)KVH * TB;
+    const float sl2 = p.scale_log2;
+
+    int k_cls = 0;   // classes so far; class k goes to team k % kTeams
+    for (unsigned todo = exists; todo != 0u; ++k_cls) {
+        const int c = __ffs(todo) - 1;
+        const unsigned cls = (c == 0 && (match & 1u)) ? (match & todo) : 1u << c;
+        todo &= ~cls;
+        if (k_cls % kTeams != team) continue;
+        int L = mlen[0], rowc = mrow[0];
+#pragma unroll
+        for (int i = 1; i < kMaxMembers; ++i) {
+            L = c == i ? mlen[i] : L;
+            rowc = c == i ? mrow[i] : rowc;
+        }
+        // blocks of the class's partition; a malformed sequence reads none
+        const int nb_seq = (L + kBlock - 1) / kBlock;
+        bool bad = nb_seq > mbps || (L - 1) / PS + 1 > P;
+        const int blk_end = bad ? blk_begin : min(nb_seq, blk_begin + pb);
+        const int tok_end = min(L, (part + 1) * PS);
+        const int first = blk_begin + sub;
+        const int n = first < blk_end ? (blk_end - first + SF - 1) / SF : 0;
+        // Cached loads when other sequences read these blocks too (the class
+        // has several members, or another member's partition starts on the
+        // same block); the rest is streamed.
+        bool cached = __popc(cls) > 1;
+        {
+            const int b0 = __builtin_amdgcn_readfirstlane(rowc);
+#pragma unroll
+            for (int i = 0; i < kMaxMembers; ++i)
+                cached = cached || (((exists >> i) & 1u) != 0u && i != c &&
+                                    __builtin_amdgcn_readfirstlane(mrow[i]) == b0);
+        }
+
+        typename Path::State st;
+        Path::init(st);
+        auto phys = [&](int j) {   // physical id of the wave's block j (clamped to its last)
+            const int v = __builtin_amdgcn_readlane(rowc, sub + max(min(j, n - 1), 0) * SF);
+            const bool ok = (unsigned)v < (unsigned)p.num_blocks;
+            bad = bad || (!ok && n > 0);
+            return ok ? v : 0;
+        };
+        auto valid = [&](int k) { return min(kBlock, tok_end - (first + k * SF) * kBlock); };
+        auto live = [&](int j) { return j < n ? TB : 0; };
+        auto walk = [&](auto nt_tag) {
+            constexpr bool NTL = decltype(nt_tag)::value;
+            constexpr int DP = Path::kDepth;
+            typename Path::Tile t[DP];
+#pragma unroll
+            for (int j = 0; j < DP - 1; ++j) {
+                const int id = phys(j);
+                Path::template load<NTL>(t[j], kbase + (size_t)id * blk_stride,
+                                         vbase + (size_t)id * blk_stride, live(j));
+            }
+            int k = 0;
+            for (; k < (n & ~(DP - 1)); k += DP) {
+#pragma unroll
+                for (int j = 0; j < DP; ++j) {
+                    const int id = phys(k + j + DP - 1);
+                    Path::template load<NTL>(t[(j + DP - 1) % DP], kbase + (size_t)id * blk_stride,
+                                             vbase + (size_t)id * blk_stride, live(k + j + DP - 1));
+                    Path::process(st, t[j], qr, valid(k + j), sl2);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < DP - 1; ++j)
+                if (k + j < n) Path::process(st, t[j], qr, valid(k + j), sl2);
+        };
+        if (cached) walk(std::false_type{});
+        else walk(std::true_type{});
+
+        // The class's rows of this wave's state (tile row i belongs to member
+        // i / G, so classes never share rows), then a count of the team's
+        // waves done with the class: the LDS writes above are complete before
+        // the add (release), and the last wave sees all of them (acquire).
+        const float ltot = Path::wave_l(st);
+        Path::stage(st, ltot, s_acc + sub * 16 * D, s_m + sub * 16, s_l + sub * 16, 16,
+                    ((cls >> ((lane & 15) / G)) & 1u) != 0u);
+        if (lane < kMaxMembers && ((cls >> lane) & 1u)) s_bad[sub * kMaxMembers + lane] = bad ? 1 : 0;
+        int prev = 0;
+        if (lane == 0)
+            prev = __hip_atomic_fetch_add(s_done + c, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (__builtin_amdgcn_readfirstlane(prev) != SF - 1) continue;
+
+        // merge the SF states of the class's rows, in wave order
+        for (unsigned mm = cls; mm != 0u; mm &= mm - 1u) {
+            const int m = __ffs(mm) - 1;
+            int any_bad = 0;
+#pragma unroll
+            for (int v = 0; v < SF; ++v) any_bad |= s_bad[v * kMaxMembers + m];
+            const size_t orow = ((size_t)(lead + m) * P + part) * p.num_heads + h0;
+            for (int e = lane; e < G * (D / 4); e += 64) {
+                const int j = e / (D / 4), d4 = e - j * (D / 4), i = m * G + j;
+                float mx = -INFINITY;
+#pragma unroll
+                for (int v = 0; v < SF; ++v) mx = fmaxf(mx, s_m[v * 16 + i]);
+                f32x4 num = {0.f, 0.f, 0.f, 0.f};
+                float den = 0.f;
+#pragma unroll
+                for (int v = 0; v < SF; ++v) {
+                    const float f = exp2_fast((s_m[v * 16 + i] - mx) * sl2);
+                    num += *reinterpret_cast<const f32x4*>(s_acc + (v * 16 + i) * D + 4 * d4) * f;
+                    den += s_l[v * 16 + i] * f;
+                }
+                f32x4 o = num / den * p.v_scale;
+                if (any_bad) o = f32x4{NAN, NAN, NAN, NAN};
+                st_stream(reinterpret_cast<f32x4*>(p.out + (orow + j) * D) + d4, o);
+                if (d4 == 0) {
+                    st_stream(p.max_logits + orow + j, any_bad ? NAN : mx * p.scale);
+                    st_stream(p.exp_sums + orow + j, any_bad ? NAN : den);
+                }
+            }
+        }
+    }
+}
+
+// --------------------------------------------------------------------------
 // Host side
 // --------------------------------------------------------------------------
 static size_t merge_lds_bytes(int NW, int nh_max, int D, int hp) {
@@ -714,6 +926,22 @@ static int launch_nw(int NW, const DecodeParams& p0, int grid, int nh_max, hipSt
         case 2: hipLaunchKernelGGL((pa_decode_kernel<Path, D, 2, V2>), dim3(grid), dim3(128), lds, st, p); break;
         case 4: hipLaunchKernelGGL((pa_decode_kernel<Path, D, 4, V2>), dim3(grid), dim3(256), lds, st, p); break;
         case 8: hipLaunchKernelGGL((pa_decode_kernel<Path, D, 8, V2>), dim3(grid), dim3(512), lds, st, p); break;
+        default: return PA_ERR_INVALID_ARG;
+    }
+    return launch_status();
+}
+
+// The set kernel: NW waves per (set, partition, KV head) workgroup, in teams
+// of SF waves per class.
+template <class Path, int D>
+static int launch_set(const DecodeParams& p, int NW, int grid, hipStream_t st) {
+    constexpr int SF = PA_SET_SPLIT;
+    const size_t lds = (size_t)SF * (16 * D + 2 * 16 + kMaxMembers) * sizeof(float) +
+                       kMaxMembers * sizeof(int);
+    switch (NW) {
+        case SF: hipLaunchKernelGGL((pa_decode_set_kernel<Path, D, SF, SF>), dim3(grid), dim3(64 * SF), lds, st, p); break;
+        case 2 * SF: hipLaunchKernelGGL((pa_decode_set_kernel<Path, D, 2 * SF, SF>), dim3(grid), dim3(128 * SF), lds, st, p); break;
+        case 4 * SF: hipLaunchKernelGGL((pa_decode_set_kernel<Path, D, 4 * SF, SF>), dim3(grid), dim3(256 * SF), lds, st, p); break;
         default: return PA_ERR_INVALID_ARG;
     }
     return launch_status();
@@ -829,6 +1057,22 @@ extern "C" int pa_decode_v2(float* tmp_out, float* exp_sums, float* max_logits, 
     p.max_logits = max_logits;
     p.max_num_partitions = max_num_partitions;
     p.partition_size = partition_size;
+    const bool fp8 = kv_cache_dtype == PA_KV_FP8_E4M3;
+    // Larger batches of GQA groups that fill a score tile evenly go to the set
+    // kernel: one workgroup per (set of 16/G sequences, partition, KV head).
+    if (PA_SET_WAVES > 0 && !PA_V2_WAVES && num_seqs > 64 && p.group >= 2 && p.group <= kMaxMembers &&
+        16 % p.group == 0 && partition_size <= 64 * kBlock) {
+        const int M = 16 / p.group;
+        const long long sets = (num_seqs + M - 1) / M;
+        const long long grid = sets * max_num_partitions * num_kv_heads;
+        if (grid > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
+        hipStream_t st = as_stream(stream);
+        if (fp8)
+            return head_size == 128 ? launch_set<MfmaPath8<128>, 128>(p, PA_SET_WAVES, (int)grid, st)
+                                    : launch_set<MfmaPath8<64>, 64>(p, PA_SET_WAVES, (int)grid, st);
+        return head_size == 128 ? launch_set<MfmaPath<128>, 128>(p, PA_SET_WAVES, (int)grid, st)
+                                : launch_set<MfmaPath<64>, 64>(p, PA_SET_WAVES, (int)grid, st);
+    }
     // the grid covers whole snake rounds; workgroups past the real units exit
     p.num_cus = compute_units(stream);
     p.unit_period = p.num_cus > 0 && p.num_cus % kXcds == 0 ? p.num_cus : 1;
@@ -836,7 +1080,6 @@ extern "C" int pa_decode_v2(float* tmp_out, float* exp_sums, float* max_logits, 
     const long long grid = (units + p.unit_period - 1) / p.unit_period * p.unit_period;
     if (grid > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
     // a sequence has on average about half of max_num_partitions partitions
-    const bool fp8 = kv_cache_dtype == PA_KV_FP8_E4M3;
     const int nw = PA_V2_WAVES ? PA_V2_WAVES
                                : pick_waves(units / 2, partition_size / 16, head_size, fp8 ? 1 : 2);
     return launch_decode<true>(p, head_size, fp8, nw, (int)grid, as_stream(stream));

@@ -36,12 +36,26 @@ REDUCE_CASES = [
 # 200 sequences span four 64-lane chunks of its lookup, 128-block partitions
 # leave the partly filled ones unsorted, 1,200 sequences x 8 partitions
 # exceed what the device holds (plain order), and 64 sequences x 8 KV heads x
-# up to 16 partitions exceed it with no shared blocks (XCD-major order)
+# up to 16 partitions exceed it with no shared blocks (XCD-major order).
+# Beyond 64 sequences these take G = 7: G = 2, 4, 8 go to the set kernel.
 ORDER_CASES = [
-    ("order_200seqs", 200, 8, 2, 64, 1, 700, 128),
+    ("order_200seqs", 200, 14, 2, 64, 1, 700, 128),
     ("order_ps2048", 3, 8, 2, 128, 1, 5000, 2048),
-    ("order_big_grid", 1200, 8, 2, 64, 1, 1000, 128),
+    ("order_big_grid", 1200, 14, 2, 64, 1, 1000, 128),
     ("order_xcd_major", 64, 32, 8, 128, 1, 1024, 64),
+]
+# the set kernel (v2, more than 64 sequences, G = 2, 4, 8, PS <= 1024): sets of
+# 16/G sequences, the last one cut short by the batch (70 = 8 x 8 + 6,
+# 67 = 2 x 33 + 1); 64-block partitions (every entry of the class check's
+# table window used); one-block partitions, where most waves walk nothing;
+# a grid far beyond what the device holds
+SET_CASES = [
+    ("set_g4_d128", 72, 8, 2, 128, 1, 700, 128),
+    ("set_g2_d64", 70, 4, 2, 64, 1, 500, 64),
+    ("set_g2_d128", 66, 8, 4, 128, 1, 800, 256),
+    ("set_g8_d128", 67, 16, 2, 128, 1, 1100, 1024),
+    ("set_g4_ps16", 80, 8, 2, 64, 1, 300, 16),
+    ("set_g4_big_grid", 1200, 8, 2, 64, 1, 1000, 128),
 ]
 
 
@@ -98,8 +112,8 @@ def test_v1_matches_oracle(case):
     assert_parity(run_v1(inp), ref_out(inp), case[0])
 
 
-@pytest.mark.parametrize("case", CASES + REDUCE_CASES + ORDER_CASES,
-                         ids=[c[0] for c in CASES + REDUCE_CASES + ORDER_CASES])
+@pytest.mark.parametrize("case", CASES + REDUCE_CASES + ORDER_CASES + SET_CASES,
+                         ids=[c[0] for c in CASES + REDUCE_CASES + ORDER_CASES + SET_CASES])
 def test_v2_partials_and_merge_match_oracle(case):
     inp = make_case(case, 3)
     ps = case[7]
@@ -348,22 +362,98 @@ def test_partitions_shared_by_sequences_match_private_copies(G, LEN, PS):
     shared = wl.DecodeInputs(w, inp.seed, L, bt, inp.num_blocks, inp.q, inp.k_cache, inp.v_cache)
     oracle.poison_unused(shared.k_cache, shared.v_cache, shared.block_tables, shared.seq_lens, 16)
 
-    # private copies: every table entry gets its own physical block
-    used = [(s, i) for s in range(S) for i in range(-(-int(L[s]) // 16))]
+    assert_shared_equals_private(shared, PS, f"shared G={G}")
+
+
+def private_copies(inp):
+    """The same sequences with every table entry in a physical block of its
+    own (shared blocks copied), NaN in every other slot."""
+    L, bt = inp.seq_lens, inp.block_tables
+    used = [(s, i) for s in range(bt.shape[0]) for i in range(-(-int(L[s]) // 16))]
     kc = np.full((len(used) + 3,) + inp.k_cache.shape[1:], np.float16(np.nan))
     vc = np.full((len(used) + 3,) + inp.v_cache.shape[1:], np.float16(np.nan))
     bt2 = np.full_like(bt, -1)
     for n, (s, i) in enumerate(used):
-        kc[n + 3] = shared.k_cache[bt[s, i]]
-        vc[n + 3] = shared.v_cache[bt[s, i]]
+        kc[n + 3] = inp.k_cache[bt[s, i]]
+        vc[n + 3] = inp.v_cache[bt[s, i]]
         bt2[s, i] = n + 3
-    private = wl.DecodeInputs(w, inp.seed, L, bt2, kc.shape[0], inp.q, kc, vc)
+    return wl.DecodeInputs(inp.workload, inp.seed, L, bt2, kc.shape[0], inp.q, kc, vc)
 
+
+def assert_shared_equals_private(shared, PS, label):
     out_s, tmp_s, es_s, ml_s, P = run_v2(shared, PS)
-    out_p, tmp_p, es_p, ml_p, _ = run_v2(private, PS)
+    out_p, tmp_p, es_p, ml_p, _ = run_v2(private_copies(shared), PS)
     valid = ~np.isnan(es_p)
     assert np.array_equal(tmp_s[valid], tmp_p[valid])
     assert np.array_equal(es_s[valid], es_p[valid]) and np.array_equal(ml_s[valid], ml_p[valid])
     assert np.isnan(es_s[~valid]).all(), "a partition past a sequence was written"
     assert np.array_equal(out_s, out_p)
-    assert_parity(out_s, ref_out(shared), f"shared G={G}")
+    assert_parity(out_s, ref_out(shared), label)
+
+
+@pytest.mark.parametrize("G,PS", [(2, 128), (4, 64), (4, 512), (8, 256)])
+def test_set_kernel_shared_partitions_match_private_copies(G, PS):
+    """The set kernel (more than 64 sequences, sets of M = 16/G): sequences
+    that read the same blocks equal, bit for bit, the same sequences reading
+    private copies, and the oracle.  Covered: a whole set that shares; a set
+    whose second member differs in one block; a member with a shorter range in
+    the last partition; a short leader whose longer members share among
+    themselves; sharing across two sets' boundary; a last set cut short by the
+    batch (67 sequences)."""
+    M, S, KVH, D, LEN = 16 // G, 67, 2, 128, 600
+    w = wl.small_workload("share_sets", num_seqs=S, num_heads=G * KVH, num_kv_heads=KVH,
+                          head_size=D, seq_len_lo=LEN, seq_len_hi=LEN, partition_size=PS)
+    inp = wl.make_inputs(w, 23)
+    L = inp.seq_lens.copy()
+    nb = -(-LEN // 16)
+    L[3 * M - 1] = LEN - 10                  # same blocks as its leader, shorter last partition
+    L[3 * M] = 10                            # a short leader
+    pattern = [(d, 0, 0, nb) for d in range(1, M)]                    # set 0: one copy
+    pattern += [(d, M, 0, nb) for d in range(M + 1, 2 * M)]           # set 1 ...
+    pattern += [(d, 2 * M, 0, nb) for d in range(2 * M + 1, 3 * M)]   # set 2
+    pattern += [(d, 3 * M + 1, 0, nb) for d in range(3 * M + 2, 4 * M)]   # set 3 without its leader
+    pattern += [(5 * M, 5 * M - 1, 0, nb)]                            # across sets 4 and 5
+    last = S - S % M
+    pattern += [(d, last, 0, nb) for d in range(last + 1, S)]         # the cut-short last set
+    bt = _share_tables(inp.block_tables, L, pattern)
+    bt[M + 1, 2] = inp.block_tables[M + 1, 2]   # ... but set 1's second member differs in one block
+    shared = wl.DecodeInputs(w, inp.seed, L, bt, inp.num_blocks, inp.q, inp.k_cache, inp.v_cache)
+    oracle.poison_unused(shared.k_cache, shared.v_cache, shared.block_tables, shared.seq_lens, 16)
+    assert_shared_equals_private(shared, PS, f"set kernel G={G} PS={PS}")
+
+
+def test_set_kernel_edge_cases():
+    """The set kernel: a zero-length sequence (no partition, zeros after the
+    merge), a one-token sequence (returns V exactly), and an out-of-range block
+    id in a partition that a whole set shares (NaN for those four sequences
+    only).  The pools are allocated four blocks larger than the num_blocks the
+    call sees, so the id stays inside memory even if the check were missing."""
+    S, H, KVH, D, PS = 70, 8, 2, 128, 128
+    w = wl.small_workload("set_edges", num_seqs=S, num_heads=H, num_kv_heads=KVH, head_size=D,
+                          seq_len_lo=1, seq_len_hi=700, partition_size=PS)
+    inp = wl.make_inputs(w, 24)
+    L = inp.seq_lens
+    L[5], L[6] = 0, 1
+    n8 = -(-int(L[8]) // 16)
+    L[9:12] = L[8]                          # set 2 (sequences 8-11) reads one copy
+    bt = inp.block_tables
+    bt[9:12, :n8] = bt[8, :n8]
+    oracle.poison_unused(inp.k_cache, inp.v_cache, bt, L, 16)
+    ref = ref_out(inp)
+    out = run_v2(inp, PS)[0]
+    assert (out[5] == 0).all()
+    b = bt[6, 0]
+    assert np.array_equal(out[6], inp.v_cache[b, np.arange(H) // (H // KVH), :, 0].astype(np.float32))
+    assert_parity(out, ref, "set kernel")
+
+    NB = inp.num_blocks
+    kc = np.concatenate([inp.k_cache, np.zeros((4,) + inp.k_cache.shape[1:], np.float16)])
+    vc = np.concatenate([inp.v_cache, np.zeros((4,) + inp.v_cache.shape[1:], np.float16)])
+    bt_bad = bt.copy()
+    bt_bad[8:12, 3] = NB + 2
+    o = pa.paged_attention_v2(to_dev(inp.q), to_dev(kc)[:NB], to_dev(vc)[:NB], to_dev(bt_bad),
+                              to_dev(L), inp.scale, PS, w.max_seq_len).cpu().numpy()
+    assert np.isnan(o[8:12]).all()
+    ok = np.ones(S, dtype=bool)
+    ok[8:12] = False
+    assert_parity(o[ok], ref[ok], "set kernel, other sequences unaffected")

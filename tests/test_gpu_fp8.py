@@ -164,12 +164,13 @@ def test_fp8_write_then_decode_pipeline():
     assert_parity(out, ref, "fp8 write + decode")
 
 
-def test_fp8_partitions_shared_by_sequences_match_private_copies():
+@pytest.mark.parametrize("S", [8, 72], ids=["units", "set_kernel"])
+def test_fp8_partitions_shared_by_sequences_match_private_copies(S):
     """fp8 pools: v2 units of sequences that read the same blocks over a
     partition (one tile for the aligned set of four, G = 4) equal, bit for bit,
     the same sequences reading private copies of the codes, and the oracle over
-    the decoded values."""
-    S, KVH, G, D, PS = 8, 2, 4, 128, 128
+    the decoded values; with 72 sequences the set kernel runs."""
+    KVH, G, D, PS = 2, 4, 128, 128
     inp, k8, v8, ks, vs = fp8_case("share8", S, G * KVH, KVH, D, 400, 400, seed=33)
     nb = -(-400 // 16)
     bt = inp.block_tables.copy()
@@ -232,11 +233,15 @@ def test_fp8_long_unit_crosses_table_windows(H, D, L):
 # v2 unit orders on fp8 pools: 64 sequences x 8 KV heads x up to 16
 # partitions is more than the device holds at once and shares no blocks (the
 # XCD-major order); 1,200 sequences exceed it with the plain order; 200
-# sequences fit (largest-first order over four lookup chunks).
+# sequences fit (largest-first order over four lookup chunks).  Beyond 64
+# sequences G = 7 keeps these on the one-unit-per-sequence kernel; with G = 4
+# and 8 they take the set kernel.
 FP8_ORDER_CASES = [
     ("xcd_major", 64, 32, 8, 128, 1, 1024, 64),
-    ("big_grid", 1200, 8, 2, 64, 1, 1000, 128),
-    ("resident_200", 200, 8, 2, 64, 1, 700, 128),
+    ("big_grid", 1200, 14, 2, 64, 1, 1000, 128),
+    ("resident_200", 200, 14, 2, 64, 1, 700, 128),
+    ("set_g4_big_grid", 1200, 8, 2, 64, 1, 1000, 128),
+    ("set_g8_d128", 130, 16, 2, 128, 1, 900, 256),
 ]
 
 
