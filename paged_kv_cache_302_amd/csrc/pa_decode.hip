@@ -720,7 +720,14 @@ __global__ __launch_bounds__(64 * NW) void pa_decode_set_kernel(DecodeParams p) 
     auto fits = [&](int len) {   // the partition exists and the sequence is well formed
         return len > part * PS && (len - 1) / PS + 1 <= P && (len + kBlock - 1) / kBlock <= mbps;
     };
+    // The leader's class: members with the leader's token range in the
+    // partition and its table entries over it, the last one excepted (after a
+    // fork, copy-on-write gives every sample its own copy of the partly filled
+    // last block).  When a member's last block differs, each member's last
+    // block is walked on its own, in the class's tile but folded into its own
+    // rows only, after the shared blocks: the same steps as its private walk.
     unsigned exists = 0, match = 0;
+    bool own_last = false;
     {
         const int tend = min(mlen[0], (part + 1) * PS);
         const int nblk = (tend - part * PS + kBlock - 1) / kBlock;   // <= 64 blocks
@@ -730,8 +737,10 @@ __global__ __launch_bounds__(64 * NW) void pa_decode_set_kernel(DecodeParams p) 
             exists |= (in && mlen[i] > part * PS) ? 1u << i : 0u;
             const bool ok = in && fits(mlen[0]) && fits(mlen[i]) &&
                             min(mlen[i], (part + 1) * PS) == tend;
-            const bool same = __ballot(lane < nblk && mrow[i] != mrow[0]) == 0;
-            match |= (ok && same) ? 1u << i : 0u;
+            const unsigned long long diff = __ballot(lane < nblk && mrow[i] != mrow[0]);
+            const bool body = (diff & ~(1ull << (max(nblk, 1) - 1))) == 0;
+            match |= (ok && body) ? 1u << i : 0u;
+            own_last = own_last || (ok && body && diff != 0);
         }
     }
 
@@ -759,7 +768,29 @@ __global__ __launch_bounds__(64 * NW) void pa_decode_set_kernel(DecodeParams p) 
         const int blk_end = bad ? blk_begin : min(nb_seq, blk_begin + pb);
         const int tok_end = min(L, (part + 1) * PS);
         const int first = blk_begin + sub;
-        const int n = first < blk_end ? (blk_end - first + SF - 1) / SF : 0;
+        // Members' own last blocks (leader's class only): the shared walk
+        // stops before the last block, and the wave whose share holds it
+        // walks every member's copy after its shared blocks.
+        const bool split = own_last && c == 0 && cls != 1u && blk_end > blk_begin;
+        const int shared_end = split ? blk_end - 1 : blk_end;
+        const int n_sh = first < shared_end ? (shared_end - first + SF - 1) / SF : 0;
+        const int j_last = blk_end - 1 - blk_begin;   // the last block's index in the partition
+        const int n = n_sh + ((split && j_last % SF == sub) ? __popc(cls) : 0);
+        const int last_valid = tok_end - (blk_end - 1) * kBlock;
+        auto member_of = [&](int j) {   // member whose own last block is walk step j >= n_sh
+            unsigned b = cls;
+            for (int x = n_sh; x < j; ++x) b &= b - 1u;
+            return __ffs(b) - 1;
+        };
+        // lane m: member m's own last block (static register indices only)
+        int own_ids = 0;
+        if (split) {
+#pragma unroll
+            for (int i = 0; i < kMaxMembers; ++i) {
+                const int v = __builtin_amdgcn_readlane(mrow[i], j_last);
+                own_ids = lane == i ? v : own_ids;
+            }
+        }
         // Cached loads when other sequences read these blocks too (the class
         // has several members, or another member's partition starts on the
         // same block); the rest is streamed.
@@ -774,17 +805,40 @@ __global__ __launch_bounds__(64 * NW) void pa_decode_set_kernel(DecodeParams p) 
 
         typename Path::State st;
         Path::init(st);
-        auto phys = [&](int j) {   // physical id of the wave's block j (clamped to its last)
-            const int v = __builtin_amdgcn_readlane(rowc, sub + max(min(j, n - 1), 0) * SF);
-            const bool ok = (unsigned)v < (unsigned)p.num_blocks;
-            bad = bad || (!ok && n > 0);
-            return ok ? v : 0;
-        };
-        auto valid = [&](int k) { return min(kBlock, tok_end - (first + k * SF) * kBlock); };
-        auto live = [&](int j) { return j < n ? TB : 0; };
-        auto walk = [&](auto nt_tag) {
+        // The walk: steps j < n_sh are the wave's shared blocks, the rest
+        // (SPLIT only) the members' own last blocks, each folded into its
+        // member's rows only.  An id outside the pool marks the class bad
+        // (a member's own last block: that member) and reads block 0.
+        unsigned bad_own = 0;
+        auto walk = [&](auto nt_tag, auto split_tag) {
             constexpr bool NTL = decltype(nt_tag)::value;
+            constexpr bool SPLIT = decltype(split_tag)::value;
             constexpr int DP = Path::kDepth;
+            auto phys = [&](int j) {   // physical id of walk step j (clamped to the last)
+                j = max(min(j, n - 1), 0);
+                if (!SPLIT || j < n_sh) {
+                    const int v = __builtin_amdgcn_readlane(rowc, sub + j * SF);
+                    const bool ok = (unsigned)v < (unsigned)p.num_blocks;
+                    bad = bad || (!ok && n > 0);
+                    return ok ? v : 0;
+                }
+                const int m = member_of(j);
+                const int v = __builtin_amdgcn_readlane(own_ids, m);
+                const bool ok = (unsigned)v < (unsigned)p.num_blocks;
+                bad_own |= ok ? 0u : 1u << m;
+                return ok ? v : 0;
+            };
+            auto valid = [&](int k) {
+                return (!SPLIT || k < n_sh) ? min(kBlock, tok_end - (first + k * SF) * kBlock) : last_valid;
+            };
+            auto live = [&](int j) { return j < n ? TB : 0; };
+            auto step = [&](typename Path::Tile& t, int k) {
+                if constexpr (SPLIT)   // a shared block: every head; an own last block: its member's
+                    Path::template process<true>(st, t, qr, valid(k), sl2,
+                                                 k < n_sh || (lane & 15) / G == member_of(k));
+                else
+                    Path::process(st, t, qr, valid(k), sl2);
+            };
             typename Path::Tile t[DP];
 #pragma unroll
             for (int j = 0; j < DP - 1; ++j) {
@@ -799,15 +853,16 @@ __global__ __launch_bounds__(64 * NW) void pa_decode_set_kernel(DecodeParams p) 
                     const int id = phys(k + j + DP - 1);
                     Path::template load<NTL>(t[(j + DP - 1) % DP], kbase + (size_t)id * blk_stride,
                                              vbase + (size_t)id * blk_stride, live(k + j + DP - 1));
-                    Path::process(st, t[j], qr, valid(k + j), sl2);
+                    step(t[j], k + j);
                 }
             }
 #pragma unroll
             for (int j = 0; j < DP - 1; ++j)
-                if (k + j < n) Path::process(st, t[j], qr, valid(k + j), sl2);
+                if (k + j < n) step(t[j], k + j);
         };
-        if (cached) walk(std::false_type{});
-        else walk(std::true_type{});
+        if (split) walk(std::false_type{}, std::true_type{});   // a shared class: cached loads
+        else if (cached) walk(std::false_type{}, std::false_type{});
+        else walk(std::true_type{}, std::false_type{});
 
         // The class's rows of this wave's state (tile row i belongs to member
         // i / G, so classes never share rows), then a count of the team's
@@ -816,7 +871,8 @@ __global__ __launch_bounds__(64 * NW) void pa_decode_set_kernel(DecodeParams p) 
         const float ltot = Path::wave_l(st);
         Path::stage(st, ltot, s_acc + sub * 16 * D, s_m + sub * 16, s_l + sub * 16, 16,
                     ((cls >> ((lane & 15) / G)) & 1u) != 0u);
-        if (lane < kMaxMembers && ((cls >> lane) & 1u)) s_bad[sub * kMaxMembers + lane] = bad ? 1 : 0;
+        if (lane < kMaxMembers && ((cls >> lane) & 1u))
+            s_bad[sub * kMaxMembers + lane] = (bad || ((bad_own >> lane) & 1u)) ? 1 : 0;
         int prev = 0;
         if (lane == 0)
             prev = __hip_atomic_fetch_add(s_done + c, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);

@@ -229,9 +229,12 @@ struct MfmaPath {
     }
 
     // nvalid: tokens of the block inside the sequence (the rest is never
-    // read), masked to -inf before the softmax.
+    // read), masked to -inf before the softmax.  With ROWS, only the heads
+    // whose lanes pass `keep` take the block in (the others' state is left
+    // exactly as it was; the kept heads get the same arithmetic as without).
+    template <bool ROWS = false>
     __device__ __forceinline__ static void process(State& st, Tile& t, const QRegs& qr,
-                                                   int nvalid, float sl2) {
+                                                   int nvalid, float sl2, bool keep = true) {
         const int l = lane_id(), g = l >> 4;
         f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -251,11 +254,17 @@ struct MfmaPath {
         }
         float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
         bm = col4_max(bm);
-        const float mn = fmaxf(st.m, bm);
-        const float corr = exp2_fast((st.m - mn) * sl2);
+        float mn = fmaxf(st.m, bm);
+        float corr = exp2_fast((st.m - mn) * sl2);
         float pr[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) pr[r] = exp2_fast((s[r] - mn) * sl2);
+        if constexpr (ROWS) {
+            mn = keep ? mn : st.m;
+            corr = keep ? corr : 1.f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) pr[r] = keep ? pr[r] : 0.f;
+        }
         st.l = st.l * corr + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
         st.m = mn;
         const f16x4 pv = {(f16)pr[0], (f16)pr[1], (f16)pr[2], (f16)pr[3]};
@@ -484,8 +493,10 @@ struct MfmaPath8 : MfmaPath<D> {
             t.v[nt] = *reinterpret_cast<const uint32_t*>(slot + kTileBytes + 16 * (16 * nt + i) + 4 * g);
     }
 
+    template <bool ROWS = false>
     __device__ __forceinline__ static void process(typename Base::State& st, Tile& t,
-                                                   const QRegs& qr, int nvalid, float sl2) {
+                                                   const QRegs& qr, int nvalid, float sl2,
+                                                   bool keep = true) {
         const int l = lane_id(), g = l >> 4;
         f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -506,11 +517,17 @@ struct MfmaPath8 : MfmaPath<D> {
         }
         float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
         bm = col4_max(bm);
-        const float mn = fmaxf(st.m, bm);
-        const float corr = exp2_fast((st.m - mn) * sl2);
+        float mn = fmaxf(st.m, bm);
+        float corr = exp2_fast((st.m - mn) * sl2);
         float pr[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) pr[r] = exp2_fast((s[r] - mn) * sl2);
+        if constexpr (ROWS) {   // as in the fp16 path
+            mn = keep ? mn : st.m;
+            corr = keep ? corr : 1.f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) pr[r] = keep ? pr[r] : 0.f;
+        }
         st.l = st.l * corr + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
         st.m = mn;
         const f16x4 pv = {(f16)pr[0], (f16)pr[1], (f16)pr[2], (f16)pr[3]};

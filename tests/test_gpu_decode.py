@@ -398,8 +398,9 @@ def test_set_kernel_shared_partitions_match_private_copies(G, PS):
     private copies, and the oracle.  Covered: a whole set that shares; a set
     whose second member differs in one block; a member with a shorter range in
     the last partition; a short leader whose longer members share among
-    themselves; sharing across two sets' boundary; a last set cut short by the
-    batch (67 sequences)."""
+    themselves; sharing across two sets' boundary; a set that shares all but
+    its members' last blocks (a fork after copy-on-write); a last set cut
+    short by the batch (67 sequences)."""
     M, S, KVH, D, LEN = 16 // G, 67, 2, 128, 600
     w = wl.small_workload("share_sets", num_seqs=S, num_heads=G * KVH, num_kv_heads=KVH,
                           head_size=D, seq_len_lo=LEN, seq_len_hi=LEN, partition_size=PS)
@@ -413,6 +414,7 @@ def test_set_kernel_shared_partitions_match_private_copies(G, PS):
     pattern += [(d, 2 * M, 0, nb) for d in range(2 * M + 1, 3 * M)]   # set 2
     pattern += [(d, 3 * M + 1, 0, nb) for d in range(3 * M + 2, 4 * M)]   # set 3 without its leader
     pattern += [(5 * M, 5 * M - 1, 0, nb)]                            # across sets 4 and 5
+    pattern += [(d, 6 * M, 0, nb - 1) for d in range(6 * M + 1, 7 * M)]   # set 6: own last blocks
     last = S - S % M
     pattern += [(d, last, 0, nb) for d in range(last + 1, S)]         # the cut-short last set
     bt = _share_tables(inp.block_tables, L, pattern)
@@ -424,10 +426,12 @@ def test_set_kernel_shared_partitions_match_private_copies(G, PS):
 
 def test_set_kernel_edge_cases():
     """The set kernel: a zero-length sequence (no partition, zeros after the
-    merge), a one-token sequence (returns V exactly), and an out-of-range block
-    id in a partition that a whole set shares (NaN for those four sequences
-    only).  The pools are allocated four blocks larger than the num_blocks the
-    call sees, so the id stays inside memory even if the check were missing."""
+    merge), a one-token sequence (returns V exactly), an out-of-range block id
+    in a partition that a whole set shares (NaN for those four sequences only),
+    and one in a member's own last block of a set that shares the rest (NaN
+    for that member only).  The pools are allocated four blocks larger than
+    the num_blocks the call sees, so the ids stay inside memory even if the
+    check were missing."""
     S, H, KVH, D, PS = 70, 8, 2, 128, 128
     w = wl.small_workload("set_edges", num_seqs=S, num_heads=H, num_kv_heads=KVH, head_size=D,
                           seq_len_lo=1, seq_len_hi=700, partition_size=PS)
@@ -438,6 +442,8 @@ def test_set_kernel_edge_cases():
     L[9:12] = L[8]                          # set 2 (sequences 8-11) reads one copy
     bt = inp.block_tables
     bt[9:12, :n8] = bt[8, :n8]
+    L[16:20] = 300                          # set 4 reads one copy of all but its last blocks
+    bt[17:20, :18] = bt[16, :18]
     oracle.poison_unused(inp.k_cache, inp.v_cache, bt, L, 16)
     ref = ref_out(inp)
     out = run_v2(inp, PS)[0]
@@ -451,9 +457,11 @@ def test_set_kernel_edge_cases():
     vc = np.concatenate([inp.v_cache, np.zeros((4,) + inp.v_cache.shape[1:], np.float16)])
     bt_bad = bt.copy()
     bt_bad[8:12, 3] = NB + 2
+    bt_bad[18, 18] = NB + 2
     o = pa.paged_attention_v2(to_dev(inp.q), to_dev(kc)[:NB], to_dev(vc)[:NB], to_dev(bt_bad),
                               to_dev(L), inp.scale, PS, w.max_seq_len).cpu().numpy()
-    assert np.isnan(o[8:12]).all()
+    assert np.isnan(o[8:12]).all() and np.isnan(o[18]).all()
     ok = np.ones(S, dtype=bool)
     ok[8:12] = False
+    ok[18] = False
     assert_parity(o[ok], ref[ok], "set kernel, other sequences unaffected")
