@@ -44,9 +44,11 @@
  *     up at the caller's next synchronisation, as HIP does.
  *   - Values the host cannot see (block ids, seq_lens, slots) are checked on
  *     the device so that no bad value turns into an out-of-bounds access:
- *     a decode unit that meets a block id outside [0, num_blocks) or a length
- *     longer than its block-table row writes NaN into its outputs instead of
- *     reading; the cache write skips slots outside the pool.
+ *     a sequence whose walk over a partition (v2) or over its whole table
+ *     (v1) meets a block id outside [0, num_blocks), or whose length is
+ *     longer than its block-table row, gets NaN in that walk's output rows
+ *     (every head of the KV group) instead of a read; the cache write skips
+ *     slots outside the pool.
  */
 #ifndef PA_MI355X_PA_H
 #define PA_MI355X_PA_H
