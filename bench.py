@@ -6,8 +6,9 @@
 One step is one decode step of the whole hot path over one synthetic batch:
 the cache write of the step's new token per sequence (reshape_and_cache at
 logical position L_s - 1), then the decode attention over L_s tokens
-(pa_decode_v2 + pa_reduce, or pa_decode_v1).  Inputs are generated once and
-are resident in HBM before timing starts.
+(pa_decode_v2 + pa_reduce, or pa_decode_v1; batches that share blocks, the
+shared_prefix and fork workloads, call pa_decode_v2_shared).  Inputs are
+generated once and are resident in HBM before timing starts.
 
 The metric is effective KV bandwidth: sum_s L_s * 2 * num_kv_heads * head_size
 * 2 bytes per step divided by the step time, also given as a fraction of the
@@ -16,7 +17,7 @@ MI355X HBM peak (8 TB/s).  Rank 0 prints one JSON line.
 `--workload fork` times the first decode step after a parallel-sampling fork:
 the native block manager hands out the step's slots, tables and
 copy-on-write pairs before timing, and the step is copy_blocks +
-reshape_and_cache + pa_decode_v2 + pa_reduce.
+reshape_and_cache + pa_decode_v2_shared + pa_reduce.
 """
 from __future__ import annotations
 
@@ -398,7 +399,7 @@ def main_fork(args):
         pa.reshape_and_cache(key, val, kc, vc, slot_d)
         if ev is not None:
             ev[2].record(stream)
-        pa.pa_decode_v2(tmp, es, ml, q, kc, vc, bt, sl, w.scale, PS)
+        pa.pa_decode_v2_shared(tmp, es, ml, q, kc, vc, bt, sl, w.scale, PS)
         if ev is not None:
             ev[3].record(stream)
         pa.pa_reduce(out, tmp, es, ml, sl, PS)
@@ -432,7 +433,7 @@ def main_fork(args):
         "data": "synthetic",
         "config": {
             "workload": "fork",
-            "kernel": "copy_blocks + reshape_and_cache + pa_decode_v2 + pa_reduce",
+            "kernel": "copy_blocks + reshape_and_cache + pa_decode_v2_shared + pa_reduce",
             "groups": w.groups, "samples": w.samples, "prompt_len": w.prompt_len,
             "num_seqs": S, "num_heads": H, "num_kv_heads": KVH, "head_size": D,
             "block_size": B, "partition_size": PS, "num_blocks": NB,
@@ -445,14 +446,15 @@ def main_fork(args):
         "kernels_us": {
             "copy_blocks": round(med(0) * 1e3, 2),
             "reshape_and_cache": round(med(1) * 1e3, 2),
-            "pa_decode_v2": round(med(2) * 1e3, 2),
+            "pa_decode_v2_shared": round(med(2) * 1e3, 2),
             "pa_reduce": round(med(3) * 1e3, 2),
         },
-        "kernels_us_cold": {"pa_decode_v2": round(float(np.median(
+        "kernels_us_cold": {"pa_decode_v2_shared": round(float(np.median(
             [e[2].elapsed_time(e[3]) for e in cold])) * 1e3, 2)},
-        "roofline": roofline_entry("pa_decode_v2", unique_bytes, dec_s,
-                                   read_traffic("pa_decode_v2", "fork")),
-        "roofline_warm": roofline_entry("pa_decode_v2", unique_bytes, dec_warm_s, cache="warm"),
+        "roofline": roofline_entry("pa_decode_v2_shared", unique_bytes, dec_s,
+                                   read_traffic("pa_decode_v2_shared", "fork")),
+        "roofline_warm": roofline_entry("pa_decode_v2_shared", unique_bytes, dec_warm_s,
+                                        cache="warm"),
         "copy_blocks": {
             "bytes_per_launch": copy_bytes,
             "achieved_gbs": round(copy_bytes / copy_s / 1e9, 2),
@@ -666,6 +668,8 @@ def main():
     tmp, es, ml = pa.v2_scratch(S, H, D, P, dev)
     out = torch.empty((S, H, D), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
+    # batches built to share blocks take the entry point made for them
+    shared = bool(w.group_size)
 
     def step(ev=None):
         if ev is not None:
@@ -674,7 +678,8 @@ def main():
         if ev is not None:
             ev[1].record(stream)
         if args.kernel == "v2":
-            pa.pa_decode_v2(tmp, es, ml, q, kc, vc, bt, sl, inp.scale, PS, ks, vs)
+            pa.pa_decode_v2(tmp, es, ml, q, kc, vc, bt, sl, inp.scale, PS, ks, vs,
+                            shared_blocks=shared)
             if ev is not None:
                 ev[2].record(stream)
             pa.pa_reduce(out, tmp, es, ml, sl, PS)
@@ -703,7 +708,8 @@ def main():
     unique_bytes = (inp.unique_kv_bytes if w.group_size else inp.kv_bytes) * esz // 2
     value = kv_bytes / (ms_per_step / 1e3) / 1e9
     achieved = unique_bytes / dec_avg_s / 1e9
-    kname = "pa_decode_v2" if args.kernel == "v2" else "pa_decode_v1"
+    kname = ("pa_decode_v2_shared" if shared else "pa_decode_v2") if args.kernel == "v2" \
+        else "pa_decode_v1"
     names = ["reshape_and_cache", kname] + (["pa_reduce"] if args.kernel == "v2" else [])
     traffic = read_traffic(kname, args.workload + ("_fp8" if fp8 else ""))
 

@@ -159,6 +159,34 @@ PA_API int pa_decode_v2(float* tmp_out, float* exp_sums, float* max_logits,
                  int kv_cache_dtype, float k_scale, float v_scale, void* stream);
 
 /*
+ * pa_decode_v2_shared -- pa_decode_v2 for batches whose sequences share K/V
+ * blocks ("vLLM 的 PagedAttention：KV cache 为什么要分页", §4.2: parallel
+ * sampling and beam search point several sequences' block tables at the same
+ * physical blocks, and copy-on-write gives each its own copy of a partly
+ * filled block it writes).  Same
+ * arguments and outputs as pa_decode_v2, for any batch.
+ *
+ * With G = num_heads / num_kv_heads in {2, 4, 8} and partition_size <= 1024,
+ * aligned sets of 16/G sequences are taken together: the sequences of a set
+ * whose token range in a partition and block-table entries over it equal the
+ * set's first sequence's (the partition's last entry may differ) are computed
+ * in one walk of the shared blocks, split over two waves, each sequence's
+ * own last block folded into its own rows; every other sequence alone, with
+ * the same two-wave split.  A sequence's results are bit for bit the same
+ * whether its blocks are shared or private copies.  Other G or partition
+ * sizes: exactly pa_decode_v2.  On batches that share nothing it is correct
+ * but slower than pa_decode_v2 when the lengths in a set differ (a set's
+ * sequences run one after another in one workgroup).
+ */
+PA_API int pa_decode_v2_shared(float* tmp_out, float* exp_sums, float* max_logits,
+                 const void* q, const void* k_cache, const void* v_cache,
+                 const int32_t* block_tables, const int32_t* seq_lens,
+                 int num_seqs, int num_heads, int num_kv_heads, int head_size,
+                 int block_size, int max_blocks_per_seq, int num_blocks,
+                 int max_num_partitions, int partition_size, float scale,
+                 int kv_cache_dtype, float k_scale, float v_scale, void* stream);
+
+/*
  * pa_reduce -- v2 second pass: log-sum-exp merge of the partials (the pages
  * say only "merged afterwards"; this is the exact merge).
  *

@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     pa_abi_version,
     pa_decode_v1,
     pa_decode_v2,
+    pa_decode_v2_shared,
     pa_decode_v2_noalloc,
     pa_prefill,
     pa_gather_kv,

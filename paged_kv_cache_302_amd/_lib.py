@@ -31,6 +31,8 @@ _SIGNATURES = {
     "pa_decode_v1": ([_ptr] * 6 + [_c_int] * 7 + [_c_float, _c_int, _c_float, _c_float, _ptr], _c_int),
     "pa_v2_max_partitions": ([_c_int, _c_int], _c_int),
     "pa_decode_v2": ([_ptr] * 8 + [_c_int] * 9 + [_c_float, _c_int, _c_float, _c_float, _ptr], _c_int),
+    "pa_decode_v2_shared": ([_ptr] * 8 + [_c_int] * 9 + [_c_float, _c_int, _c_float, _c_float, _ptr],
+                            _c_int),
     "pa_reduce": ([_ptr] * 5 + [_c_int] * 5 + [_ptr], _c_int),
     "pa_decode_v2_noalloc": ([_ptr] * 6 + [_c_int] * 9 + [_c_float, _c_int, _c_float, _c_float, _ptr],
                              _c_int),
@@ -181,8 +183,10 @@ def pa_decode_v1(out, q, k_cache, v_cache, block_tables, seq_lens, scale: float,
 
 def pa_decode_v2(tmp_out, exp_sums, max_logits, q, k_cache, v_cache, block_tables, seq_lens,
                  scale: float, partition_size: int, k_scale: float = 1.0, v_scale: float = 1.0,
-                 stream=None):
-    """Per-partition partials (tmp_out[S,P,H,D], exp_sums/max_logits[S,P,H])."""
+                 stream=None, shared_blocks: bool = False):
+    """Per-partition partials (tmp_out[S,P,H,D], exp_sums/max_logits[S,P,H]).
+    shared_blocks=True calls pa_decode_v2_shared (same results, for batches
+    whose block tables share physical blocks)."""
     S, H, KVH, D, B, NB, MB = _decode_common(q, k_cache, v_cache, block_tables, seq_lens)
     _want(tmp_out, "tmp_out", torch.float32, 4, q.device)
     _want(exp_sums, "exp_sums", torch.float32, 3, q.device)
@@ -192,11 +196,20 @@ def pa_decode_v2(tmp_out, exp_sums, max_logits, q, k_cache, v_cache, block_table
             tuple(max_logits.shape) != (S, P, H):
         raise ValueError("v2 scratch shapes must be [S,P,H,D] and [S,P,H]")
     lib = load_library()
-    rc = lib.pa_decode_v2(_p(tmp_out), _p(exp_sums), _p(max_logits), _p(q), _p(k_cache),
-                          _p(v_cache), _p(block_tables), _p(seq_lens), S, H, KVH, D, B, MB, NB,
-                          P, int(partition_size), float(scale), kv_dtype_of(k_cache),
-                          float(k_scale), float(v_scale), _stream(q, stream))
-    _check(rc, "pa_decode_v2")
+    name = "pa_decode_v2_shared" if shared_blocks else "pa_decode_v2"
+    rc = getattr(lib, name)(_p(tmp_out), _p(exp_sums), _p(max_logits), _p(q), _p(k_cache),
+                            _p(v_cache), _p(block_tables), _p(seq_lens), S, H, KVH, D, B, MB, NB,
+                            P, int(partition_size), float(scale), kv_dtype_of(k_cache),
+                            float(k_scale), float(v_scale), _stream(q, stream))
+    _check(rc, name)
+
+
+def pa_decode_v2_shared(tmp_out, exp_sums, max_logits, q, k_cache, v_cache, block_tables,
+                        seq_lens, scale: float, partition_size: int, k_scale: float = 1.0,
+                        v_scale: float = 1.0, stream=None):
+    """pa_decode_v2 for batches whose sequences share K/V blocks (include/pa.h)."""
+    pa_decode_v2(tmp_out, exp_sums, max_logits, q, k_cache, v_cache, block_tables, seq_lens,
+                 scale, partition_size, k_scale, v_scale, stream, shared_blocks=True)
 
 
 def pa_decode_v2_noalloc(out, q, k_cache, v_cache, block_tables, seq_lens, scale: float,
@@ -323,14 +336,14 @@ def v2_scratch(num_seqs: int, num_heads: int, head_size: int, max_num_partitions
 
 def paged_attention_v2(q, k_cache, v_cache, block_tables, seq_lens, scale: float,
                        partition_size: int = 512, max_seq_len: Optional[int] = None,
-                       k_scale: float = 1.0, v_scale: float = 1.0):
+                       k_scale: float = 1.0, v_scale: float = 1.0, shared_blocks: bool = False):
     S, H, D = q.shape
     if max_seq_len is None:
         max_seq_len = block_tables.shape[1] * k_cache.shape[3]
     P = pa_v2_max_partitions(max_seq_len, partition_size)
     tmp, es, ml = v2_scratch(S, H, D, P, q.device)
     pa_decode_v2(tmp, es, ml, q, k_cache, v_cache, block_tables, seq_lens, scale, partition_size,
-                 k_scale, v_scale)
+                 k_scale, v_scale, shared_blocks=shared_blocks)
     out = torch.empty((S, H, D), dtype=torch.float32, device=q.device)
     return pa_reduce(out, tmp, es, ml, seq_lens, partition_size)
 

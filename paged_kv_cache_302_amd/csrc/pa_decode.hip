@@ -1,4 +1,5 @@
-// Paged decode attention for gfx950 (MI355X): pa_decode_v1 and pa_decode_v2.
+// Paged decode attention for gfx950 (MI355X): pa_decode_v1, pa_decode_v2 and
+// pa_decode_v2_shared.
 //
 // What is computed (page "读 vLLM 的 PagedAttention kernel", §2 flowchart,
 // §3.3 and §3.4): for one query token per sequence, walk the sequence's block
@@ -21,6 +22,12 @@
 // sum over seq_lens inside each workgroup), so the grid is dense in real
 // work and the round-robin placement of workgroups on the eight XCDs stays
 // balanced.
+//
+// pa_decode_v2_shared serves batches whose block tables share physical
+// blocks (parallel samples, forks; page "vLLM 的 PagedAttention：KV cache
+// 为什么要分页", §4.2): with G = 2, 4 or 8 one workgroup takes an aligned set of 16/G
+// sequences for one (partition, KV head), and the members that read the same
+// blocks over the partition are walked once (the set kernel below).
 //
 // Two inner paths:
 //  * MFMA (G = H/KVH >= 2).  Scores S^T[t][h] = K[t][:] . Q[h][:] are one
@@ -649,7 +656,7 @@ void pa_decode_kernel(DecodeParams p) {
 }
 
 // --------------------------------------------------------------------------
-// Set kernel (v2, MFMA path, G = 2, 4 or 8, more than 64 sequences, PS <= 1024).
+// Set kernel (pa_decode_v2_shared; MFMA path, G = 2, 4 or 8, PS <= 1024).
 // One workgroup per (aligned set of M = 16/G sequences, partition, KV head):
 // a score tile has 16 query rows and one KV group fills G of them, so the
 // set's M groups fill the tile.  The set's members fall into classes: the
@@ -1089,12 +1096,13 @@ extern "C" int pa_v2_max_partitions(int max_seq_len, int partition_size) {
     return (max_seq_len - 1) / partition_size + 1;
 }
 
-extern "C" int pa_decode_v2(float* tmp_out, float* exp_sums, float* max_logits, const void* q,
-                            const void* k_cache, const void* v_cache, const int32_t* block_tables,
-                            const int32_t* seq_lens, int num_seqs, int num_heads, int num_kv_heads,
-                            int head_size, int block_size, int max_blocks_per_seq, int num_blocks,
-                            int max_num_partitions, int partition_size, float scale,
-                            int kv_cache_dtype, float k_scale, float v_scale, void* stream) {
+// pa_decode_v2 and pa_decode_v2_shared: the set kernel only for the latter.
+static int decode_v2(bool sets, float* tmp_out, float* exp_sums, float* max_logits, const void* q,
+                     const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                     const int32_t* seq_lens, int num_seqs, int num_heads, int num_kv_heads,
+                     int head_size, int block_size, int max_blocks_per_seq, int num_blocks,
+                     int max_num_partitions, int partition_size, float scale, int kv_cache_dtype,
+                     float k_scale, float v_scale, void* stream) {
     int rc = check_decode_args(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_heads,
                                num_kv_heads, head_size, block_size, max_blocks_per_seq, num_blocks,
                                scale, kv_cache_dtype, k_scale, v_scale);
@@ -1114,13 +1122,14 @@ extern "C" int pa_decode_v2(float* tmp_out, float* exp_sums, float* max_logits, 
     p.max_num_partitions = max_num_partitions;
     p.partition_size = partition_size;
     const bool fp8 = kv_cache_dtype == PA_KV_FP8_E4M3;
-    // Larger batches of GQA groups that fill a score tile evenly go to the set
-    // kernel: one workgroup per (set of 16/G sequences, partition, KV head).
-    if (PA_SET_WAVES > 0 && !PA_V2_WAVES && num_seqs > 64 && p.group >= 2 && p.group <= kMaxMembers &&
-        16 % p.group == 0 && partition_size <= 64 * kBlock) {
+    // Batches declared to share blocks, with GQA groups that fill a score
+    // tile evenly, go to the set kernel: one workgroup per (set of 16/G
+    // sequences, partition, KV head).
+    if (sets && PA_SET_WAVES > 0 && p.group >= 2 && p.group <= kMaxMembers && 16 % p.group == 0 &&
+        partition_size <= 64 * kBlock) {
         const int M = 16 / p.group;
-        const long long sets = (num_seqs + M - 1) / M;
-        const long long grid = sets * max_num_partitions * num_kv_heads;
+        const long long sets_n = (num_seqs + M - 1) / M;
+        const long long grid = sets_n * max_num_partitions * num_kv_heads;
         if (grid > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
         hipStream_t st = as_stream(stream);
         if (fp8)
@@ -1139,4 +1148,29 @@ extern "C" int pa_decode_v2(float* tmp_out, float* exp_sums, float* max_logits, 
     const int nw = PA_V2_WAVES ? PA_V2_WAVES
                                : pick_waves(units / 2, partition_size / 16, head_size, fp8 ? 1 : 2);
     return launch_decode<true>(p, head_size, fp8, nw, (int)grid, as_stream(stream));
+}
+
+extern "C" int pa_decode_v2(float* tmp_out, float* exp_sums, float* max_logits, const void* q,
+                            const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                            const int32_t* seq_lens, int num_seqs, int num_heads, int num_kv_heads,
+                            int head_size, int block_size, int max_blocks_per_seq, int num_blocks,
+                            int max_num_partitions, int partition_size, float scale,
+                            int kv_cache_dtype, float k_scale, float v_scale, void* stream) {
+    return decode_v2(false, tmp_out, exp_sums, max_logits, q, k_cache, v_cache, block_tables, seq_lens,
+                     num_seqs, num_heads, num_kv_heads, head_size, block_size, max_blocks_per_seq,
+                     num_blocks, max_num_partitions, partition_size, scale, kv_cache_dtype, k_scale,
+                     v_scale, stream);
+}
+
+extern "C" int pa_decode_v2_shared(float* tmp_out, float* exp_sums, float* max_logits, const void* q,
+                                   const void* k_cache, const void* v_cache,
+                                   const int32_t* block_tables, const int32_t* seq_lens, int num_seqs,
+                                   int num_heads, int num_kv_heads, int head_size, int block_size,
+                                   int max_blocks_per_seq, int num_blocks, int max_num_partitions,
+                                   int partition_size, float scale, int kv_cache_dtype,
+                                   float k_scale, float v_scale, void* stream) {
+    return decode_v2(true, tmp_out, exp_sums, max_logits, q, k_cache, v_cache, block_tables, seq_lens,
+                     num_seqs, num_heads, num_kv_heads, head_size, block_size, max_blocks_per_seq,
+                     num_blocks, max_num_partitions, partition_size, scale, kv_cache_dtype, k_scale,
+                     v_scale, stream);
 }

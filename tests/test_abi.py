@@ -39,7 +39,7 @@ def arg_ctype(arg):
 
 def test_header_lists_the_entry_points():
     names = set(header_decls())
-    assert {"pa_decode_v1", "pa_decode_v2", "pa_reduce", "reshape_and_cache", "pa_gather_kv",
+    assert {"pa_decode_v1", "pa_decode_v2", "pa_decode_v2_shared", "pa_reduce", "reshape_and_cache", "pa_gather_kv",
             "pa_v2_max_partitions", "pa_status_str", "pa_abi_version", "copy_blocks",
             "pa_bm_create", "pa_bm_append_slots"} <= names
     assert names == set(_lib.exported_symbols())
@@ -116,6 +116,9 @@ def test_v2_and_reduce_reject_bad_partitioning():
                             None) == -1
     assert lib.pa_decode_v2(A, A, A, A, A, A, A, A, 2, 8, 2, 128, 16, 4, 10, 2, 512, 0.1, 1, -1.0, 1.0,
                             None) == -1
+    shared = lib.pa_decode_v2_shared
+    assert shared(A, A, A, A, A, A, A, A, 2, 8, 2, 128, 16, 4, 10, 2, 100, 0.1, 0, 1.0, 1.0, None) == -1
+    assert shared(A, A, A, A, A, A, A, A, 2, 8, 2, 128, 16, 4, 10, 2, 512, 0.1, 1, -1.0, 1.0, None) == -1
     assert lib.pa_reduce(A, A, A, A, A, 2, 8, 128, 0, 512, None) == -1
     assert lib.pa_reduce(A, A, A, A, A, 2, 8, 100, 4, 512, None) == -2
     assert lib.pa_reduce(A, M, A, A, A, 2, 8, 128, 4, 512, None) == -3

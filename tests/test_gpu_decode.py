@@ -37,18 +37,17 @@ REDUCE_CASES = [
 # leave the partly filled ones unsorted, 1,200 sequences x 8 partitions
 # exceed what the device holds (plain order), and 64 sequences x 8 KV heads x
 # up to 16 partitions exceed it with no shared blocks (XCD-major order).
-# Beyond 64 sequences these take G = 7: G = 2, 4, 8 go to the set kernel.
 ORDER_CASES = [
     ("order_200seqs", 200, 14, 2, 64, 1, 700, 128),
     ("order_ps2048", 3, 8, 2, 128, 1, 5000, 2048),
     ("order_big_grid", 1200, 14, 2, 64, 1, 1000, 128),
     ("order_xcd_major", 64, 32, 8, 128, 1, 1024, 64),
 ]
-# the set kernel (v2, more than 64 sequences, G = 2, 4, 8, PS <= 1024): sets of
-# 16/G sequences, the last one cut short by the batch (70 = 8 x 8 + 6,
-# 67 = 2 x 33 + 1); 64-block partitions (every entry of the class check's
-# table window used); one-block partitions, where most waves walk nothing;
-# a grid far beyond what the device holds
+# the set kernel (pa_decode_v2_shared with G = 2, 4, 8 and PS <= 1024): sets
+# of 16/G sequences, the last one cut short by the batch (70 = 8 x 8 + 6,
+# 67 = 2 x 33 + 1); 64-block partitions (every lane of the class check used);
+# one-block partitions, where most waves walk nothing; a grid far beyond what
+# the device holds.  Through pa_decode_v2 they take the per-sequence kernel.
 SET_CASES = [
     ("set_g4_d128", 72, 8, 2, 128, 1, 700, 128),
     ("set_g2_d64", 70, 4, 2, 64, 1, 500, 64),
@@ -77,7 +76,7 @@ def run_v1(inp):
     return out.cpu().numpy()
 
 
-def run_v2(inp, ps, max_seq_len=None):
+def run_v2(inp, ps, max_seq_len=None, shared=False):
     d = dev_inputs(inp)
     S, H, D = inp.q.shape
     msl = max_seq_len or inp.workload.max_seq_len
@@ -86,7 +85,7 @@ def run_v2(inp, ps, max_seq_len=None):
     for t in (tmp, es, ml):
         t.fill_(float("nan"))
     pa.pa_decode_v2(tmp, es, ml, d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
-                    d["seq_lens"], inp.scale, ps)
+                    d["seq_lens"], inp.scale, ps, shared_blocks=shared)
     out = torch.full((S, H, D), float("nan"), dtype=torch.float32, device=device())
     pa.pa_reduce(out, tmp, es, ml, d["seq_lens"], ps)
     # partials come back [S,P,H,...]; return them [S,H,P,...] like the oracle
@@ -115,18 +114,34 @@ def test_v1_matches_oracle(case):
 @pytest.mark.parametrize("case", CASES + REDUCE_CASES + ORDER_CASES + SET_CASES,
                          ids=[c[0] for c in CASES + REDUCE_CASES + ORDER_CASES + SET_CASES])
 def test_v2_partials_and_merge_match_oracle(case):
-    inp = make_case(case, 3)
-    ps = case[7]
-    out, tmp, es, ml, P = run_v2(inp, ps)
+    check_v2_against_oracle(make_case(case, 3), case[7], case[0], False)
+
+
+# pa_decode_v2_shared on batches that share nothing: the set kernel's cases,
+# batches of a few sequences (one set cut short), and shapes it leaves to the
+# per-sequence kernel (G = 1, 7, 16, 24; PS = 2048)
+SHARED_ENTRY_CASES = SET_CASES + [c for c in CASES if c[0] in (
+    "g2_d128", "g8_d64", "mha_d128", "g7_d128", "g16_d128", "g24_d128")] \
+    + [c for c in ORDER_CASES if c[0] == "order_ps2048"] \
+    + [("set_g8_8seqs", 8, 16, 2, 128, 1, 3000, 512), ("set_g2_64seqs", 64, 16, 8, 64, 1, 900, 256)]
+
+
+@pytest.mark.parametrize("case", SHARED_ENTRY_CASES, ids=[c[0] for c in SHARED_ENTRY_CASES])
+def test_v2_shared_entry_matches_oracle(case):
+    check_v2_against_oracle(make_case(case, 3), case[7], case[0] + " shared entry", True)
+
+
+def check_v2_against_oracle(inp, ps, label, shared):
+    out, tmp, es, ml, P = run_v2(inp, ps, shared=shared)
     t_ref, e_ref, m_ref = oracle.partition_partials(inp.q, inp.k_cache, inp.v_cache,
                                                     inp.block_tables, inp.seq_lens, inp.scale, 16,
                                                     ps, P)
     valid = ~np.isnan(e_ref)                     # partitions that exist
     assert np.isnan(es[~valid]).all(), "v2 wrote a partition past the sequence"
-    assert_parity(tmp[valid], t_ref[valid], case[0] + " o_p")
+    assert_parity(tmp[valid], t_ref[valid], label + " o_p")
     np.testing.assert_allclose(ml[valid], m_ref[valid], rtol=1e-5, atol=1e-5)
     np.testing.assert_allclose(es[valid], e_ref[valid], rtol=2e-5)
-    assert_parity(out, ref_out(inp), case[0] + " v2+reduce")
+    assert_parity(out, ref_out(inp), label + " v2+reduce")
 
 
 @pytest.mark.parametrize("case", CASES[:5] + REDUCE_CASES, ids=[c[0] for c in CASES[:5] + REDUCE_CASES])
@@ -363,6 +378,7 @@ def test_partitions_shared_by_sequences_match_private_copies(G, LEN, PS):
     oracle.poison_unused(shared.k_cache, shared.v_cache, shared.block_tables, shared.seq_lens, 16)
 
     assert_shared_equals_private(shared, PS, f"shared G={G}")
+    assert_shared_equals_private(shared, PS, f"shared G={G}, shared entry", True)
 
 
 def private_copies(inp):
@@ -380,9 +396,9 @@ def private_copies(inp):
     return wl.DecodeInputs(inp.workload, inp.seed, L, bt2, kc.shape[0], inp.q, kc, vc)
 
 
-def assert_shared_equals_private(shared, PS, label):
-    out_s, tmp_s, es_s, ml_s, P = run_v2(shared, PS)
-    out_p, tmp_p, es_p, ml_p, _ = run_v2(private_copies(shared), PS)
+def assert_shared_equals_private(shared, PS, label, entry=False):
+    out_s, tmp_s, es_s, ml_s, P = run_v2(shared, PS, shared=entry)
+    out_p, tmp_p, es_p, ml_p, _ = run_v2(private_copies(shared), PS, shared=entry)
     valid = ~np.isnan(es_p)
     assert np.array_equal(tmp_s[valid], tmp_p[valid])
     assert np.array_equal(es_s[valid], es_p[valid]) and np.array_equal(ml_s[valid], ml_p[valid])
@@ -393,7 +409,7 @@ def assert_shared_equals_private(shared, PS, label):
 
 @pytest.mark.parametrize("G,PS", [(2, 128), (4, 64), (4, 512), (8, 256)])
 def test_set_kernel_shared_partitions_match_private_copies(G, PS):
-    """The set kernel (more than 64 sequences, sets of M = 16/G): sequences
+    """The set kernel (pa_decode_v2_shared, sets of M = 16/G): sequences
     that read the same blocks equal, bit for bit, the same sequences reading
     private copies, and the oracle.  Covered: a whole set that shares; a set
     whose second member differs in one block; a member with a shorter range in
@@ -421,7 +437,7 @@ def test_set_kernel_shared_partitions_match_private_copies(G, PS):
     bt[M + 1, 2] = inp.block_tables[M + 1, 2]   # ... but set 1's second member differs in one block
     shared = wl.DecodeInputs(w, inp.seed, L, bt, inp.num_blocks, inp.q, inp.k_cache, inp.v_cache)
     oracle.poison_unused(shared.k_cache, shared.v_cache, shared.block_tables, shared.seq_lens, 16)
-    assert_shared_equals_private(shared, PS, f"set kernel G={G} PS={PS}")
+    assert_shared_equals_private(shared, PS, f"set kernel G={G} PS={PS}", True)
 
 
 def test_set_kernel_edge_cases():
@@ -446,7 +462,7 @@ def test_set_kernel_edge_cases():
     bt[17:20, :18] = bt[16, :18]
     oracle.poison_unused(inp.k_cache, inp.v_cache, bt, L, 16)
     ref = ref_out(inp)
-    out = run_v2(inp, PS)[0]
+    out = run_v2(inp, PS, shared=True)[0]
     assert (out[5] == 0).all()
     b = bt[6, 0]
     assert np.array_equal(out[6], inp.v_cache[b, np.arange(H) // (H // KVH), :, 0].astype(np.float32))
@@ -459,7 +475,8 @@ def test_set_kernel_edge_cases():
     bt_bad[8:12, 3] = NB + 2
     bt_bad[18, 18] = NB + 2
     o = pa.paged_attention_v2(to_dev(inp.q), to_dev(kc)[:NB], to_dev(vc)[:NB], to_dev(bt_bad),
-                              to_dev(L), inp.scale, PS, w.max_seq_len).cpu().numpy()
+                              to_dev(L), inp.scale, PS, w.max_seq_len,
+                              shared_blocks=True).cpu().numpy()
     assert np.isnan(o[8:12]).all() and np.isnan(o[18]).all()
     ok = np.ones(S, dtype=bool)
     ok[8:12] = False

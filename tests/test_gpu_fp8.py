@@ -164,12 +164,13 @@ def test_fp8_write_then_decode_pipeline():
     assert_parity(out, ref, "fp8 write + decode")
 
 
-@pytest.mark.parametrize("S", [8, 72], ids=["units", "set_kernel"])
-def test_fp8_partitions_shared_by_sequences_match_private_copies(S):
+@pytest.mark.parametrize("S,entry", [(8, False), (8, True), (72, True)],
+                         ids=["units", "set_kernel_8", "set_kernel_72"])
+def test_fp8_partitions_shared_by_sequences_match_private_copies(S, entry):
     """fp8 pools: v2 units of sequences that read the same blocks over a
     partition (one tile for the aligned set of four, G = 4) equal, bit for bit,
     the same sequences reading private copies of the codes, and the oracle over
-    the decoded values; with 72 sequences the set kernel runs."""
+    the decoded values; through pa_decode_v2_shared the set kernel runs."""
     KVH, G, D, PS = 2, 4, 128, 128
     inp, k8, v8, ks, vs = fp8_case("share8", S, G * KVH, KVH, D, 400, 400, seed=33)
     nb = -(-400 // 16)
@@ -190,7 +191,7 @@ def test_fp8_partitions_shared_by_sequences_match_private_copies(S):
         P = pa.pa_v2_max_partitions(400, PS)
         tmp, es, ml = pa.v2_scratch(S, G * KVH, D, P, device())
         pa.pa_decode_v2(tmp, es, ml, to_dev(inp.q), to_dev(kc8), to_dev(vc8), to_dev(table),
-                        to_dev(L), inp.scale, PS, ks, vs)
+                        to_dev(L), inp.scale, PS, ks, vs, shared_blocks=entry)
         out = torch.empty((S, G * KVH, D), dtype=torch.float32, device=device())
         pa.pa_reduce(out, tmp, es, ml, to_dev(L), PS)
         return tmp.cpu().numpy(), es.cpu().numpy(), ml.cpu().numpy(), out.cpu().numpy()
@@ -203,12 +204,12 @@ def test_fp8_partitions_shared_by_sequences_match_private_copies(S):
     assert_parity(shared[3], ref, "fp8 shared")
 
 
-def fp8_decode_both(inp, k8, v8, ks, vs, ps):
+def fp8_decode_both(inp, k8, v8, ks, vs, ps, shared=False):
     q, bt, sl = to_dev(inp.q), to_dev(inp.block_tables), to_dev(inp.seq_lens)
     kc, vc = to_dev(k8), to_dev(v8)
     out1 = pa.paged_attention_v1(q, kc, vc, bt, sl, inp.scale, ks, vs).cpu().numpy()
     out2 = pa.paged_attention_v2(q, kc, vc, bt, sl, inp.scale, ps, inp.workload.max_seq_len,
-                                 ks, vs).cpu().numpy()
+                                 ks, vs, shared_blocks=shared).cpu().numpy()
     return out1, out2
 
 
@@ -233,9 +234,9 @@ def test_fp8_long_unit_crosses_table_windows(H, D, L):
 # v2 unit orders on fp8 pools: 64 sequences x 8 KV heads x up to 16
 # partitions is more than the device holds at once and shares no blocks (the
 # XCD-major order); 1,200 sequences exceed it with the plain order; 200
-# sequences fit (largest-first order over four lookup chunks).  Beyond 64
-# sequences G = 7 keeps these on the one-unit-per-sequence kernel; with G = 4
-# and 8 they take the set kernel.
+# sequences fit (largest-first order over four lookup chunks).  The set_
+# cases go through pa_decode_v2_shared, which takes the set kernel for G = 4
+# and 8.
 FP8_ORDER_CASES = [
     ("xcd_major", 64, 32, 8, 128, 1, 1024, 64),
     ("big_grid", 1200, 14, 2, 64, 1, 1000, 128),
@@ -251,6 +252,6 @@ def test_fp8_v2_unit_orders(case):
     inp, k8, v8, ks, vs = fp8_case(label, S, H, KVH, D, lo, hi, seed=34)
     dk, dv = fp8.dequantize_pools(k8, v8, ks, vs)
     ref = oracle.paged_decode(inp.q, dk, dv, inp.block_tables, inp.seq_lens, inp.scale, 16)
-    out1, out2 = fp8_decode_both(inp, k8, v8, ks, vs, ps)
+    out1, out2 = fp8_decode_both(inp, k8, v8, ks, vs, ps, label.startswith("set_"))
     assert_parity(out2, ref, label + " fp8 v2")
     assert_parity(out1, ref, label + " fp8 v1")
