@@ -1,7 +1,7 @@
 """GPU tests of copy-on-write: copy_blocks bit-exact against the oracle, and
 parallel sampling end to end -- the native block manager hands out the
 slots, tables and copies, copy_blocks and reshape_and_cache update the
-pools, and pa_decode_v1 / pa_decode_v2 + pa_reduce must give, for every
+pools, and pa_decode_v1 / pa_decode_v2 (and _shared) + pa_reduce must give, for every
 sample, the dense attention over that sample's own token history (its
 prompt plus its own generated tokens), which the oracle computes on
 contiguous arrays.  Sharing and copy-on-write change where K/V live, never
@@ -98,3 +98,6 @@ def test_parallel_sampling_decode_matches_dense_histories(prompts, samples, step
     assert_parity(out1, want, "v1 after fork / copy-on-write")
     out2 = pa.paged_attention_v2(dq, kc, vc, dt, dl, scale, 64, int(lens.max())).cpu().numpy()
     assert_parity(out2, want, "v2 after fork / copy-on-write")
+    out3 = pa.paged_attention_v2(dq, kc, vc, dt, dl, scale, 64, int(lens.max()),
+                                 shared_blocks=True).cpu().numpy()
+    assert_parity(out3, want, "v2 shared after fork / copy-on-write")

@@ -61,9 +61,11 @@ class Step:
     def run(self, kernel):
         ks, vs = getattr(self, "ks", 1.0), getattr(self, "vs", 1.0)
         pa.reshape_and_cache(self.key, self.val, self.kc, self.vc, self.slot_d, ks, vs)
-        if kernel == "v2":
+        if kernel in ("v2", "v2s"):
+            # v2s: pa_decode_v2_shared, as bench.py runs the workloads that share blocks
             pa.pa_decode_v2(self.tmp, self.es, self.ml, self.q, self.kc, self.vc, self.bt, self.sl,
-                            self.inp.scale, self.w.partition_size, ks, vs)
+                            self.inp.scale, self.w.partition_size, ks, vs,
+                            shared_blocks=kernel == "v2s")
             pa.pa_reduce(self.out, self.tmp, self.es, self.ml, self.sl, self.w.partition_size)
         else:
             pa.pa_decode_v1(self.out, self.q, self.kc, self.vc, self.bt, self.sl, self.inp.scale,
@@ -90,7 +92,7 @@ def sample_heads(w, seq_lens, n_seq=4, seed=0):
 
 @pytest.mark.parametrize("name,kernel", [
     ("gqa7b", "v1"), ("gqa7b", "v2"), ("mha7b", "v1"), ("mha7b", "v2"),
-    ("long_gqa", "v2"), ("shared_prefix", "v2"),
+    ("long_gqa", "v2"), ("shared_prefix", "v2"), ("shared_prefix", "v2s"),
 ])
 def test_full_workload_step_sampled_parity(name, kernel):
     w = wl.WORKLOADS[name]
@@ -130,6 +132,7 @@ def fp8_reference(inp, pairs, ks, vs):
 
 @pytest.mark.parametrize("name,kernel", [
     ("long_gqa", "v2"), ("gqa7b", "v1"), ("gqa7b", "v2"), ("mha7b", "v1"), ("shared_prefix", "v2"),
+    ("shared_prefix", "v2s"),
 ])
 def test_full_workload_fp8_step_sampled_parity(name, kernel):
     """The fp8 bench lines' shapes and launch configurations (k_scale = v_scale
@@ -151,13 +154,15 @@ def test_full_workload_fp8_step_sampled_parity(name, kernel):
     assert_parity(out[idx], ref[idx], f"{name} fp8 {kernel}")
 
 
-def test_shared_prefix_equals_private_copies_bit_exact():
+@pytest.mark.parametrize("kernel", ["v2", "v2s"])
+def test_shared_prefix_equals_private_copies_bit_exact(kernel):
     """Sequences that share their prefix blocks (one physical copy, referenced
     by every table of the group) give bit-identical outputs to the same
-    sequences with the prefix copied into private blocks."""
+    sequences with the prefix copied into private blocks, through
+    pa_decode_v2 and pa_decode_v2_shared."""
     w = wl.WORKLOADS["shared_prefix"]
     inp = wl.make_inputs(w, 5)
-    shared = Step(inp).run("v2")
+    shared = Step(inp).run(kernel)
     B = w.block_size
     pre = w.prefix_len // B
     NB = inp.num_blocks
@@ -178,7 +183,7 @@ def test_shared_prefix_equals_private_copies_bit_exact():
     assert nxt == kc.shape[0]
     priv = wl.DecodeInputs(w, inp.seed, inp.seq_lens, bt, kc.shape[0], inp.q, kc, vc,
                            key=inp.key, value=inp.value, new_pos=inp.new_pos)
-    private = Step(priv).run("v2")
+    private = Step(priv).run(kernel)
     assert np.array_equal(shared, private)
 
 
