@@ -82,6 +82,27 @@
 
 namespace pa {
 
+// Stores of the results.  The v2 statistics (max_logits, exp_sums) are
+// plain cached stores: a 128-byte line of [S][P][H] is written in 16-byte
+// pieces by the KV heads' units of one partition (as nontemporal stores
+// they cost the decodes 0.5-3%).  Result rows are nontemporal stores when
+// the grid is larger than the device holds at once (cached, the long-context
+// decode's 28 MB of rows cost it 4%) and cached stores when the whole grid
+// is resident (1-3% faster on the short decodes).
+__device__ __forceinline__ void st_stat(float* p, float v) { *p = v; }
+template <class T>
+__device__ __forceinline__ void st_row(T* p, T v, bool cached) {
+    if (cached) {
+        *p = v;
+    } else {
+        // (the empty statements keep the compiler from hoisting or sinking
+        // the two stores into one plain store, which drops the hint)
+        asm volatile("" ::: "memory");
+        st_stream(p, v);
+        asm volatile("" ::: "memory");
+    }
+}
+
 // --------------------------------------------------------------------------
 // v2 unit order.  The existing partitions (p < ceil(L_s / PS), capped at
 // max_num_partitions) are numbered largest first: every full partition in
@@ -599,15 +620,15 @@ void pa_decode_kernel(DecodeParams p) {
                 const float inv = empty ? 0.f : p.v_scale / s_l[i];
                 f32x4 v = src[e] * inv;
                 if (bad) v = f32x4{NAN, NAN, NAN, NAN};
-                st_stream(reinterpret_cast<f32x4*>(p.out + out_row(i) * D) + (e - i * (D / 4)), v);
+                st_row(reinterpret_cast<f32x4*>(p.out + out_row(i) * D) + (e - i * (D / 4)), v, p.resident > 0);
             }
         }
         if constexpr (V2) {
             // lane l < nrows holds tile row l's max and total weight on both paths
             const int l = lane_id();
             if (l < nrows && live(l)) {
-                st_stream(p.max_logits + out_row(l), bad ? NAN : st.m * p.scale);
-                st_stream(p.exp_sums + out_row(l), bad ? NAN : ltot);
+                st_stat(p.max_logits + out_row(l), bad ? NAN : st.m * p.scale);
+                st_stat(p.exp_sums + out_row(l), bad ? NAN : ltot);
             }
         }
         return;
@@ -638,7 +659,7 @@ void pa_decode_kernel(DecodeParams p) {
                 den += s_l[v * HP + j] * f;
             }
             const float o = empty ? 0.f : num / den * p.v_scale;
-            st_stream(out_h0 + (size_t)j * out_head_stride + d, any_bad ? NAN : o);
+            st_row(out_h0 + (size_t)j * out_head_stride + d, any_bad ? NAN : o, p.resident > 0);
             if (V2 && d == 0) {
                 s_fin[j] = M;
                 s_fin[16 + j] = den;
@@ -648,8 +669,8 @@ void pa_decode_kernel(DecodeParams p) {
             __syncthreads();
             const int t = threadIdx.x;
             if (t < nh) {
-                st_stream(p.max_logits + row0 + t, any_bad ? NAN : s_fin[t] * p.scale);
-                st_stream(p.exp_sums + row0 + t, any_bad ? NAN : s_fin[16 + t]);
+                st_stat(p.max_logits + row0 + t, any_bad ? NAN : s_fin[t] * p.scale);
+                st_stat(p.exp_sums + row0 + t, any_bad ? NAN : s_fin[16 + t]);
             }
         }
     }
@@ -907,10 +928,10 @@ __global__ __launch_bounds__(64 * NW) void pa_decode_set_kernel(DecodeParams p) 
                 }
                 f32x4 o = num / den * p.v_scale;
                 if (any_bad) o = f32x4{NAN, NAN, NAN, NAN};
-                st_stream(reinterpret_cast<f32x4*>(p.out + (orow + j) * D) + d4, o);
+                st_row(reinterpret_cast<f32x4*>(p.out + (orow + j) * D) + d4, o, p.resident > 0);
                 if (d4 == 0) {
-                    st_stream(p.max_logits + orow + j, any_bad ? NAN : mx * p.scale);
-                    st_stream(p.exp_sums + orow + j, any_bad ? NAN : den);
+                    st_stat(p.max_logits + orow + j, any_bad ? NAN : mx * p.scale);
+                    st_stat(p.exp_sums + orow + j, any_bad ? NAN : den);
                 }
             }
         }
@@ -942,13 +963,14 @@ static int launch_nw(int NW, const DecodeParams& p0, int grid, int nh_max, hipSt
         case 8: fn = reinterpret_cast<const void*>(&pa_decode_kernel<Path, D, 8, V2>); break;
         default: return PA_ERR_INVALID_ARG;
     }
-    if (V2) {
+    {
         // Only when the whole grid is resident at once does the placement fix
-        // each CU's share: then the kernel takes the balanced unit order.
+        // each CU's share: then a v2 kernel takes the balanced unit order.
         // With more units the dispatcher balances the CUs itself as slots
         // free up, and the plain order keeps the units that share blocks
-        // (forks, samples of one prompt) running together.  The occupancy
-        // of each (wave count, LDS size) is asked for once.
+        // (forks, samples of one prompt) running together.  Residency also
+        // picks the result rows' store policy (v1 and v2).  The occupancy of
+        // each (wave count, LDS size) is asked for once.
         static std::atomic<long long> occ_cache[5];   // (lds << 8) | (workgroups per CU + 1)
         auto resident_slots = [&](const void* f, int threads, size_t lds_bytes, int slot) {
             long long c = occ_cache[slot].load(std::memory_order_relaxed);
@@ -1083,6 +1105,7 @@ extern "C" int pa_decode_v1(float* out, const void* q, const void* k_cache, cons
                                  num_kv_heads, max_blocks_per_seq, num_blocks, scale,
                                  kv_cache_dtype, k_scale, v_scale);
     p.out = out;
+    p.num_cus = compute_units(stream);   // residency (the row stores' policy)
     const long long units = (long long)num_seqs * num_kv_heads * p.head_chunks;
     if (units > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
     const bool fp8 = kv_cache_dtype == PA_KV_FP8_E4M3;

@@ -110,7 +110,7 @@ struct DecodeParams {
     int max_num_partitions;
     int unit_period;      // v2: compute units the unit order snakes over (1 = plain order)
     int num_cus;          // compute units of the device (0 = unknown)
-    int resident;         // v2: >0 when the device holds the whole grid at once
+    int resident;         // >0 when the device holds the whole grid at once
     int partition_size;   // tokens, multiple of 16 (v2)
     float scale;          // natural units (fp8: scale * k_scale)
     float scale_log2;     // scale * log2(e)
