@@ -1167,9 +1167,14 @@ static int decode_v2(bool sets, float* tmp_out, float* exp_sums, float* max_logi
     const long long units = (long long)num_seqs * num_kv_heads * p.head_chunks * max_num_partitions;
     const long long grid = (units + p.unit_period - 1) / p.unit_period * p.unit_period;
     if (grid > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
-    // a sequence has on average about half of max_num_partitions partitions
+    // A sequence has on average about half of max_num_partitions partitions.
+    // One-wave fp8 MFMA units walk their tiles through the LDS ring, and the
+    // wave count is picked as for fp16 tiles there (GQA-7B on fp8 pools: two
+    // waves per unit 36.8 us, one 35.3).
+    const bool fp8_ring = fp8 && p.group >= 2;
     const int nw = PA_V2_WAVES ? PA_V2_WAVES
-                               : pick_waves(units / 2, partition_size / 16, head_size, fp8 ? 1 : 2);
+                               : pick_waves(units / 2, partition_size / 16, head_size,
+                                            fp8 && !fp8_ring ? 1 : 2);
     return launch_decode<true>(p, head_size, fp8, nw, (int)grid, as_stream(stream));
 }
 
