@@ -163,8 +163,8 @@ PA_API int pa_decode_v2(float* tmp_out, float* exp_sums, float* max_logits,
  * blocks ("vLLM 的 PagedAttention：KV cache 为什么要分页", §4.2: parallel
  * sampling and beam search point several sequences' block tables at the same
  * physical blocks, and copy-on-write gives each its own copy of a partly
- * filled block it writes).  Same
- * arguments and outputs as pa_decode_v2, for any batch.
+ * filled block it writes).  Same arguments, outputs, validation and error
+ * codes as pa_decode_v2, for any batch.
  *
  * With G = num_heads / num_kv_heads in {2, 4, 8} and partition_size <= 1024,
  * aligned sets of 16/G sequences are taken together: the sequences of a set
