@@ -629,7 +629,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode "
-              "kernels are not sharded across GPUs in this build.", file=sys.stderr)
+              "kernels run on one GPU; sharding over GPUs is not implemented.", file=sys.stderr)
         sys.exit(2)
 
     import torch
