@@ -508,11 +508,15 @@ void pa_decode_kernel(DecodeParams p) {
             // k + DP - 1 is requested just before block k is processed
             constexpr int DP = Path::kDepth;
             static_assert(DP == 2 || DP == 4, "the ring must divide a 64-entry window");
-            typename Path::Tile t[DP];
+            typename Path::Stage t[DP];
+            auto step = [&](const typename Path::Stage& ts, int kk) {
+                typename Path::Tile tt = Path::unstage(ts);
+                Path::process(st, tt, qr, valid(kk), sl2);
+            };
 #pragma unroll
             for (int j = 0; j < DP - 1; ++j) {
                 const int id = phys(0, j);
-                Path::template load<NTL>(t[j], tile_k(id), tile_v(id), live(j));
+                Path::template load_stage<NTL>(t[j], tile_k(id), tile_v(id), live(j));
             }
             int k = 0;
             for (int kw = 0;; kw += 64) {
@@ -522,9 +526,9 @@ void pa_decode_kernel(DecodeParams p) {
 #pragma unroll
                     for (int j = 0; j < DP; ++j) {
                         const int id = phys(kw, k + j + DP - 1);
-                        Path::template load<NTL>(t[(j + DP - 1) % DP], tile_k(id), tile_v(id),
-                                                 live(k + j + DP - 1));
-                        Path::process(st, t[j], qr, valid(k + j), sl2);
+                        Path::template load_stage<NTL>(t[(j + DP - 1) % DP], tile_k(id), tile_v(id),
+                                                       live(k + j + DP - 1));
+                        step(t[j], k + j);
                     }
                 }
                 if (kw + 64 >= n) break;
@@ -534,7 +538,7 @@ void pa_decode_kernel(DecodeParams p) {
             // the last n - k < DP blocks, already requested into t[0 ..]
 #pragma unroll
             for (int j = 0; j < DP - 1; ++j)
-                if (k + j < n) Path::process(st, t[j], qr, valid(k + j), sl2);
+                if (k + j < n) step(t[j], k + j);
         };
         // The LDS ring (units of grids the device holds at once, where it
         // measured faster: fewer registers per wave; elsewhere the register
@@ -860,27 +864,28 @@ __global__ __launch_bounds__(64 * NW) void pa_decode_set_kernel(DecodeParams p) 
                 return (!SPLIT || k < n_sh) ? min(kBlock, tok_end - (first + k * SF) * kBlock) : last_valid;
             };
             auto live = [&](int j) { return j < n ? TB : 0; };
-            auto step = [&](typename Path::Tile& t, int k) {
+            auto step = [&](const typename Path::Stage& ts, int k) {
+                typename Path::Tile t = Path::unstage(ts);
                 if constexpr (SPLIT)   // a shared block: every head; an own last block: its member's
                     Path::template process<true>(st, t, qr, valid(k), sl2,
                                                  k < n_sh || (lane & 15) / G == member_of(k));
                 else
                     Path::process(st, t, qr, valid(k), sl2);
             };
-            typename Path::Tile t[DP];
+            typename Path::Stage t[DP];
 #pragma unroll
             for (int j = 0; j < DP - 1; ++j) {
                 const int id = phys(j);
-                Path::template load<NTL>(t[j], kbase + (size_t)id * blk_stride,
-                                         vbase + (size_t)id * blk_stride, live(j));
+                Path::template load_stage<NTL>(t[j], kbase + (size_t)id * blk_stride,
+                                               vbase + (size_t)id * blk_stride, live(j));
             }
             int k = 0;
             for (; k < (n & ~(DP - 1)); k += DP) {
 #pragma unroll
                 for (int j = 0; j < DP; ++j) {
                     const int id = phys(k + j + DP - 1);
-                    Path::template load<NTL>(t[(j + DP - 1) % DP], kbase + (size_t)id * blk_stride,
-                                             vbase + (size_t)id * blk_stride, live(k + j + DP - 1));
+                    Path::template load_stage<NTL>(t[(j + DP - 1) % DP], kbase + (size_t)id * blk_stride,
+                                                   vbase + (size_t)id * blk_stride, live(k + j + DP - 1));
                     step(t[j], k + j);
                 }
             }
@@ -987,8 +992,8 @@ static int launch_nw(int NW, const DecodeParams& p0, int grid, int nh_max, hipSt
             }
             return (long long)per_cu * p.num_cus;
         };
-        // one-wave MFMA units walk their tiles through the LDS ring: fp16
-        // tiles when the device holds the whole grid at once, fp8 tiles always
+        // one-wave fp16 MFMA units walk their tiles through the LDS ring when
+        // the device holds the whole grid at once
         if constexpr (V2 && Path::kRing) {
             if (NW == 1) {
                 const size_t lds_ring = std::max(lds, (size_t)2 * Path::kSlot);
@@ -1167,14 +1172,9 @@ static int decode_v2(bool sets, float* tmp_out, float* exp_sums, float* max_logi
     const long long units = (long long)num_seqs * num_kv_heads * p.head_chunks * max_num_partitions;
     const long long grid = (units + p.unit_period - 1) / p.unit_period * p.unit_period;
     if (grid > 0x7fffffffLL) return PA_ERR_INVALID_ARG;
-    // A sequence has on average about half of max_num_partitions partitions.
-    // One-wave fp8 MFMA units walk their tiles through the LDS ring, and the
-    // wave count is picked as for fp16 tiles there (GQA-7B on fp8 pools: two
-    // waves per unit 36.8 us, one 35.3).
-    const bool fp8_ring = fp8 && p.group >= 2;
+    // a sequence has on average about half of max_num_partitions partitions
     const int nw = PA_V2_WAVES ? PA_V2_WAVES
-                               : pick_waves(units / 2, partition_size / 16, head_size,
-                                            fp8 && !fp8_ring ? 1 : 2);
+                               : pick_waves(units / 2, partition_size / 16, head_size, fp8 ? 1 : 2);
     return launch_decode<true>(p, head_size, fp8, nw, (int)grid, as_stream(stream));
 }
 

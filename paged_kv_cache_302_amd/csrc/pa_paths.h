@@ -206,6 +206,14 @@ struct MfmaPath {
         for (int nt = 0; nt < NT; ++nt) t.v[nt] = ld_tile<NTL, f16x4>(rv, 8 * (4 * i + g + 64 * nt));
     }
 
+    // tiles are used as loaded
+    using Stage = Tile;
+    template <bool NTL>
+    __device__ __forceinline__ static void load_stage(Stage& t, const char* kt, const char* vt, int bytes) {
+        load<NTL>(t, kt, vt, bytes);
+    }
+    __device__ __forceinline__ static Tile unstage(const Stage& s) { return s; }
+
     // LDS-staged tiles (load_slot): a slot's tiles read into the MFMA
     // operand registers, in the same layout as load(); with fp16 tiles the
     // ring takes only grids the device holds at once (measured faster there,
@@ -342,6 +350,14 @@ struct ValuPath {
         for (int c = 0; c < KC; ++c) t.v[c] = ld_tile<NTL, f16x8>(rv, 16 * (l + 64 * c));
     }
 
+    // tiles are used as loaded
+    using Stage = Tile;
+    template <bool NTL>
+    __device__ __forceinline__ static void load_stage(Stage& t, const char* kt, const char* vt, int bytes) {
+        load<NTL>(t, kt, vt, bytes);
+    }
+    __device__ __forceinline__ static Tile unstage(const Stage& s) { return s; }
+
     __device__ __forceinline__ static void process(State& st, Tile& t, const QRegs& qr,
                                                    int nvalid, float sl2) {
         const int l = lane_id(), i = l & 15, h = l & 1;
@@ -462,36 +478,57 @@ struct MfmaPath8 : MfmaPath<D> {
         for (int c = 0; c < KC; ++c) qr.q[c] = i < nh ? qr.q[c] : z;
     }
 
+    // Staged tiles: the V tile comes as whole 16-byte rows, lane (i, g)
+    // taking rows 16 (kVR g + e) + i for e < kVR (two loads at D = 128
+    // instead of eight 4-byte pieces), and is put into the Tile layout once
+    // the loads have landed: a 4 x 4 transpose of dwords across the four
+    // 16-lane rows (v_permlane32_swap exchanges rows 0-1 with 2-3, then
+    // v_permlane16_swap row 0 with 1 and 2 with 3), after which lane (i, g)
+    // holds dword g -- tokens 4g .. 4g+3 -- of the rows of lanes (i, 0 .. 3).
+    static constexpr int kVR = NT / 4;
+    __device__ __forceinline__ static void v_from_rows(Tile& t, const u32x4 (&vr)[kVR]) {
+#pragma unroll
+        for (int e = 0; e < kVR; ++e) {
+            uint32_t a0 = vr[e][0], a1 = vr[e][1], a2 = vr[e][2], a3 = vr[e][3];
+            const auto x0 = __builtin_amdgcn_permlane32_swap(a0, a2, false, false);
+            const auto x1 = __builtin_amdgcn_permlane32_swap(a1, a3, false, false);
+            a0 = x0[0];
+            a2 = x0[1];
+            a1 = x1[0];
+            a3 = x1[1];
+            const auto y0 = __builtin_amdgcn_permlane16_swap(a0, a1, false, false);
+            const auto y1 = __builtin_amdgcn_permlane16_swap(a2, a3, false, false);
+            t.v[e] = y0[0];
+            t.v[kVR + e] = y0[1];
+            t.v[2 * kVR + e] = y1[0];
+            t.v[3 * kVR + e] = y1[1];
+        }
+    }
+    struct Stage {
+        u32x4 k[KR];
+        u32x4 vr[kVR];
+    };
     template <bool NTL>
-    __device__ __forceinline__ static void load(Tile& t, const char* kt, const char* vt, int bytes) {
+    __device__ __forceinline__ static void load_stage(Stage& t, const char* kt, const char* vt, int bytes) {
         const int l = lane_id(), i = l & 15, g = l >> 4;
         const auto rk = tile_rsrc(kt, bytes), rv = tile_rsrc(vt, bytes);
 #pragma unroll
         for (int r = 0; r < KR; ++r) t.k[r] = ld_tile<NTL, u32x4>(rk, 16 * (l + 64 * r));
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) t.v[nt] = ld_tile<NTL, uint32_t>(rv, 16 * (16 * nt + i) + 4 * g);
+        for (int e = 0; e < kVR; ++e) t.vr[e] = ld_tile<NTL, u32x4>(rv, 16 * (16 * (kVR * g + e) + i));
+    }
+    __device__ __forceinline__ static Tile unstage(const Stage& s) {
+        Tile t;
+#pragma unroll
+        for (int r = 0; r < KR; ++r) t.k[r] = s.k[r];
+        v_from_rows(t, s.vr);
+        return t;
     }
 
-    // LDS-staged tiles (load_slot), read as load() would; with fp8 tiles the
-    // ring takes every grid (its 16-byte V loads against 4-byte ones in
-    // registers)
-    static constexpr bool kRing = true;
-    static constexpr bool kRingAll = true;
-    static constexpr int kTileBytes = D * kBlock;
-    static constexpr int kSlot = 2 * kTileBytes;
-    static constexpr int kSlotLoads = kSlot / 1024;
-    template <bool NTL>
-    __device__ __forceinline__ static void load_lds(char* slot, const char* kt, const char* vt) {
-        load_slot<NTL, kTileBytes>(slot, kt, vt);
-    }
-    __device__ __forceinline__ static void read_lds(Tile& t, const char* slot) {
-        const int l = lane_id(), i = l & 15, g = l >> 4;
-#pragma unroll
-        for (int r = 0; r < KR; ++r) t.k[r] = *reinterpret_cast<const u32x4*>(slot + 16 * (l + 64 * r));
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-            t.v[nt] = *reinterpret_cast<const uint32_t*>(slot + kTileBytes + 16 * (16 * nt + i) + 4 * g);
-    }
+    // No LDS ring for fp8 tiles: with the V rows fetched 16 bytes at a time
+    // (load_stage) the register ring measured as fast or faster (long-context
+    // decode 308.1 -> 305.0 us cold against the ring on every grid).
+    static constexpr bool kRing = false;
 
     template <bool ROWS = false>
     __device__ __forceinline__ static void process(typename Base::State& st, Tile& t,
@@ -595,6 +632,14 @@ struct ValuPath8 {
 #pragma unroll
         for (int r = 0; r < KR; ++r) t.v[r] = ld_tile<NTL, u32x4>(rv, 16 * (64 * r + l));
     }
+
+    // tiles are used as loaded
+    using Stage = Tile;
+    template <bool NTL>
+    __device__ __forceinline__ static void load_stage(Stage& t, const char* kt, const char* vt, int bytes) {
+        load<NTL>(t, kt, vt, bytes);
+    }
+    __device__ __forceinline__ static Tile unstage(const Stage& s) { return s; }
 
     __device__ __forceinline__ static void process(State& st, Tile& t, const QRegs& qr,
                                                    int nvalid, float sl2) {

@@ -89,11 +89,6 @@ struct MfmaGroups {
         }
     }
 
-    template <bool NTL>
-    __device__ __forceinline__ static void load(Tile& t, const char* kt, const char* vt, int bytes) {
-        Base::template load<NTL>(t, kt, vt, bytes);
-    }
-
     // Raw scores of one block (q . k).  Tokens at or past nvalid are masked,
     // and, when `causal` (a block that reaches past the earliest column's
     // position), tokens past lim[gr], the last offset this lane's column of
