@@ -133,6 +133,21 @@ __device__ __forceinline__ int table_window(const int32_t* row, int first, int n
     return row[min(first + k * NW, row_len - 1)];
 }
 
+// 4 x 4 transpose of dwords across the four 16-lane rows of a wave: lane
+// (i, g) ends with a[j] = what lane (i, j) held in a[g] (v_permlane32_swap
+// exchanges rows 0-1 with 2-3, then v_permlane16_swap row 0 with 1 and 2
+// with 3).
+__device__ __forceinline__ void lane_transpose4(uint32_t (&a)[4]) {
+    const auto x0 = __builtin_amdgcn_permlane32_swap(a[0], a[2], false, false);
+    const auto x1 = __builtin_amdgcn_permlane32_swap(a[1], a[3], false, false);
+    const auto y0 = __builtin_amdgcn_permlane16_swap(x0[0], x1[0], false, false);
+    const auto y1 = __builtin_amdgcn_permlane16_swap(x0[1], x1[1], false, false);
+    a[0] = y0[0];
+    a[1] = y0[1];
+    a[2] = y1[0];
+    a[3] = y1[1];
+}
+
 // --------------------------------------------------------------------------
 // MFMA path (2 <= G): up to 16 query heads of one KV group per wave
 // --------------------------------------------------------------------------
@@ -206,7 +221,8 @@ struct MfmaPath {
         for (int nt = 0; nt < NT; ++nt) t.v[nt] = ld_tile<NTL, f16x4>(rv, 8 * (4 * i + g + 64 * nt));
     }
 
-    // tiles are used as loaded
+    // tiles are used as loaded (16-byte V rows with a quad-word transpose
+    // across lanes, as the fp8 path does, measured slower for fp16 tiles)
     using Stage = Tile;
     template <bool NTL>
     __device__ __forceinline__ static void load_stage(Stage& t, const char* kt, const char* vt, int bytes) {
@@ -481,27 +497,17 @@ struct MfmaPath8 : MfmaPath<D> {
     // Staged tiles: the V tile comes as whole 16-byte rows, lane (i, g)
     // taking rows 16 (kVR g + e) + i for e < kVR (two loads at D = 128
     // instead of eight 4-byte pieces), and is put into the Tile layout once
-    // the loads have landed: a 4 x 4 transpose of dwords across the four
-    // 16-lane rows (v_permlane32_swap exchanges rows 0-1 with 2-3, then
-    // v_permlane16_swap row 0 with 1 and 2 with 3), after which lane (i, g)
-    // holds dword g -- tokens 4g .. 4g+3 -- of the rows of lanes (i, 0 .. 3).
+    // the loads have landed: after the dword transpose across the 16-lane
+    // rows lane (i, g) holds dword g -- tokens 4g .. 4g+3 -- of the rows of
+    // lanes (i, 0 .. 3).
     static constexpr int kVR = NT / 4;
     __device__ __forceinline__ static void v_from_rows(Tile& t, const u32x4 (&vr)[kVR]) {
 #pragma unroll
         for (int e = 0; e < kVR; ++e) {
-            uint32_t a0 = vr[e][0], a1 = vr[e][1], a2 = vr[e][2], a3 = vr[e][3];
-            const auto x0 = __builtin_amdgcn_permlane32_swap(a0, a2, false, false);
-            const auto x1 = __builtin_amdgcn_permlane32_swap(a1, a3, false, false);
-            a0 = x0[0];
-            a2 = x0[1];
-            a1 = x1[0];
-            a3 = x1[1];
-            const auto y0 = __builtin_amdgcn_permlane16_swap(a0, a1, false, false);
-            const auto y1 = __builtin_amdgcn_permlane16_swap(a2, a3, false, false);
-            t.v[e] = y0[0];
-            t.v[kVR + e] = y0[1];
-            t.v[2 * kVR + e] = y1[0];
-            t.v[3 * kVR + e] = y1[1];
+            uint32_t a[4] = {vr[e][0], vr[e][1], vr[e][2], vr[e][3]};
+            lane_transpose4(a);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) t.v[kVR * j + e] = a[j];
         }
     }
     struct Stage {
