@@ -999,8 +999,8 @@ static int launch_nw(int NW, const DecodeParams& p0, int grid, int nh_max, hipSt
                 const size_t lds_ring = std::max(lds, (size_t)2 * Path::kSlot);
                 const void* fr = reinterpret_cast<const void*>(&pa_decode_kernel<Path, D, 1, true, true>);
                 const long long res = resident_slots(fr, 64, lds_ring, 4);
-                if (grid <= res || Path::kRingAll) {
-                    p.resident = grid <= res ? (int)res : 0;
+                if (grid <= res) {
+                    p.resident = (int)res;
                     hipLaunchKernelGGL((pa_decode_kernel<Path, D, 1, true, true>), dim3(grid), dim3(64),
                                        lds_ring, st, p);
                     return launch_status();

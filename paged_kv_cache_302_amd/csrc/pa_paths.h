@@ -235,7 +235,6 @@ struct MfmaPath {
     // ring takes only grids the device holds at once (measured faster there,
     // slower on larger grids of short units)
     static constexpr bool kRing = true;
-    static constexpr bool kRingAll = false;
     static constexpr int kTileBytes = D * kBlock * 2;
     static constexpr int kSlot = 2 * kTileBytes;
     static constexpr int kSlotLoads = kSlot / 1024;   // load instructions per slot
