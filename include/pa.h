@@ -266,7 +266,8 @@ PA_API int pa_prefill(float* out, const void* q, const void* k_cache, const void
                float k_scale, float v_scale, void* stream);
 
 /*
- * reshape_and_cache -- scatter new tokens' K and V into the pools through
+ * pa_reshape_and_cache -- the pages' reshape_and_cache: scatter new tokens'
+ * K and V into the pools through
  * slot_mapping (§3.2: a flat physical slot = block id * block_size + offset
  * in the block; the write is the same indirection as the read, in the other
  * direction).
@@ -287,11 +288,11 @@ PA_API int pa_prefill(float* out, const void* q, const void* k_cache, const void
  * With num_tokens == 0 nothing is enqueued and key, value and slot_mapping
  * may be NULL.
  */
-PA_API int reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
-                      const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
-                      int head_size, int block_size, int num_blocks,
-                      int64_t key_stride, int64_t value_stride,
-                      int kv_cache_dtype, float k_scale, float v_scale, void* stream);
+PA_API int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                         const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
+                         int head_size, int block_size, int num_blocks,
+                         int64_t key_stride, int64_t value_stride,
+                         int kv_cache_dtype, float k_scale, float v_scale, void* stream);
 
 /*
  * pa_gather_kv -- the read-side indirection alone: every sequence's K and V

@@ -105,7 +105,7 @@ PA_API int pa_bm_seq_len(const pa_block_manager* bm, int64_t seq_id);
 PA_API int pa_bm_refcount(const pa_block_manager* bm, int block);
 
 /*
- * copy_blocks -- the device side of copy-on-write: for each pair i,
+ * pa_copy_blocks -- the device side of copy-on-write: for each pair i,
  * block block_pairs[2i+1] of both pools becomes a bit-exact copy of block
  * block_pairs[2i] (all KV heads, all slots).  Pairs are independent (a
  * destination must not be another pair's source or destination, which
@@ -118,9 +118,9 @@ PA_API int pa_bm_refcount(const pa_block_manager* bm, int block);
  *                     num_pairs == 0, which enqueues nothing)
  * Enqueued on `stream`; PA_ERR_* as in pa.h for bad host arguments.
  */
-PA_API int copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs, int num_pairs,
-                       int num_kv_heads, int head_size, int block_size, int num_blocks,
-                       int kv_cache_dtype, void* stream);
+PA_API int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs, int num_pairs,
+                          int num_kv_heads, int head_size, int block_size, int num_blocks,
+                          int kv_cache_dtype, void* stream);
 
 #ifdef __cplusplus
 }

@@ -10,6 +10,7 @@ from ._lib import (  # noqa: F401
     BlockManager,
     BlockManagerError,
     copy_blocks,
+    pa_copy_blocks,
     PagedAttentionError,
     exported_symbols,
     kv_dtype_of,
@@ -26,6 +27,7 @@ from ._lib import (  # noqa: F401
     paged_attention_v1,
     paged_attention_v2,
     reshape_and_cache,
+    pa_reshape_and_cache,
     split_kv_cache,
     v2_scratch,
 )

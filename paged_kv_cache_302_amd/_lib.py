@@ -37,7 +37,7 @@ _SIGNATURES = {
     "pa_decode_v2_noalloc": ([_ptr] * 6 + [_c_int] * 9 + [_c_float, _c_int, _c_float, _c_float, _ptr],
                              _c_int),
     "pa_prefill": ([_ptr] * 7 + [_c_int] * 9 + [_c_float, _c_int, _c_float, _c_float, _ptr], _c_int),
-    "reshape_and_cache": ([_ptr] * 5 + [_c_int] * 5 + [_c_i64, _c_i64, _c_int, _c_float, _c_float,
+    "pa_reshape_and_cache": ([_ptr] * 5 + [_c_int] * 5 + [_c_i64, _c_i64, _c_int, _c_float, _c_float,
                                                          _ptr], _c_int),
     "pa_gather_kv": ([_ptr] * 7 + [_c_int] * 7 + [_ptr], _c_int),
     # block manager (host) and its device block copy -- include/pa_blocks.h
@@ -52,7 +52,7 @@ _SIGNATURES = {
     "pa_bm_num_sequences": ([_ptr], _c_int),
     "pa_bm_seq_len": ([_ptr, _c_i64], _c_int),
     "pa_bm_refcount": ([_ptr, _c_int], _c_int),
-    "copy_blocks": ([_ptr] * 3 + [_c_int] * 6 + [_ptr], _c_int),
+    "pa_copy_blocks": ([_ptr] * 3 + [_c_int] * 6 + [_ptr], _c_int),
 }
 
 _lib = None
@@ -276,8 +276,8 @@ def pa_reduce(out, tmp_out, exp_sums, max_logits, seq_lens, partition_size: int,
     return out
 
 
-def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, k_scale: float = 1.0,
-                      v_scale: float = 1.0, stream=None):
+def pa_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, k_scale: float = 1.0,
+                         v_scale: float = 1.0, stream=None):
     """Scatter key/value [T,KVH,D] into the pools at slot_mapping[T] (int64);
     into fp8 pools as E4M3 codes of key / k_scale and value / v_scale."""
     NB, KVH, D, B = _cache_dims(k_cache, v_cache)
@@ -292,11 +292,15 @@ def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, k_scale: float
     if tuple(key.shape) != (T, KVH, D) or tuple(value.shape) != (T, KVH, D) or slot_mapping.shape[0] != T:
         raise ValueError("key/value must be [T, num_kv_heads, head_size], slot_mapping [T]")
     lib = load_library()
-    rc = lib.reshape_and_cache(_p(key), _p(value), _p(k_cache), _p(v_cache), _p(slot_mapping), T, KVH,
+    rc = lib.pa_reshape_and_cache(_p(key), _p(value), _p(k_cache), _p(v_cache), _p(slot_mapping), T, KVH,
                                D, B, NB, key.stride(0) if T else KVH * D,
                                value.stride(0) if T else KVH * D, kv_dtype_of(k_cache),
                                float(k_scale), float(v_scale), _stream(key, stream))
-    _check(rc, "reshape_and_cache")
+    _check(rc, "pa_reshape_and_cache")
+
+
+# the pages' name of the operation
+reshape_and_cache = pa_reshape_and_cache
 
 
 def pa_gather_kv(k_out, v_out, k_cache, v_cache, block_tables, seq_lens, cu_seq_lens, stream=None):
@@ -458,13 +462,16 @@ class BlockManager:
         return [self.refcount_of(b) for b in range(self.num_blocks)]
 
 
-def copy_blocks(k_cache, v_cache, block_pairs, stream=None):
+def pa_copy_blocks(k_cache, v_cache, block_pairs, stream=None):
     """Copy-on-write on the device: block_pairs int32 [n, 2] (source, destination)."""
     NB, KVH, D, B = _cache_dims(k_cache, v_cache)
     _want(block_pairs, "block_pairs", torch.int32, 2, k_cache.device)
     if block_pairs.shape[1] != 2:
         raise ValueError("block_pairs must be [num_pairs, 2]")
-    rc = load_library().copy_blocks(_p(k_cache), _p(v_cache), _p(block_pairs),
+    rc = load_library().pa_copy_blocks(_p(k_cache), _p(v_cache), _p(block_pairs),
                                     block_pairs.shape[0], KVH, D, B, NB, kv_dtype_of(k_cache),
                                     _stream(k_cache, stream))
-    _check(rc, "copy_blocks")
+    _check(rc, "pa_copy_blocks")
+
+
+copy_blocks = pa_copy_blocks

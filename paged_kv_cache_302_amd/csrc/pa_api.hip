@@ -1,7 +1,7 @@
 // ABI version and status strings of libpa.
 #include "pa.h"
 
-extern "C" int pa_abi_version(void) { return 7; }
+extern "C" int pa_abi_version(void) { return 8; }
 
 extern "C" const char* pa_status_str(int status) {
     switch (status) {

@@ -168,9 +168,9 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(
 
 using namespace pa;
 
-extern "C" int copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs, int num_pairs,
-                           int num_kv_heads, int head_size, int block_size, int num_blocks,
-                           int kv_cache_dtype, void* stream) {
+extern "C" int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs, int num_pairs,
+                              int num_kv_heads, int head_size, int block_size, int num_blocks,
+                              int kv_cache_dtype, void* stream) {
     int rc = check_head_block(head_size, block_size);
     if (rc != PA_OK) return rc;
     rc = check_kv_dtype(kv_cache_dtype, 1.f, 1.f);
@@ -189,11 +189,11 @@ extern "C" int copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pa
     return launch_status();
 }
 
-extern "C" int reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
-                                 const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
-                                 int head_size, int block_size, int num_blocks,
-                                 int64_t key_stride, int64_t value_stride, int kv_cache_dtype,
-                                 float k_scale, float v_scale, void* stream) {
+extern "C" int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                                    const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
+                                    int head_size, int block_size, int num_blocks,
+                                    int64_t key_stride, int64_t value_stride, int kv_cache_dtype,
+                                    float k_scale, float v_scale, void* stream) {
     int rc = check_head_block(head_size, block_size);
     if (rc != PA_OK) return rc;
     rc = check_kv_dtype(kv_cache_dtype, k_scale, v_scale);

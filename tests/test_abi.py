@@ -39,8 +39,8 @@ def arg_ctype(arg):
 
 def test_header_lists_the_entry_points():
     names = set(header_decls())
-    assert {"pa_decode_v1", "pa_decode_v2", "pa_decode_v2_shared", "pa_reduce", "reshape_and_cache", "pa_gather_kv",
-            "pa_v2_max_partitions", "pa_status_str", "pa_abi_version", "copy_blocks",
+    assert {"pa_decode_v1", "pa_decode_v2", "pa_decode_v2_shared", "pa_reduce", "pa_reshape_and_cache", "pa_gather_kv",
+            "pa_v2_max_partitions", "pa_status_str", "pa_abi_version", "pa_copy_blocks",
             "pa_bm_create", "pa_bm_append_slots"} <= names
     assert names == set(_lib.exported_symbols())
 
@@ -61,7 +61,7 @@ def test_binding_signatures_match_header():
 
 def test_status_strings_and_version():
     lib = pa.load_library()
-    assert lib.pa_abi_version() == 7
+    assert lib.pa_abi_version() == 8
     assert lib.pa_status_str(0) == b"ok"
     for rc in (-1, -2, -3, -4, -5):
         assert len(lib.pa_status_str(rc)) > 5
@@ -126,20 +126,20 @@ def test_v2_and_reduce_reject_bad_partitioning():
 
 def test_cache_write_rejects_bad_arguments():
     lib = pa.load_library()
-    rc = lambda *a: lib.reshape_and_cache(*a[:12], a[12] if len(a) > 12 else 0, 1.0, 1.0, None)
+    rc = lambda *a: lib.pa_reshape_and_cache(*a[:12], a[12] if len(a) > 12 else 0, 1.0, 1.0, None)
     assert rc(A, A, A, A, A, 4, 2, 128, 16, 8, 100, 256) == -1  # stride < row
     assert rc(A, A, A, A, A, 4, 2, 128, 16, 8, 260, 260) == -3  # stride % 8
     assert rc(A, A, A, A, A, 4, 2, 64, 8, 8, 128, 128) == -2
     assert rc(A, A, A, A, A, 0, 2, 128, 16, 8, 256, 256) == 0   # no tokens
     assert rc(A, A, A, A, A, 4, 2, 128, 16, 8, 256, 256, 5) == -2   # unknown dtype
-    assert lib.reshape_and_cache(A, A, A, A, A, 4, 2, 128, 16, 8, 256, 256, 1, 0.0, 1.0, None) == -1
+    assert lib.pa_reshape_and_cache(A, A, A, A, A, 4, 2, 128, 16, 8, 256, 256, 1, 0.0, 1.0, None) == -1
     assert lib.pa_gather_kv(A, A, A, A, A, A, None, 2, 2, 128, 16, 4, 8, 0, None) == -1
     assert lib.pa_gather_kv(A, A, A, A, A, A, A, 2, 2, 128, 16, 4, 8, 3, None) == -2
-    assert lib.copy_blocks(A, A, A, 3, 2, 96, 16, 8, 0, None) == -2
-    assert lib.copy_blocks(A, A, None, 3, 2, 128, 16, 8, 0, None) == -1
-    assert lib.copy_blocks(M, A, A, 3, 2, 128, 16, 8, 0, None) == -3
-    assert lib.copy_blocks(A, A, A, 0, 2, 128, 16, 8, 1, None) == 0    # no pairs
-    assert lib.copy_blocks(A, A, A, 3, 2, 128, 16, 8, 7, None) == -2
+    assert lib.pa_copy_blocks(A, A, A, 3, 2, 96, 16, 8, 0, None) == -2
+    assert lib.pa_copy_blocks(A, A, None, 3, 2, 128, 16, 8, 0, None) == -1
+    assert lib.pa_copy_blocks(M, A, A, 3, 2, 128, 16, 8, 0, None) == -3
+    assert lib.pa_copy_blocks(A, A, A, 0, 2, 128, 16, 8, 1, None) == 0    # no pairs
+    assert lib.pa_copy_blocks(A, A, A, 3, 2, 128, 16, 8, 7, None) == -2
 
 
 def test_block_manager_rejects_bad_arguments():
