@@ -356,19 +356,16 @@ void pa_decode_kernel(DecodeParams p) {
         s = r_unit;
         L = p.seq_lens[s];
     }
-    // v1 out[S][H][D]; v2 tmp_out[S][P][H][D]: either way the unit's heads
-    // are consecutive rows, so its result is one contiguous run of memory
-    const size_t out_head_stride = D;
-    const size_t row0 = V2 ? ((size_t)s * p.max_num_partitions + part) * p.num_heads + h0
-                           : (size_t)s * p.num_heads + h0;
-    float* out_h0 = p.out + row0 * D;   // exp_sums / max_logits [S][P][H]: index row0 + j
+    // v1 out[S][H][D]; v2 tmp_out[S][P][H][D]: either way a sequence's heads
+    // of the unit are consecutive rows, one contiguous run of memory (out_row
+    // below maps the tile rows)
 
     // Shared partitions: M members per unit (1: the unit's own heads only).
     // Only KV groups that fill the 16 rows evenly (G = 2, 4, 8): with others
     // (G = 7: two members) the member check cost GQA-7B batches, which share
     // nothing, 2% and could at best halve the shared reads.
     int M = 1;
-    if constexpr (V2 && NW == 1 && Path::kHeads == 16) {
+    if constexpr (V2 && Path::kHeads == 16) {
         if (p.group <= kMaxMembers && 16 % p.group == 0 && p.head_chunks == 1 &&
             p.partition_size <= 64 * kBlock)
             M = 16 / p.group;
@@ -595,6 +592,14 @@ void pa_decode_kernel(DecodeParams p) {
     }
 
     const float ltot = Path::wave_l(st);
+    // tile row i -> output row of head h0 + i % gsz of sequence lead + i / gsz
+    // (M == 1: row0 + i)
+    auto out_row = [&](int i) {
+        const size_t sq = (size_t)(lead + i / gsz);
+        const size_t r = V2 ? (sq * p.max_num_partitions + part) * p.num_heads
+                            : sq * p.num_heads;
+        return r + h0 + i % gsz;
+    };
     if constexpr (NW == 1) {
         // The unit's result (nh rows of D, one contiguous run) goes out as
         // whole 1 KiB-per-instruction stores: stage the rows in LDS (this
@@ -607,14 +612,6 @@ void pa_decode_kernel(DecodeParams p) {
         float* s_l = s_m + HP;            // [HP]
         if constexpr (Path::kHeads == 16) Path::stage(st, ltot, s_o, s_m, s_l, nrows, live(lane_id() & 15));
         else Path::stage(st, ltot, s_o, s_m, s_l, nrows);
-        // tile row i -> output row of head h0 + i % gsz of sequence lead + i / gsz
-        // (M == 1: row0 + i)
-        auto out_row = [&](int i) {
-            const size_t sq = (size_t)(lead + i / gsz);
-            const size_t r = V2 ? (sq * p.max_num_partitions + part) * p.num_heads
-                                : sq * p.num_heads;
-            return r + h0 + i % gsz;
-        };
         const f32x4* src = reinterpret_cast<const f32x4*>(s_o);
         for (unsigned mm = members; mm != 0u; mm &= mm - 1u) {   // the rows of each member
             const int m = __ffs(mm) - 1;
@@ -637,21 +634,27 @@ void pa_decode_kernel(DecodeParams p) {
         }
         return;
     } else {
-        // merge the NW wave states through LDS
+        // merge the NW wave states through LDS (the tile rows of every member
+        // computed here)
         const int HP = Path::kHeads;
-        float* s_acc = lds;                              // [NW][nh][D]
-        float* s_m = lds + NW * nh * D;                  // [NW][HP]
+        float* s_acc = lds;                              // [NW][nrows][D]
+        float* s_m = lds + NW * nrows * D;               // [NW][HP]
         float* s_l = s_m + NW * HP;                      // [NW][HP]
         int* s_bad = reinterpret_cast<int*>(s_l + NW * HP);  // [NW]
         float* s_fin = reinterpret_cast<float*>(s_bad + NW);  // [2][16]: merged m, l
-        Path::stage(st, ltot, s_acc + w * nh * D, s_m + w * HP, s_l + w * HP, nh);
+        if constexpr (Path::kHeads == 16)
+            Path::stage(st, ltot, s_acc + w * nrows * D, s_m + w * HP, s_l + w * HP, nrows,
+                        live(lane_id() & 15));
+        else
+            Path::stage(st, ltot, s_acc + w * nrows * D, s_m + w * HP, s_l + w * HP, nrows);
         if (lane_id() == 0) s_bad[w] = bad ? 1 : 0;
         __syncthreads();
         int any_bad = 0;
 #pragma unroll
         for (int v = 0; v < NW; ++v) any_bad |= s_bad[v];
-        for (int e = threadIdx.x; e < nh * D; e += 64 * NW) {
+        for (int e = threadIdx.x; e < nrows * D; e += 64 * NW) {
             const int j = e / D, d = e - j * D;
+            if (!live(j)) continue;   // a member that computes its rows in its own unit
             float M = -INFINITY;
 #pragma unroll
             for (int v = 0; v < NW; ++v) M = fmaxf(M, s_m[v * HP + j]);
@@ -659,11 +662,11 @@ void pa_decode_kernel(DecodeParams p) {
 #pragma unroll
             for (int v = 0; v < NW; ++v) {
                 const float f = exp2_fast((s_m[v * HP + j] - M) * sl2);
-                num += s_acc[(v * nh + j) * D + d] * f;
+                num += s_acc[(v * nrows + j) * D + d] * f;
                 den += s_l[v * HP + j] * f;
             }
             const float o = empty ? 0.f : num / den * p.v_scale;
-            st_row(out_h0 + (size_t)j * out_head_stride + d, any_bad ? NAN : o, p.resident > 0);
+            st_row(p.out + out_row(j) * D + d, any_bad ? NAN : o, p.resident > 0);
             if (V2 && d == 0) {
                 s_fin[j] = M;
                 s_fin[16 + j] = den;
@@ -672,9 +675,9 @@ void pa_decode_kernel(DecodeParams p) {
         if constexpr (V2) {
             __syncthreads();
             const int t = threadIdx.x;
-            if (t < nh) {
-                st_stat(p.max_logits + row0 + t, any_bad ? NAN : s_fin[t] * p.scale);
-                st_stat(p.exp_sums + row0 + t, any_bad ? NAN : s_fin[16 + t]);
+            if (t < nrows && live(t)) {
+                st_stat(p.max_logits + out_row(t), any_bad ? NAN : s_fin[t] * p.scale);
+                st_stat(p.exp_sums + out_row(t), any_bad ? NAN : s_fin[16 + t]);
             }
         }
     }
@@ -954,20 +957,30 @@ static size_t merge_lds_bytes(int NW, int nh_max, int D, int hp) {
 
 template <class Path, int D, bool V2>
 static int launch_nw(int NW, const DecodeParams& p0, int grid, int nh_max, hipStream_t st) {
-    // keep the merge buffer within the default 64 KiB of dynamic LDS
-    while (NW > 1 && merge_lds_bytes(NW, nh_max, D, Path::kHeads) > 65536) NW /= 2;
-    // a one-wave v2 MFMA unit may hold several sequences' heads: 16 tile rows
-    if (V2 && NW == 1 && Path::kHeads == 16) nh_max = 16;
-    const size_t lds = merge_lds_bytes(NW, nh_max, D, Path::kHeads);
-    DecodeParams p = p0;
+    const int nh_unit = nh_max;
+    // v2 MFMA units whose sequences may share a unit (the kernel's condition)
+    const bool members = p0.group <= kMaxMembers && 16 % p0.group == 0 && p0.head_chunks == 1 &&
+                         p0.partition_size <= 64 * kBlock;
+    size_t lds = 0;
     const void* fn = nullptr;
-    switch (NW) {
-        case 1: fn = reinterpret_cast<const void*>(&pa_decode_kernel<Path, D, 1, V2>); break;
-        case 2: fn = reinterpret_cast<const void*>(&pa_decode_kernel<Path, D, 2, V2>); break;
-        case 4: fn = reinterpret_cast<const void*>(&pa_decode_kernel<Path, D, 4, V2>); break;
-        case 8: fn = reinterpret_cast<const void*>(&pa_decode_kernel<Path, D, 8, V2>); break;
-        default: return PA_ERR_INVALID_ARG;
-    }
+    auto setup = [&](int nw) {
+        NW = nw;
+        // keep the merge buffer within the default 64 KiB of dynamic LDS
+        while (NW > 1 && merge_lds_bytes(NW, nh_unit, D, Path::kHeads) > 65536) NW /= 2;
+        // a v2 MFMA unit may hold several sequences' heads: 16 tile rows
+        nh_max = V2 && Path::kHeads == 16 && members ? 16 : nh_unit;
+        lds = merge_lds_bytes(NW, nh_max, D, Path::kHeads);
+        switch (NW) {
+            case 1: fn = reinterpret_cast<const void*>(&pa_decode_kernel<Path, D, 1, V2>); break;
+            case 2: fn = reinterpret_cast<const void*>(&pa_decode_kernel<Path, D, 2, V2>); break;
+            case 4: fn = reinterpret_cast<const void*>(&pa_decode_kernel<Path, D, 4, V2>); break;
+            case 8: fn = reinterpret_cast<const void*>(&pa_decode_kernel<Path, D, 8, V2>); break;
+            default: fn = nullptr;
+        }
+    };
+    setup(NW);
+    if (!fn) return PA_ERR_INVALID_ARG;
+    DecodeParams p = p0;
     {
         // Only when the whole grid is resident at once does the placement fix
         // each CU's share: then a v2 kernel takes the balanced unit order.
@@ -1006,6 +1019,18 @@ static int launch_nw(int NW, const DecodeParams& p0, int grid, int nh_max, hipSt
                     return launch_status();
                 }
             }
+        }
+        // Long contexts (64 or more partitions of at least 16 blocks) on a
+        // grid larger than the device holds at once: four waves per MFMA unit
+        // (interleaved A/B: long-context decode 569.3 -> 563.1 us cold, fp8
+        // pools 304.4 -> 299.7).  Not for shorter batches, where it measured
+        // -2% to +7%, nor on the VALU path; it also gives up the one-wave
+        // units' member sharing, which batches that share blocks get from
+        // pa_decode_v2_shared.
+        if constexpr (V2 && Path::kHeads == 16 && PA_V2_WAVES == 0) {
+            if (NW == 1 && p.partition_size >= 16 * kBlock && p.max_num_partitions >= 64 &&
+                grid > resident_slots(fn, 64, lds, 0))
+                setup(4);
         }
         const int slot = NW == 1 ? 0 : NW == 2 ? 1 : NW == 4 ? 2 : 3;
         const long long resident = resident_slots(fn, 64 * NW, lds, slot);

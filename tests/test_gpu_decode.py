@@ -36,12 +36,15 @@ REDUCE_CASES = [
 # 200 sequences span four 64-lane chunks of its lookup, 128-block partitions
 # leave the partly filled ones unsorted, 1,200 sequences x 8 partitions
 # exceed what the device holds (plain order), and 64 sequences x 8 KV heads x
-# up to 16 partitions exceed it with no shared blocks (XCD-major order).
+# up to 16 partitions exceed it with no shared blocks (XCD-major order), and
+# 8 sequences of up to 20,000 tokens in 256-token partitions take four waves
+# per unit.
 ORDER_CASES = [
     ("order_200seqs", 200, 14, 2, 64, 1, 700, 128),
     ("order_ps2048", 3, 8, 2, 128, 1, 5000, 2048),
     ("order_big_grid", 1200, 14, 2, 64, 1, 1000, 128),
     ("order_xcd_major", 64, 32, 8, 128, 1, 1024, 64),
+    ("order_long_four_waves", 8, 32, 8, 128, 1, 20000, 256),
 ]
 # the set kernel (pa_decode_v2_shared with G = 2, 4, 8 and PS <= 1024): sets
 # of 16/G sequences, the last one cut short by the batch (70 = 8 x 8 + 6,
@@ -350,18 +353,20 @@ def _share_tables(bt, seq_lens, pattern):
     return bt
 
 
-@pytest.mark.parametrize("G,LEN,PS", [(2, 300, 64), (4, 300, 64), (8, 300, 64), (4, 5000, 16)],
-                         ids=["g2", "g4", "g8", "g4_big_grid"])
-def test_partitions_shared_by_sequences_match_private_copies(G, LEN, PS):
+@pytest.mark.parametrize("G,LEN,PS,KVH", [(2, 300, 64, 2), (4, 300, 64, 2), (8, 300, 64, 2),
+                                          (4, 5000, 16, 2), (4, 20000, 256, 8)],
+                         ids=["g2", "g4", "g8", "g4_big_grid", "g4_long_four_waves"])
+def test_partitions_shared_by_sequences_match_private_copies(G, LEN, PS, KVH):
     """v2 units of sequences that read the same blocks over a partition (taken
     together in one tile) equal, bit for bit, the same sequences reading
     private copies of those blocks, and the oracle; covered: whole sets that
     share, a member that differs in one block, a member whose token range in
     the last partition differs, sharing that crosses the sets' alignment.
-    The last case's grid (12 x 2 x 313 one-block partitions) exceeds what the
-    device holds: shared tables keep the plain unit order, the private copies
-    take the XCD-major one."""
-    S, KVH, D = 12, 2, 128
+    The fourth case's grid (12 x 2 x 313 one-block partitions) exceeds what
+    the device holds: shared tables keep the plain unit order, the private
+    copies take the XCD-major one.  The last one (79 partitions of 16 blocks,
+    a grid larger than the device holds) runs four waves per unit."""
+    S, D = 12, 128
     w = wl.small_workload("share", num_seqs=S, num_heads=G * KVH, num_kv_heads=KVH,
                           head_size=D, seq_len_lo=LEN, seq_len_hi=LEN, partition_size=PS)
     inp = wl.make_inputs(w, 21)

@@ -243,6 +243,7 @@ FP8_ORDER_CASES = [
     ("resident_200", 200, 14, 2, 64, 1, 700, 128),
     ("set_g4_big_grid", 1200, 8, 2, 64, 1, 1000, 128),
     ("set_g8_d128", 130, 16, 2, 128, 1, 900, 256),
+    ("long_four_waves", 8, 32, 8, 128, 1, 20000, 256),
 ]
 
 
